@@ -1,0 +1,328 @@
+"""Plain, slow fp64 oracle for KV-cache scoring, selection, compaction and H2O.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``.  The HIP product path never imports
+it, and it imports nothing from the product package.
+
+Sources followed (cited per function):
+  * LORE-KV project page, "Monte Carlo Estimation for KV-Cache Eviction":
+    Method ("Prefill", "Projected deletion score" Eqs. 5-7, "Evict and decode"
+    Eq. 8) and the Hyperparameters table (w, M, T, lambda_L, eps, chunk).
+  * H2O summary page, "H2O: Heavy-Hitter Oracle": 3.4 formal problem
+    formulation (Defs. 2.1-2.2), the H2O eviction algorithm (accumulated
+    scores, greedy eviction, budget split), System Implementation Details.
+
+Readings taken where the pages leave a step open (each also listed in the
+design notes): softmax logits carry 1/sqrt(d); window rows are causal at their
+own positions; psi is the arithmetic mean; the GQA group score is the mean of
+its query heads' scores; chunk pooling is the mean over a chunk's candidate
+members; ties rank by lower index; H2O's budget is floor(frac * current
+length) per part, the recent part is protected, and the prompt is reduced to
+the budget by accumulated column sums before decoding.
+"""
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lore_oracle.c")
+_BUILD = os.path.join(_HERE, "_build")
+_SO = os.path.join(_BUILD, "liboracle.so")
+_lib_handle = None
+
+_DP = ctypes.POINTER(ctypes.c_double)
+
+
+def build(force: bool = False) -> str:
+    """Compile the C part of the oracle with gcc (IEEE fp64: no fast-math)."""
+    os.makedirs(_BUILD, exist_ok=True)
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        tmp = _SO + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def _lib():
+    global _lib_handle
+    if _lib_handle is None:
+        lib = ctypes.CDLL(build())
+        i, d = ctypes.c_int, ctypes.c_double
+        lib.ora_lore_attention.argtypes = [i, i, i, i, i, i, i, _DP, _DP, _DP, _DP, _DP, _DP, i]
+        lib.ora_lore_attention.restype = i
+        lib.ora_lore_scores.argtypes = [i, i, i, i, i, i, i, i, d, d,
+                                        _DP, _DP, _DP, _DP, _DP, _DP, _DP, _DP, _DP, i]
+        lib.ora_lore_scores.restype = i
+        lib.ora_max_threads.argtypes = []
+        lib.ora_max_threads.restype = i
+        _lib_handle = lib
+    return _lib_handle
+
+
+def max_threads() -> int:
+    return _lib().ora_max_threads()
+
+
+def _f64(x):
+    """Exact widening to a contiguous fp64 numpy array (torch tensors accepted)."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu")
+        import torch
+        x = x.to(torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    return a.ctypes.data_as(_DP)
+
+
+# --------------------------------------------------------------------------
+# LORE-KV
+# --------------------------------------------------------------------------
+
+def lore_attention(Q, K, V, w, nthreads=0):
+    """Softmax statistics and outputs of the w + M*T scoring rows.
+
+    LORE-KV page, Method: "Prefill" keeps the window queries of the last w
+    prompt tokens; Eq. 5 uses the attention output o_q.  Row r < w sees
+    tokens 0..n-w+r (causal at its own position); later rows see all n.
+    Returns (row_max [b][h_q][n_q], row_sum [b][h_q][n_q], O [b][h_q][n_q][d]).
+    """
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    b, h_q, n_q, d = Q.shape
+    _, h_kv, n, _ = K.shape
+    m = np.empty((b, h_q, n_q)); l = np.empty((b, h_q, n_q)); O = np.empty((b, h_q, n_q, d))
+    rc = _lib().ora_lore_attention(b, n, h_q, h_kv, d, n_q, w, _ptr(Q), _ptr(K), _ptr(V),
+                                   _ptr(m), _ptr(l), _ptr(O), int(nthreads))
+    if rc != 0:
+        raise ValueError("ora_lore_attention: invalid shape")
+    return m, l, O
+
+
+def projection_factors(W_O, h_q, d):
+    """R_h (upper triangular) with R_h^T R_h = W_h^T W_h for every query head.
+
+    W_h is the d_model x d column slice h*d..h*d+d-1 of W_O (the head's output
+    projection, LORE-KV page Eq. 6).  ||W_h x|| == ||R_h x|| for every x, so
+    the oracle can take the projected norm in d dimensions.  The Cholesky
+    factorisation is the library step.
+    """
+    W = _f64(W_O)
+    R = np.empty((h_q, d, d))
+    for h in range(h_q):
+        Wh = W[:, h * d:(h + 1) * d]
+        L = np.linalg.cholesky(Wh.T @ Wh)
+        R[h] = L.T
+    return R
+
+
+def lore_scores(Q, K, V, W_O, omega, *, w, m, t, eps, lambda_l, nthreads=0, R=None):
+    """Projected deletion score of every cached token for every KV head.
+
+    LORE-KV page, "Projected deletion score", Eqs. 5-7, with psi the mean and
+    the KV head's score the mean over its GQA group of query heads ("Evict and
+    decode", Eq. 8: each KV head keeps its own top-B).
+    Returns a dict: S [b][h_kv][n], S_head [b][h_q][n], row_max, row_sum, O.
+    """
+    Q, K, V, omega = _f64(Q), _f64(K), _f64(V), _f64(omega)
+    b, h_q, n_q, d = Q.shape
+    _, h_kv, n, _ = K.shape
+    if n_q != w + m * t:
+        raise ValueError("n_q must equal w + m*t")
+    if R is None:
+        R = projection_factors(W_O, h_q, d)
+    R = _f64(R)
+    row_max, row_sum, O = lore_attention(Q, K, V, w, nthreads)
+    S_head = np.empty((b, h_q, n))
+    rc = _lib().ora_lore_scores(b, n, h_q, h_kv, d, w, m, t, float(eps), float(lambda_l),
+                                _ptr(Q), _ptr(K), _ptr(V), _ptr(R), _ptr(omega),
+                                _ptr(row_max), _ptr(row_sum), _ptr(O), _ptr(S_head),
+                                int(nthreads))
+    if rc != 0:
+        raise ValueError("ora_lore_scores: invalid shape (%d)" % rc)
+    S = S_head.reshape(b, h_kv, h_q // h_kv, n).mean(axis=2)
+    return {"S": S, "S_head": S_head, "row_max": row_max, "row_sum": row_sum, "O": O}
+
+
+def pooled_scores(S, n_sink, w, chunk):
+    """Chunk pooling ("adjacent-token grouping", chunk = 4 in the LORE-KV
+    Hyperparameters table): each candidate gets the mean score of the
+    candidates in its aligned chunk [chunk*floor(i/chunk), +chunk).
+    Candidates are [n_sink, n - w); protected tokens get NaN.
+    """
+    S = _f64(S)
+    n = S.shape[-1]
+    flat = S.reshape(-1, n)
+    idx = np.arange(n)
+    cand = (idx >= n_sink) & (idx < n - w)
+    cid = idx // chunk
+    counts = np.bincount(cid[cand], minlength=cid[-1] + 1)
+    P = np.full(flat.shape, np.nan)
+    for row in range(flat.shape[0]):
+        sums = np.bincount(cid[cand], weights=flat[row, cand], minlength=cid[-1] + 1)
+        P[row, cand] = sums[cid[cand]] / counts[cid[cand]]
+    return P.reshape(S.shape)
+
+
+def topb_select(S, *, n_sink, w, chunk, budget):
+    """Kept token indices per KV head, ascending.
+
+    LORE-KV page, Eq. 8: each KV head keeps the protected set (the attention
+    sink(s) [0, n_sink) and the window [n - w, n)) plus its top-B candidates,
+    ranked by pooled score descending, ties by lower index.
+    Returns (kept [..][n_keep] int64, pooled [..][n]).
+    """
+    S = _f64(S)
+    n = S.shape[-1]
+    P = pooled_scores(S, n_sink, w, chunk)
+    flat = P.reshape(-1, n)
+    cand = np.arange(n_sink, n - w)
+    protected = np.concatenate([np.arange(n_sink), np.arange(n - w, n)])
+    out = []
+    for row in range(flat.shape[0]):
+        order = np.lexsort((cand, -flat[row, cand]))  # last key primary: score desc, then index asc
+        chosen = cand[order[:budget]]
+        out.append(np.sort(np.concatenate([protected, chosen])))
+    kept = np.stack(out).reshape(S.shape[:-1] + (len(out[0]),))
+    return kept.astype(np.int64), P
+
+
+def compact(K, V, kept):
+    """Gather the kept rows: K'[..][r] = K[..][kept[r]] (decoding then runs on
+    the compressed cache, LORE-KV Method).  Works on any dtype, exact copy."""
+    K = np.asarray(K); V = np.asarray(V); kept = np.asarray(kept)
+    idx = kept[..., None].repeat(K.shape[-1], axis=-1)
+    return np.take_along_axis(K, idx, axis=-2), np.take_along_axis(V, idx, axis=-2)
+
+
+# --------------------------------------------------------------------------
+# H2O
+# --------------------------------------------------------------------------
+
+def h2o_prefill_acc(Qp, Kp):
+    """Accumulated attention of every prompt token over the causal prompt.
+
+    H2O page, 3.4: the accumulated score of a token is the sum of the attention
+    weights it receives from the tokens after it (and itself); row r attends to
+    keys 0..r with softmax(q.k / sqrt(d)).  Qp, Kp [..][P][d] -> acc [..][P].
+    """
+    Qp, Kp = _f64(Qp), _f64(Kp)
+    P, d = Kp.shape[-2:]
+    Qf = Qp.reshape(-1, P, d); Kf = Kp.reshape(-1, P, d)
+    acc = np.empty((Qf.shape[0], P))
+    future = np.triu(np.ones((P, P), dtype=bool), k=1)
+    for row in range(Qf.shape[0]):
+        s = Qf[row] @ Kf[row].T / math.sqrt(d)
+        s[future] = -np.inf
+        s -= s.max(axis=1, keepdims=True)
+        a = np.exp(s)
+        a /= a.sum(axis=1, keepdims=True)
+        acc[row] = a.sum(axis=0)
+    return acc.reshape(Qp.shape[:-1])
+
+
+def h2o_budget(cur_len, heavy_frac, recent_frac):
+    """(k_heavy, k_recent) for the current length: floor of each fraction."""
+    return int(heavy_frac * cur_len), int(recent_frac * cur_len)
+
+
+class H2OOracle:
+    """Step-by-step H2O eviction over independent (sequence, head) rows.
+
+    H2O page: the cache keeps the recent tokens plus the heavy hitters by
+    accumulated attention (3.2); each step the new query attends over the
+    retained cache and itself, its probabilities are added to the
+    accumulators (o~_i = o~_{i-1} + o_i), and if the cache is over budget the
+    retained non-recent token with the lowest accumulated score is evicted
+    (ties: the later position goes first), at most one per step (Def. 2.1).
+    The prompt is reduced to the budget by its causal column sums before the
+    first decode step.
+
+    State per row: pos [cap] (-1 = empty), acc [cap], K, V [cap][d], fp64.
+    Slot order is the oracle's own and carries no meaning.
+    """
+
+    def __init__(self, Qp, Kp, Vp, heavy_frac, recent_frac, cap):
+        Qp, Kp, Vp = _f64(Qp), _f64(Kp), _f64(Vp)
+        P, d = Kp.shape[-2:]
+        self.rows = int(np.prod(Kp.shape[:-2]))
+        self.d, self.cap = d, cap
+        self.heavy_frac, self.recent_frac = heavy_frac, recent_frac
+        acc = h2o_prefill_acc(Qp, Kp).reshape(self.rows, P)
+        self.prefill_acc = acc.copy()
+        k_h, k_r = h2o_budget(P, heavy_frac, recent_frac)
+        kept, _ = topb_select(acc, n_sink=0, w=k_r, chunk=1, budget=k_h)
+        if kept.shape[1] > cap:
+            raise ValueError("cap too small for the prompt budget")
+        self.pos = np.full((self.rows, cap), -1, dtype=np.int64)
+        self.acc = np.zeros((self.rows, cap))
+        self.K = np.zeros((self.rows, cap, d)); self.V = np.zeros((self.rows, cap, d))
+        Kf = Kp.reshape(self.rows, P, d); Vf = Vp.reshape(self.rows, P, d)
+        nk = kept.shape[1]
+        for row in range(self.rows):
+            self.pos[row, :nk] = kept[row]
+            self.acc[row, :nk] = acc[row, kept[row]]
+            self.K[row, :nk] = Kf[row, kept[row]]
+            self.V[row, :nk] = Vf[row, kept[row]]
+        self.cur_len = P
+        self.kept_prompt = kept
+        self.evicted_mass = np.zeros(self.rows)
+
+    def attend(self, q, k, v):
+        """Append the new token and accumulate its query's attention.
+
+        q, k, v [rows][d].  Returns (o [rows][d], probs [rows][cap]).
+        """
+        q, k, v = _f64(q).reshape(self.rows, self.d), _f64(k).reshape(self.rows, self.d), \
+            _f64(v).reshape(self.rows, self.d)
+        self.cur_len += 1
+        for row in range(self.rows):
+            free = np.nonzero(self.pos[row] < 0)[0]
+            if free.size == 0:
+                raise RuntimeError("no free slot")
+            s = free[0]
+            self.pos[row, s] = self.cur_len - 1
+            self.acc[row, s] = 0.0
+            self.K[row, s] = k[row]
+            self.V[row, s] = v[row]
+        valid = self.pos >= 0
+        logits = np.einsum("rcd,rd->rc", self.K, q) / math.sqrt(self.d)
+        logits[~valid] = -np.inf
+        logits -= logits.max(axis=1, keepdims=True)
+        a = np.exp(logits)
+        a /= a.sum(axis=1, keepdims=True)
+        self.acc += a
+        o = np.einsum("rc,rcd->rd", a, self.V)
+        return o, a
+
+    def choose(self):
+        """Slot each row would evict now (-1 if within budget): the lowest
+        accumulated score among retained non-recent tokens, ties to the
+        later position."""
+        k_h, k_r = h2o_budget(self.cur_len, self.heavy_frac, self.recent_frac)
+        out = np.full(self.rows, -1, dtype=np.int64)
+        for row in range(self.rows):
+            valid = self.pos[row] >= 0
+            if valid.sum() <= k_h + k_r:
+                continue
+            cand = np.nonzero(valid & (self.pos[row] < self.cur_len - k_r))[0]
+            order = np.lexsort((-self.pos[row, cand], self.acc[row, cand]))
+            out[row] = cand[order[0]]
+        return out
+
+    def evict(self, slots):
+        for row, s in enumerate(np.asarray(slots).reshape(-1)):
+            if s >= 0:
+                self.evicted_mass[row] += self.acc[row, s]
+                self.pos[row, s] = -1
+                self.acc[row, s] = 0.0
+
+    def retained(self, row):
+        """{position: accumulated score} of one row's cache."""
+        sl = np.nonzero(self.pos[row] >= 0)[0]
+        return {int(self.pos[row, s]): float(self.acc[row, s]) for s in sl}
