@@ -1,0 +1,257 @@
+"""Benchmark: LORE-KV scoring + top-B + compaction, one MI355X.
+
+A step is one eviction pass over every layer of the Llama-3.1-8B-shaped 128K
+workload: for each of the 32 resident layers (n = 131072 tokens, 32 query /
+8 KV heads, d = 128, d_model = 4096, bf16), kvscore_probs -> kvscore_deletion
+-> kvscore_topb_select -> kv_compact.  Inputs are seeded synthetic data
+generated on the device before timing (kvsynth recipe 'facts').
+
+Prints one JSON line.  value = KV tokens scored and compacted per second,
+counting n * H_kv tokens per layer.  The roofline object covers the kernel
+with the largest share of the timed region, from per-launch HIP event timing
+inside the library (kvs_timing_*).  cpu_baseline times the fp64 oracle on a
+bounded sample of the same workload on the host cores.  The H2O OPT-30B decode
+workload is measured after the main timed region and reported under "h2o".
+
+Usage: python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--layers 32]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def kernel_work(cfg):
+    """Algorithmic work per launch, per kernel, for one layer of cfg.
+
+    Flops count the Gram-form contractions the method needs (QK^T and AV of
+    pass 1, V.G_h for N, V.y for the cross term, W_h^T W_h); the logit
+    recompute of pass 2 and the lo half of y are extra work and not counted.
+    Bytes count one read of the operands and one write of the results.
+    """
+    b, n, hq, hk, d, D, nq = cfg.batch, cfg.n, cfg.h_q, cfg.h_kv, cfg.d, cfg.d_model, cfg.n_q
+    s = 2  # bytes per bf16 element
+    kv_bytes = 2 * b * hk * n * d * s
+    n_keep = cfg.n_keep
+    return {
+        "attn_partial": {"flops": 2 * (2 * nq * n * d) * hq * b, "bytes": kv_bytes, "bound": "mfma"},
+        "vnorm": {"flops": 2 * n * d * d * hq * b, "bytes": kv_bytes // 2, "bound": "mfma"},
+        "score_lore": {"flops": 2 * nq * n * d * hq * b, "bytes": kv_bytes + 4 * b * hk * n,
+                       "bound": "mfma"},
+        "gram": {"flops": 2 * D * d * d * hq, "bytes": D * hq * d * s, "bound": "mfma"},
+        "compact": {"flops": 0, "bytes": 2 * 2 * b * hk * n_keep * d * s, "bound": "hbm"},
+        "topb_select": {"flops": 0, "bytes": 4 * b * hk * n + 4 * b * hk * n_keep, "bound": "hbm"},
+    }
+
+
+def roofline_of(name, work, avg_ms):
+    w = work.get(name)
+    if w is None:
+        return None
+    if w["bound"] == "mfma":
+        achieved = w["flops"] / (avg_ms * 1e-3) / 1e12
+        return {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "algorithmic_per_launch": w["flops"], "avg_launch_ms": round(avg_ms, 4)}
+    achieved = w["bytes"] / (avg_ms * 1e-3) / 1e9
+    return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "algorithmic_per_launch": w["bytes"], "avg_launch_ms": round(avg_ms, 4)}
+
+
+def cpu_baseline(cfg, inp, max_seconds_hint=30.0):
+    """fp64 oracle on one (layer 0, KV head 0) unit: all n tokens, its G
+    query heads, selection and compaction of that head."""
+    import numpy as np
+    import oracle
+    G, d = cfg.group, cfg.d
+    Q = inp["Q"][:, :G].double().cpu().numpy()
+    K = inp["K"][:, :1].double().cpu().numpy()
+    V = inp["V"][:, :1].double().cpu().numpy()
+    W = inp["W_O"][:, :G * d].double().cpu().numpy()
+    om = inp["omega"].double().cpu().numpy()
+    threads = len(os.sched_getaffinity(0))
+    R = oracle.projection_factors(W, G, d)
+    t0 = time.perf_counter()
+    r = oracle.lore_scores(Q, K, V, W, om, w=cfg.w, m=cfg.m, t=cfg.t, eps=cfg.eps,
+                           lambda_l=cfg.lambda_l, nthreads=threads, R=R)
+    kept, _ = oracle.topb_select(r["S"], n_sink=cfg.n_sink, w=cfg.w, chunk=cfg.chunk,
+                                 budget=cfg.budget)
+    oracle.compact(K, V, kept)
+    dt = time.perf_counter() - t0
+    tokens = cfg.n  # one KV head of one sequence
+    return {"value": round(tokens / dt, 1), "unit": "KV tokens/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "layer 0, sequence 0, KV head 0: %d tokens x %d query heads, fp64 "
+                      "(scores, top-B, compaction); full layer = %d such units"
+                      % (cfg.n, G, cfg.batch * cfg.h_kv)}
+
+
+def bench_h2o(kv, torch, dev):
+    """H2O decode on the OPT-30B-shaped layer: prefill + 512 steps."""
+    from kvsynth import OPT30B_H2O, h2o_inputs
+    cfg = OPT30B_H2O
+    inp = h2o_inputs(cfg, device=dev)
+    cache = kv.H2OCache(cfg.batch, cfg.heads, cfg.d, cfg.cap, torch.float16, cfg.heavy_frac,
+                        cfg.recent_frac, dev)
+    st = torch.cuda.current_stream()
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    torch.cuda.synchronize()
+    kv.kvs_timing_reset()
+    kv.kvs_timing_enable(True)
+    e0.record(st)
+    cache.prefill(inp["Qp"], inp["Kp"], inp["Vp"])
+    e1.record(st)
+    slots = 0
+    for s in range(cfg.steps):
+        cache.step(inp["q"][s], inp["k"][s], inp["v"][s])
+        k_h, k_r = cache.budget(cache.cur_len)
+        slots += min(k_h + k_r + 1, cache.cur_len)
+    e2.record(st)
+    torch.cuda.synchronize()
+    recs = kv.kvs_timing_records()
+    kv.kvs_timing_enable(False)
+    kv.kvs_timing_reset()
+    dec = [ms for nm, ms in recs if nm == "h2o_decode"]
+    rows = cfg.batch * cfg.heads
+    # bytes per step: K and V of the retained slots, acc read+write, slot map, q/k/v/O
+    avg_slots = slots / cfg.steps
+    step_bytes = rows * (avg_slots * (2 * cfg.d * 2 + 8) + cfg.cap * 4 + 4 * cfg.d * 2)
+    dec_ms = sum(dec) / len(dec)
+    hbm = step_bytes / (dec_ms * 1e-3) / 1e9
+    return {"workload": cfg.name, "prefill_ms": round(e0.elapsed_time(e1), 3),
+            "decode_ms_total": round(e1.elapsed_time(e2), 3),
+            "decode_step_kernel_ms": round(dec_ms, 4),
+            "slots_attended_per_s": round(rows * slots / (e1.elapsed_time(e2) * 1e-3), 1),
+            "roofline": {"kernel": "h2o_decode", "bound": "hbm", "achieved": round(hbm, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(hbm / PEAK_HBM_GBS, 4),
+                         "traffic": None}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--config", default="llama3.1-8b-128k-32layers")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-h2o", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the scoring path needs no collectives, and this "
+              "build runs on a single MI355X (see the sharding notes). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_eviction_amd as kv
+    from kvsynth import LORE_CONFIGS, lore_inputs, TORCH_DTYPES
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    cfg = LORE_CONFIGS[args.config]
+    layers = args.layers or cfg.layers
+    dt = TORCH_DTYPES[cfg.dtype]
+    print("[bench] generating %d layers of %s on the device" % (layers, cfg.name),
+          file=sys.stderr, flush=True)
+    data = []
+    for l in range(layers):
+        inp = lore_inputs(cfg, layer=l, device=dev)
+        data.append({k: inp[k].contiguous() for k in ("Q", "K", "V", "W_O", "omega")})
+    desc = kv.lore_desc(batch=cfg.batch, n=cfg.n, h_q=cfg.h_q, h_kv=cfg.h_kv, d=cfg.d,
+                        d_model=cfg.d_model, w=cfg.w, m=cfg.m, t=cfg.t, n_sink=cfg.n_sink,
+                        chunk=cfg.chunk, budget=cfg.budget, eps=cfg.eps,
+                        lambda_l=cfg.lambda_l, dtype=dt)
+    ev = kv.LoreEviction(desc, dev)
+    outs = [(torch.empty(cfg.batch, cfg.h_kv, desc.n_keep, cfg.d, dtype=dt, device=dev),
+             torch.empty(cfg.batch, cfg.h_kv, desc.n_keep, cfg.d, dtype=dt, device=dev))
+            for _ in range(layers)]
+
+    def step():
+        for l in range(layers):
+            x = data[l]
+            ev.run(x["Q"], x["K"], x["V"], x["W_O"], x["omega"], outs[l][0], outs[l][1])
+
+    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    kv.kvs_timing_reset()
+    kv.kvs_timing_enable(True)
+    print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    start.record(st)
+    for _ in range(args.steps):
+        step()
+    stop.record(st)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    recs = kv.kvs_timing_records()
+    kv.kvs_timing_enable(False)
+    kv.kvs_timing_reset()
+
+    per = {}
+    for nm, ms in recs:
+        p = per.setdefault(nm, [0, 0.0])
+        p[0] += 1
+        p[1] += ms
+    ms_per_step = total_ms / args.steps
+    tokens = cfg.batch * cfg.n * cfg.h_kv * layers * args.steps
+    value = tokens / (total_ms * 1e-3)
+    work = kernel_work(cfg)
+    kernels = {nm: {"launches": c, "avg_ms": round(t / c, 4),
+                    "share": round(t / total_ms, 4)} for nm, (c, t) in per.items()}
+    dominant = max(per, key=lambda k: per[k][1])
+    roof = roofline_of(dominant, work, per[dominant][1] / per[dominant][0])
+    others = {nm: roofline_of(nm, work, per[nm][1] / per[nm][0]) for nm in per if nm in work}
+    credited = sum(w["flops"] for w in work.values())
+    layer_ms = ms_per_step / layers
+
+    out = {
+        "metric": "KV tokens scored+compacted/sec per layer (n*H_kv)",
+        "value": round(value, 1),
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, generated on device)",
+        "config": {"workload": cfg.name, "layers": layers, "batch": cfg.batch, "n": cfg.n,
+                   "h_q": cfg.h_q, "h_kv": cfg.h_kv, "d": cfg.d, "d_model": cfg.d_model,
+                   "w": cfg.w, "m": cfg.m, "t": cfg.t, "budget": cfg.budget, "chunk": cfg.chunk},
+        "roofline": roof,
+        "layer_ms": round(layer_ms, 4),
+        "layer_mfma_frac": round(credited / (layer_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kernels": kernels,
+        "kernel_rooflines": others,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, data[0])
+    if not args.no_h2o:
+        print("[bench] H2O decode", file=sys.stderr, flush=True)
+        del data
+        torch.cuda.empty_cache()
+        out["h2o"] = bench_h2o(kv, torch, dev)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

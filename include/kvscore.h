@@ -1,0 +1,251 @@
+/*
+ * kvscore.h -- C ABI of the KV-cache scoring and eviction library (gfx950).
+ *
+ * The library scores every cached key/value token of every KV head against a
+ * set of scoring queries, keeps each head's top-B tokens plus a protected set,
+ * and compacts the cache.  Two methods are covered:
+ *
+ *  * LORE-KV (project page "Monte Carlo Estimation for KV-Cache Eviction",
+ *    Method section): the projected deletion score of Eqs. 5-7 under the
+ *    w prompt-window queries and the M x T Monte Carlo lookahead queries,
+ *    per-KV-head top-B selection with the attention sink and window protected
+ *    (Eq. 8), chunk pooling ("chunk", Hyperparameters table), compaction.
+ *  * H2O (summary page "H2O: Heavy-Hitter Oracle", 3.4 and System
+ *    Implementation Details): accumulated attention per cached token, and the
+ *    decode-time eviction of the lowest-accumulated non-recent token from a
+ *    preallocated slot cache.
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is a DEVICE pointer to memory the caller owns and
+ *    keeps alive until the enqueued work has finished.  The library keeps no
+ *    device memory between calls; scratch comes from a caller workspace.
+ *  - Tensors are dense, row-major, in the layouts stated per argument.
+ *    Element type of Q, K, V, W_O (and of the H2O inputs) is the descriptor's
+ *    dtype; statistics and scores are fp32; indices are int32.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *    the default stream).  No call synchronises the device or copies between
+ *    host and device.
+ *  - Arguments are checked on the host before anything is enqueued.  A failed
+ *    check returns KVS_ERR_INVALID / KVS_ERR_UNSUPPORTED / KVS_ERR_WORKSPACE
+ *    and enqueues nothing.  A failed launch returns KVS_ERR_HIP.  The reason
+ *    is available from kvs_last_error() (thread-local).  Nothing aborts or
+ *    prints.
+ *  - Outputs must not alias inputs unless an argument says it is in/out.
+ *  - Calls on one stream run in order; calls on different streams that share
+ *    a workspace race.
+ */
+#ifndef KVSCORE_H
+#define KVSCORE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KVS_F32 = 0, KVS_BF16 = 1, KVS_F16 = 2 } kvs_dtype;
+
+typedef enum {
+  KVS_OK = 0,
+  KVS_ERR_INVALID = 1,     /* malformed shape, null pointer, out-of-range hyperparameter */
+  KVS_ERR_UNSUPPORTED = 2, /* well-formed but outside what the kernels implement */
+  KVS_ERR_WORKSPACE = 3,   /* workspace missing or smaller than kvs_lore_workspace_bytes() */
+  KVS_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} kvs_status;
+
+/*
+ * One LORE-KV eviction over one layer of `batch` independent sequences.
+ *
+ *  n        cached tokens per sequence and KV head (the prompt length).
+ *  h_q,h_kv query heads and KV heads; query head h reads KV head h/(h_q/h_kv).
+ *           h_q % h_kv == 0 and the group size h_q/h_kv is at most 16.
+ *  d        head dimension, 64 or 128.
+ *  d_model  rows of W_O.
+ *  w,m,t    scoring rows per query head: n_q = w + m*t, 1 <= n_q <= 64.
+ *           Rows 0..w-1 are the window queries of the last w prompt tokens
+ *           (LORE-KV "Prefill"); row r < w sits at position n-w+r and attends
+ *           to tokens 0..n-w+r.  Row w + j*t + u is lookahead query u of
+ *           trajectory j (Eq. 1) and attends to all n tokens.
+ *  n_sink   protected prefix (the attention sink); the last w tokens are
+ *           protected too.  Candidates are [n_sink, n - w); n >= n_sink + w.
+ *  chunk    adjacent-token grouping: a candidate's ranking score is the mean
+ *           score of the candidates in its aligned group [chunk*floor(i/chunk),
+ *           +chunk).  chunk >= 1.
+ *  budget   B: candidates kept per KV head.  n_keep = n_sink + min(B, n-n_sink-w) + w.
+ *  eps      the renormalisation guard of Eq. 5 (>= 0).
+ *  lambda_l weight of the lookahead term in Eq. 7.
+ *  dtype    element type of Q, K, V and W_O.
+ *
+ * Scores use softmax(q.k / sqrt(d)) probabilities a, attention outputs
+ * o = sum_i a_i v_i, e = a/(1-a+eps) * ||W_h (v_i - o)|| with W_h the d_model
+ * x d column slice h*d..h*d+d-1 of W_O, the arithmetic mean over each query
+ * set (window; each trajectory), lookahead trajectories weighted by omega
+ * and lambda_l, and the mean over the query heads of a KV head's group.
+ */
+typedef struct {
+  int32_t batch, n, h_q, h_kv, d, d_model;
+  int32_t w, m, t;
+  int32_t n_sink, chunk, budget;
+  float eps, lambda_l;
+  int32_t dtype; /* kvs_dtype */
+} kvs_lore_desc;
+
+/* Bytes of workspace any LORE entry point below needs for `desc` (0 if the
+ * descriptor is invalid; kvs_last_error() then says why).  One workspace may
+ * serve all of them in turn on one stream. */
+size_t kvs_lore_workspace_bytes(const kvs_lore_desc *desc);
+
+/*
+ * Pass 1: softmax statistics and attention outputs of the scoring rows.
+ * (LORE-KV Method: a_{q,i} and o_q of Eq. 5.)
+ *
+ *  Q        [batch][h_q][n_q][d]      scoring queries (window rows first).
+ *  K, V     [batch][h_kv][n][d]       the cache.
+ *  row_max  [batch][h_q][n_q] fp32    out: max_i q.k_i / sqrt(d) over visible i.
+ *  row_sum  [batch][h_q][n_q] fp32    out: sum_i exp(q.k_i/sqrt(d) - row_max).
+ *  O        [batch][h_q][n_q][d] fp32 out: o_q = sum_i a_{q,i} v_i.
+ *  ws, ws_bytes                       workspace (>= kvs_lore_workspace_bytes).
+ */
+kvs_status kvscore_probs(const kvs_lore_desc *desc, const void *Q, const void *K, const void *V,
+                         float *row_max, float *row_sum, float *O,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Pass 2: projected deletion score of every cached token, per KV head
+ * (LORE-KV "Projected deletion score", Eqs. 5-7, grouped per KV head as the
+ * selection of Eq. 8 needs).
+ *
+ *  Q, K, V                  as for kvscore_probs.
+ *  W_O      [d_model][h_q*d] the attention output projection (linear-layer layout).
+ *  omega    [batch][m] fp32  trajectory reliability weights (Eq. 10 output).
+ *  row_max, row_sum, O      kvscore_probs outputs for the same inputs.
+ *  S        [batch][h_kv][n] fp32 out: the KV head's score of every token
+ *           (protected tokens are scored too; selection ignores them).
+ *
+ * For bf16 input the value-side products (V.G_h, V.y, P.V) run in fp16 after
+ * an exact bf16->fp16 conversion of V; |V| must stay below 65504.
+ */
+kvs_status kvscore_deletion(const kvs_lore_desc *desc, const void *Q, const void *K, const void *V,
+                            const void *W_O, const float *omega,
+                            const float *row_max, const float *row_sum, const float *O,
+                            float *S, void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of workspace kvscore_topb_select needs (0 if the selection fields of
+ * the descriptor are invalid).  No larger than kvs_lore_workspace_bytes(). */
+size_t kvs_topb_workspace_bytes(const kvs_lore_desc *desc);
+
+/*
+ * Per-KV-head top-B selection (LORE-KV Eq. 8 with chunk pooling).
+ * Reads only batch, h_kv, n, n_sink, w, chunk and budget of the descriptor,
+ * so it also serves any other per-row score (the H2O prompt reduction uses
+ * n_sink = 0, w = recent budget, chunk = 1, budget = heavy budget).
+ *
+ *  S       [batch][h_kv][n] fp32   scores (kvscore_deletion output, or any score).
+ *  kept    [batch][h_kv][n_keep] int32 out: kept token indices, ascending:
+ *          [0, n_sink) + the B best candidates by (pooled score desc, index asc)
+ *          + [n - w, n).
+ *  pooled  [batch][h_kv][n] fp32 out, nullable: each candidate's pooled score;
+ *          protected tokens get NaN.
+ * NaN scores rank above every number.
+ */
+kvs_status kvscore_topb_select(const kvs_lore_desc *desc, const float *S, int32_t *kept,
+                               float *pooled, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Gather kept rows into a compact cache (LORE-KV: decoding then runs on the
+ * compressed cache).  Also used to load the H2O slot cache after the prompt
+ * reduction.
+ *
+ *  K, V      [batch][heads][n_src][d]  (dtype)   source cache.
+ *  kept      [batch][heads][n_keep] int32         rows to copy.
+ *  K_out, V_out [batch][heads][cap_dst][d]        out: rows 0..n_keep-1 get the copies;
+ *            rows n_keep..cap_dst-1 are left untouched.
+ *  pos_out   [batch][heads][cap_dst] int32, nullable   out: kept index per row, -1 beyond n_keep.
+ *  score_in  [batch][heads][n_src] fp32, nullable       optional per-token score to carry along;
+ *  score_out [batch][heads][cap_dst] fp32               out (needed iff score_in): gathered, 0 beyond n_keep.
+ * The copy is bit-exact.  A kept index outside [0, n_src) copies nothing
+ * (its output rows are left as they were) and records -1 / 0.
+ */
+kvs_status kv_compact(int32_t batch, int32_t heads, int32_t n_src, int32_t n_keep, int32_t cap_dst,
+                      int32_t d, int32_t dtype, const void *K, const void *V, const int32_t *kept,
+                      void *K_out, void *V_out, int32_t *pos_out,
+                      const float *score_in, float *score_out, void *stream);
+
+/* H2O modes. */
+typedef enum {
+  KVS_H2O_PREFILL = 0, /* accumulated attention of a causal prompt */
+  KVS_H2O_DECODE = 1   /* one decode step on the slot cache */
+} kvs_h2o_mode;
+
+/*
+ *  batch, heads, d   rows are (sequence, head) pairs, each independent (MHA).
+ *  d                 64 or 128.
+ *  cap               PREFILL: the prompt length P.  DECODE: slots per row.
+ *  cur_len           DECODE: sequence length after appending this step's token
+ *                    (the new token's position is cur_len - 1).
+ *  k_heavy, k_recent DECODE: budget for this step; a token is recent if its
+ *                    position is >= cur_len - k_recent.
+ *  dtype             element type of q, K, V, k_new, v_new, O.
+ */
+typedef struct {
+  int32_t batch, heads, d, cap;
+  int32_t cur_len, k_heavy, k_recent;
+  int32_t dtype;
+} kvs_h2o_desc;
+
+/*
+ * H2O accumulated attention (H2O page 3.4: the accumulated score of a token is
+ * the sum of the attention weights later queries give it; the new query
+ * attends over the retained cache and itself; o~_i = o~_{i-1} + o_i; the
+ * evictee is the retained non-recent token with the lowest accumulated score,
+ * later position first on ties, at most one per step, Def. 2.1).
+ *
+ * KVS_H2O_PREFILL:
+ *   q, K    [batch][heads][cap][d]  prompt queries and keys (row r attends to keys 0..r).
+ *   acc     [batch][heads][cap] fp32 out: acc_i = sum_{r >= i} a_{r,i}.
+ *   V, k_new, v_new, slot_pos, O, evict_slot: unused (may be NULL).
+ *   ws, ws_bytes: workspace of at least kvs_h2o_workspace_bytes(desc, mode).
+ *
+ * KVS_H2O_DECODE (one step; rows independent):
+ *   q, k_new, v_new [batch][heads][d]   this step's query, key and value.
+ *   K, V            [batch][heads][cap][d]  slot cache, in/out (the new token is
+ *                   written into the lowest-index free slot).
+ *   slot_pos        [batch][heads][cap] int32, in/out: position held by each slot,
+ *                   -1 = free.  At least one slot must be free on entry.
+ *   acc             [batch][heads][cap] fp32, in/out: accumulated attention per slot.
+ *   O               [batch][heads][d] (dtype), nullable: out, attention output.
+ *   evict_slot      [batch][heads] int32, nullable: out, slot evicted this step
+ *                   (its slot_pos becomes -1) or -1 if the row is within
+ *                   budget; -2 if the row had no free slot (nothing changed).
+ *   ws, ws_bytes: unused.
+ */
+size_t kvs_h2o_workspace_bytes(const kvs_h2o_desc *desc, int32_t mode);
+
+kvs_status kvscore_h2o_accumulate(const kvs_h2o_desc *desc, int32_t mode,
+                                  const void *q, void *K, void *V,
+                                  const void *k_new, const void *v_new,
+                                  int32_t *slot_pos, float *acc, void *O, int32_t *evict_slot,
+                                  void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Per-launch kernel timing, for benchmarks and profiling.  While enabled,
+ * every kernel the library launches is bracketed by two HIP events recorded
+ * on its launch stream (process-wide).  kvs_timing_read synchronises on the
+ * i-th record's stop event and returns the kernel's name (a static string)
+ * and its event-to-event time in milliseconds.  kvs_timing_reset waits for
+ * and drops every record.  Off by default.
+ */
+kvs_status kvs_timing_enable(int32_t on);
+int32_t kvs_timing_count(void);
+kvs_status kvs_timing_read(int32_t i, const char **kernel, float *ms);
+void kvs_timing_reset(void);
+
+/* Reason for the last non-OK status on the calling thread ("" if none). */
+const char *kvs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSCORE_H */

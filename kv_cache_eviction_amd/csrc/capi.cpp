@@ -1,0 +1,347 @@
+// C ABI of the library: argument checks, workspace planning and dispatch.
+// Every check runs on the host before anything is enqueued; see kvscore.h.
+#include "kvscore.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "launch.hpp"
+#include "timing.hpp"
+
+#define KVS_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_err;
+
+kvs_status fail(kvs_status st, const std::string &msg) {
+  g_err = msg;
+  return st;
+}
+
+kvs_status ok() {
+  g_err.clear();
+  return KVS_OK;
+}
+
+kvs_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(KVS_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+int n_pad_of(int n) { return (n + 63) / 64 * 64; }
+
+// Plans of the LORE workspace; every entry point lays out its scratch from
+// offset 0 of the same buffer.
+struct LorePlan {
+  kvs::SplitPlan split;
+  int gsplits;
+  size_t probs_bytes, deletion_bytes, topb_bytes;
+  // deletion layout
+  size_t off_gpart, off_gv, off_yhi, off_ylo, off_consts, off_n;
+  // probs layout
+  size_t off_pm, off_pl, off_po;
+};
+
+kvs_status check_lore(const kvs_lore_desc *d) {
+  if (!d) return fail(KVS_ERR_INVALID, "descriptor is NULL");
+  if (d->batch < 1 || d->n < 1 || d->h_q < 1 || d->h_kv < 1 || d->d_model < 1)
+    return fail(KVS_ERR_INVALID, "batch, n, h_q, h_kv and d_model must be >= 1");
+  if (d->h_q % d->h_kv != 0) return fail(KVS_ERR_INVALID, "h_q must be a multiple of h_kv");
+  if (d->h_q / d->h_kv > 16) return fail(KVS_ERR_UNSUPPORTED, "query-head group larger than 16");
+  if (d->d != 64 && d->d != 128) return fail(KVS_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  if (d->w < 0 || d->m < 0 || d->t < 0) return fail(KVS_ERR_INVALID, "w, m and t must be >= 0");
+  if (d->m > 0 && d->t < 1) return fail(KVS_ERR_INVALID, "t must be >= 1 when m > 0");
+  const long nq = (long)d->w + (long)d->m * d->t;
+  if (nq < 1 || nq > 64) return fail(KVS_ERR_UNSUPPORTED, "w + m*t must be in [1, 64]");
+  if (d->n_sink < 0 || d->budget < 0) return fail(KVS_ERR_INVALID, "n_sink and budget must be >= 0");
+  if ((long)d->n_sink + d->w > d->n) return fail(KVS_ERR_INVALID, "n must be >= n_sink + w");
+  if (d->chunk < 1) return fail(KVS_ERR_INVALID, "chunk must be >= 1");
+  if (d->n > (1 << 28)) return fail(KVS_ERR_UNSUPPORTED, "n above 2^28 tokens");
+  if (!(std::isfinite(d->eps) && d->eps >= 0.f)) return fail(KVS_ERR_INVALID, "eps must be finite and >= 0");
+  if (!std::isfinite(d->lambda_l)) return fail(KVS_ERR_INVALID, "lambda_l must be finite");
+  if (d->dtype != KVS_F32 && d->dtype != KVS_BF16 && d->dtype != KVS_F16)
+    return fail(KVS_ERR_INVALID, "unknown dtype");
+  return ok();
+}
+
+size_t topb_bytes_of(const kvs_lore_desc *d);
+
+LorePlan plan_lore(const kvs_lore_desc *d) {
+  LorePlan p{};
+  const size_t heads = (size_t)d->batch * d->h_q;
+  const size_t D = d->d;
+  const size_t vbytes = d->dtype == KVS_F32 ? 4 : 2;  // value-side element type
+  p.split = kvs::attn_split_plan(d->batch * d->h_kv, d->n);
+  const size_t S = p.split.splits;
+  p.off_pm = 0;
+  p.off_pl = align_up(p.off_pm + heads * S * 64 * 4);
+  p.off_po = align_up(p.off_pl + heads * S * 64 * 4);
+  p.probs_bytes = align_up(p.off_po + heads * S * D * 64 * 4);
+
+  p.gsplits = kvs::gram_splits(d->h_q, d->d_model);
+  p.off_gpart = 0;
+  p.off_gv = align_up(p.off_gpart + (size_t)p.gsplits * d->h_q * D * D * 4);
+  p.off_yhi = align_up(p.off_gv + (size_t)d->h_q * D * D * vbytes);
+  p.off_ylo = align_up(p.off_yhi + heads * 64 * D * vbytes);
+  p.off_consts = align_up(p.off_ylo + heads * 64 * D * vbytes);
+  p.off_n = align_up(p.off_consts + heads * 64 * 16);
+  p.deletion_bytes = align_up(p.off_n + heads * (size_t)n_pad_of(d->n) * 4);
+
+  p.topb_bytes = topb_bytes_of(d);
+  return p;
+}
+
+// Selection reads only the shape and selection fields of the descriptor.
+kvs_status check_select(const kvs_lore_desc *d) {
+  if (!d) return fail(KVS_ERR_INVALID, "descriptor is NULL");
+  if (d->batch < 1 || d->h_kv < 1 || d->n < 1)
+    return fail(KVS_ERR_INVALID, "batch, h_kv and n must be >= 1");
+  if (d->n_sink < 0 || d->w < 0 || d->budget < 0)
+    return fail(KVS_ERR_INVALID, "n_sink, w and budget must be >= 0");
+  if ((long)d->n_sink + d->w > d->n) return fail(KVS_ERR_INVALID, "n must be >= n_sink + w");
+  if (d->chunk < 1) return fail(KVS_ERR_INVALID, "chunk must be >= 1");
+  if (d->n > (1 << 28)) return fail(KVS_ERR_UNSUPPORTED, "n above 2^28 tokens");
+  return ok();
+}
+
+size_t topb_bytes_of(const kvs_lore_desc *d) {
+  const size_t nchunks = ((size_t)d->n + d->chunk - 1) / d->chunk;
+  return align_up((size_t)d->batch * d->h_kv * nchunks * 4);
+}
+
+kvs_status check_ws(void *ws, size_t ws_bytes, size_t need) {
+  if (ws_bytes < need) {
+    char buf[160];
+    snprintf(buf, sizeof buf, "workspace of %zu bytes is smaller than the %zu bytes needed",
+             ws_bytes, need);
+    return fail(KVS_ERR_WORKSPACE, buf);
+  }
+  if (need > 0 && !ws) return fail(KVS_ERR_WORKSPACE, "workspace pointer is NULL");
+  return ok();
+}
+
+kvs::RowGeom lore_geom(const kvs_lore_desc *d) {
+  return kvs::RowGeom{0, d->n, d->w + d->m * d->t, d->w, d->h_q / d->h_kv};
+}
+
+template <typename T> T *at(void *base, size_t off) {
+  return reinterpret_cast<T *>(static_cast<char *>(base) + off);
+}
+
+}  // namespace
+
+KVS_API const char *kvs_last_error(void) { return g_err.c_str(); }
+
+KVS_API size_t kvs_lore_workspace_bytes(const kvs_lore_desc *desc) {
+  if (check_lore(desc) != KVS_OK) return 0;
+  const LorePlan p = plan_lore(desc);
+  size_t m = p.probs_bytes;
+  if (p.deletion_bytes > m) m = p.deletion_bytes;
+  if (p.topb_bytes > m) m = p.topb_bytes;
+  return m;
+}
+
+KVS_API kvs_status kvscore_probs(const kvs_lore_desc *desc, const void *Q, const void *K,
+                                 const void *V, float *row_max, float *row_sum, float *O,
+                                 void *ws, size_t ws_bytes, void *stream) {
+  kvs_status st = check_lore(desc);
+  if (st != KVS_OK) return st;
+  if (!Q || !K || !V || !row_max || !row_sum || !O)
+    return fail(KVS_ERR_INVALID, "kvscore_probs: a required pointer is NULL");
+  const LorePlan p = plan_lore(desc);
+  st = check_ws(ws, ws_bytes, p.probs_bytes);
+  if (st != KVS_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const kvs::RowGeom geo = lore_geom(desc);
+  float *pm = at<float>(ws, p.off_pm), *pl = at<float>(ws, p.off_pl), *po = at<float>(ws, p.off_po);
+  hipError_t e = kvs::launch_attn_partial(desc->dtype, desc->d, true, Q, K, V, geo, desc->batch,
+                                          desc->h_kv, p.split, pm, pl, po, s);
+  if (e != hipSuccess) return hip_status(e, "attention pass");
+  e = kvs::launch_attn_combine_lore(desc->d, pm, pl, po, desc->batch * desc->h_q, p.split.splits,
+                                    geo.nq, row_max, row_sum, O, s);
+  return hip_status(e, "attention combine");
+}
+
+KVS_API kvs_status kvscore_deletion(const kvs_lore_desc *desc, const void *Q, const void *K,
+                                    const void *V, const void *W_O, const float *omega,
+                                    const float *row_max, const float *row_sum, const float *O,
+                                    float *S, void *ws, size_t ws_bytes, void *stream) {
+  kvs_status st = check_lore(desc);
+  if (st != KVS_OK) return st;
+  if (!Q || !K || !V || !W_O || !row_max || !row_sum || !O || !S)
+    return fail(KVS_ERR_INVALID, "kvscore_deletion: a required pointer is NULL");
+  if (desc->m > 0 && !omega) return fail(KVS_ERR_INVALID, "kvscore_deletion: omega is NULL");
+  const LorePlan p = plan_lore(desc);
+  st = check_ws(ws, ws_bytes, p.deletion_bytes);
+  if (st != KVS_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const kvs::RowGeom geo = lore_geom(desc);
+  float *gpart = at<float>(ws, p.off_gpart);
+  void *gv = at<void>(ws, p.off_gv);
+  void *yhi = at<void>(ws, p.off_yhi), *ylo = at<void>(ws, p.off_ylo);
+  float4 *consts = at<float4>(ws, p.off_consts);
+  float *nn = at<float>(ws, p.off_n);
+  const int npad = n_pad_of(desc->n);
+  hipError_t e = kvs::launch_gram(desc->dtype, desc->d, W_O, desc->d_model, desc->h_q, p.gsplits,
+                                  gpart, s);
+  if (e != hipSuccess) return hip_status(e, "gram");
+  e = kvs::launch_deletion_prep(desc->dtype, desc->d, gpart, p.gsplits, O, row_max, row_sum, omega,
+                                desc->batch, desc->h_q, desc->n, geo.nq, desc->w, desc->m, desc->t,
+                                desc->lambda_l, gv, yhi, ylo, consts, s);
+  if (e != hipSuccess) return hip_status(e, "deletion prep");
+  e = kvs::launch_vnorm(desc->dtype, desc->d, V, gv, desc->batch, desc->n, npad, desc->h_q,
+                        desc->h_kv, nn, s);
+  if (e != hipSuccess) return hip_status(e, "value norms");
+  e = kvs::launch_score(desc->dtype, desc->d, 0, Q, K, V, yhi, ylo, consts, nn, npad, geo,
+                        desc->batch, desc->h_kv, desc->eps, 1.f / (float)geo.group, S, s);
+  return hip_status(e, "deletion score");
+}
+
+KVS_API size_t kvs_topb_workspace_bytes(const kvs_lore_desc *desc) {
+  if (check_select(desc) != KVS_OK) return 0;
+  return topb_bytes_of(desc);
+}
+
+KVS_API kvs_status kvscore_topb_select(const kvs_lore_desc *desc, const float *S, int32_t *kept,
+                                       float *pooled, void *ws, size_t ws_bytes, void *stream) {
+  kvs_status st = check_select(desc);
+  if (st != KVS_OK) return st;
+  if (!S || !kept) return fail(KVS_ERR_INVALID, "kvscore_topb_select: S or kept is NULL");
+  st = check_ws(ws, ws_bytes, topb_bytes_of(desc));
+  if (st != KVS_OK) return st;
+  const int n_cand = desc->n - desc->n_sink - desc->w;
+  const int B = desc->budget < n_cand ? desc->budget : n_cand;
+  const int n_keep = desc->n_sink + B + desc->w;
+  hipError_t e = kvs::launch_topb(S, desc->batch * desc->h_kv, desc->n, desc->n_sink, desc->w,
+                                  desc->chunk, desc->budget, n_keep, at<uint32_t>(ws, 0), kept,
+                                  pooled, static_cast<hipStream_t>(stream));
+  return hip_status(e, "top-B select");
+}
+
+KVS_API kvs_status kv_compact(int32_t batch, int32_t heads, int32_t n_src, int32_t n_keep,
+                              int32_t cap_dst, int32_t d, int32_t dtype, const void *K,
+                              const void *V, const int32_t *kept, void *K_out, void *V_out,
+                              int32_t *pos_out, const float *score_in, float *score_out,
+                              void *stream) {
+  if (batch < 1 || heads < 1 || n_src < 1 || n_keep < 0 || cap_dst < 1)
+    return fail(KVS_ERR_INVALID, "kv_compact: batch, heads, n_src, cap_dst must be >= 1, n_keep >= 0");
+  if (n_keep > n_src || n_keep > cap_dst)
+    return fail(KVS_ERR_INVALID, "kv_compact: n_keep exceeds n_src or cap_dst");
+  if (d != 64 && d != 128) return fail(KVS_ERR_UNSUPPORTED, "kv_compact: head dim must be 64 or 128");
+  if (dtype != KVS_F32 && dtype != KVS_BF16 && dtype != KVS_F16)
+    return fail(KVS_ERR_INVALID, "kv_compact: unknown dtype");
+  if (!K || !V || !K_out || !V_out || (n_keep > 0 && !kept))
+    return fail(KVS_ERR_INVALID, "kv_compact: a required pointer is NULL");
+  if ((score_in == nullptr) != (score_out == nullptr))
+    return fail(KVS_ERR_INVALID, "kv_compact: score_in and score_out go together");
+  const int row_bytes = d * (int)kvs::elem_bytes(dtype);
+  hipError_t e = kvs::launch_compact(batch * heads, n_src, n_keep, cap_dst, row_bytes, K, V, kept,
+                                     K_out, V_out, pos_out, score_in, score_out,
+                                     static_cast<hipStream_t>(stream));
+  return hip_status(e, "compaction");
+}
+
+namespace {
+
+kvs_status check_h2o(const kvs_h2o_desc *d, int mode) {
+  if (!d) return fail(KVS_ERR_INVALID, "descriptor is NULL");
+  if (d->batch < 1 || d->heads < 1 || d->cap < 1)
+    return fail(KVS_ERR_INVALID, "batch, heads and cap must be >= 1");
+  if (d->d != 64 && d->d != 128) return fail(KVS_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  if (d->dtype != KVS_F32 && d->dtype != KVS_BF16 && d->dtype != KVS_F16)
+    return fail(KVS_ERR_INVALID, "unknown dtype");
+  if (mode == KVS_H2O_PREFILL) {
+    if (d->cap > 1024) return fail(KVS_ERR_UNSUPPORTED, "prefill prompt longer than 1024");
+  } else if (mode == KVS_H2O_DECODE) {
+    if (d->cap > 2048) return fail(KVS_ERR_UNSUPPORTED, "decode slot count above 2048");
+    if (d->cur_len < 1 || d->k_heavy < 0 || d->k_recent < 0)
+      return fail(KVS_ERR_INVALID, "cur_len >= 1, k_heavy >= 0, k_recent >= 0 required");
+  } else {
+    return fail(KVS_ERR_INVALID, "unknown H2O mode");
+  }
+  return ok();
+}
+
+struct H2OPlan {
+  int group;
+  kvs::SplitPlan split;
+  size_t off_pm, off_pl, off_consts, bytes;
+};
+
+H2OPlan plan_h2o(const kvs_h2o_desc *d) {
+  H2OPlan p{};
+  p.group = (d->cap + 63) / 64;
+  p.split = kvs::attn_split_plan(d->batch * d->heads, d->cap);
+  const size_t heads = (size_t)d->batch * d->heads * p.group;
+  p.off_pm = 0;
+  p.off_pl = align_up(heads * p.split.splits * 64 * 4);
+  p.off_consts = align_up(p.off_pl + heads * p.split.splits * 64 * 4);
+  p.bytes = align_up(p.off_consts + heads * 64 * 16);
+  return p;
+}
+
+}  // namespace
+
+KVS_API size_t kvs_h2o_workspace_bytes(const kvs_h2o_desc *desc, int32_t mode) {
+  if (check_h2o(desc, mode) != KVS_OK) return 0;
+  if (mode == KVS_H2O_DECODE) return 0;
+  return plan_h2o(desc).bytes;
+}
+
+KVS_API kvs_status kvscore_h2o_accumulate(const kvs_h2o_desc *desc, int32_t mode, const void *q,
+                                          void *K, void *V, const void *k_new,
+                                          const void *v_new, int32_t *slot_pos, float *acc,
+                                          void *O, int32_t *evict_slot, void *ws, size_t ws_bytes,
+                                          void *stream) {
+  kvs_status st = check_h2o(desc, mode);
+  if (st != KVS_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mode == KVS_H2O_PREFILL) {
+    if (!q || !K || !acc) return fail(KVS_ERR_INVALID, "prefill: q, K and acc are required");
+    const H2OPlan p = plan_h2o(desc);
+    st = check_ws(ws, ws_bytes, p.bytes);
+    if (st != KVS_OK) return st;
+    const kvs::RowGeom geo{1, desc->cap, 64, 0, p.group};
+    float *pm = at<float>(ws, p.off_pm), *pl = at<float>(ws, p.off_pl);
+    float4 *consts = at<float4>(ws, p.off_consts);
+    hipError_t e = kvs::launch_attn_partial(desc->dtype, desc->d, false, q, K, nullptr, geo,
+                                            desc->batch, desc->heads, p.split, pm, pl, nullptr, s);
+    if (e != hipSuccess) return hip_status(e, "prefill row statistics");
+    e = kvs::launch_attn_combine_rows(pm, pl, desc->batch * desc->heads * p.group, p.split.splits,
+                                      p.group, desc->cap, consts, s);
+    if (e != hipSuccess) return hip_status(e, "prefill row combine");
+    e = kvs::launch_score(desc->dtype, desc->d, 1, q, K, nullptr, nullptr, nullptr, consts, nullptr,
+                          0, geo, desc->batch, desc->heads, 0.f, 1.f, acc, s);
+    return hip_status(e, "prefill column sums");
+  }
+  if (!q || !K || !V || !k_new || !v_new || !slot_pos || !acc)
+    return fail(KVS_ERR_INVALID, "decode: q, K, V, k_new, v_new, slot_pos and acc are required");
+  hipError_t e = kvs::launch_h2o_decode(desc->dtype, desc->d, desc->batch * desc->heads, desc->cap,
+                                        desc->cur_len, desc->k_heavy, desc->k_recent, q, K, V,
+                                        k_new, v_new,
+                                        slot_pos, acc, O, evict_slot, s);
+  return hip_status(e, "decode step");
+}
+
+KVS_API kvs_status kvs_timing_enable(int32_t on) {
+  kvs::timing_enable(on);
+  return ok();
+}
+
+KVS_API int32_t kvs_timing_count(void) { return kvs::timing_count(); }
+
+KVS_API kvs_status kvs_timing_read(int32_t i, const char **kernel, float *ms) {
+  if (!kernel || !ms) return fail(KVS_ERR_INVALID, "kvs_timing_read: NULL output");
+  const int rc = kvs::timing_read(i, kernel, ms);
+  if (rc == 1) return fail(KVS_ERR_INVALID, "kvs_timing_read: index out of range");
+  if (rc == 2) return fail(KVS_ERR_HIP, "kvs_timing_read: event query failed");
+  return ok();
+}
+
+KVS_API void kvs_timing_reset(void) { kvs::timing_reset(); }

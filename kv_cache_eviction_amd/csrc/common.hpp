@@ -1,0 +1,135 @@
+// Device-side building blocks shared by the gfx950 kernels.
+//
+// Matrix-core convention used everywhere (one 64-lane wavefront, 16x16 output):
+//   A fragment (16 rows x 32 k): lane l holds A[l % 16][8*(l/16) + e], e = 0..7
+//   B fragment (32 k x 16 cols): lane l holds B[8*(l/16) + e][l % 16]
+//   C/D (16 x 16, fp32):         lane l holds C[4*(l/16) + j][l % 16],  j = 0..3
+// bf16 and fp16 map to v_mfma_f32_16x16x32_{bf16,f16}.  fp32 runs the same
+// fragment shape as eight v_mfma_f32_16x16x4_f32 steps, step p consuming
+// element p of every lane, so k-slot (l/16) of step p is k = 8*(l/16) + p on
+// both operands and the contraction covers all 32 k.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvs {
+
+typedef __bf16 bf16;
+typedef _Float16 f16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+struct f32x8 { f32x4 lo, hi; };
+
+template <typename T> struct FragOf;
+template <> struct FragOf<bf16> { typedef bf16x8 type; };
+template <> struct FragOf<f16> { typedef f16x8 type; };
+template <> struct FragOf<float> { typedef f32x8 type; };
+
+// Element type of the value-side products (P.V, V.G_h, V.y): fp32 stays fp32,
+// 16-bit inputs run in fp16 (V converted exactly from bf16; P, G_h, y rounded
+// to fp16's 11-bit significand).
+template <typename T> struct ValueType { typedef f16 type; };
+template <> struct ValueType<float> { typedef float type; };
+
+__device__ __forceinline__ f32x4 mma(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const f16x8 &a, const f16x8 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const f32x8 &a, const f32x8 &b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[0], b.lo[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[1], b.lo[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[2], b.lo[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[3], b.lo[3], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[0], b.hi[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[1], b.hi[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[2], b.hi[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[3], b.hi[3], c, 0, 0, 0);
+  return c;
+}
+
+// ---- scalar conversions ----------------------------------------------------
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }
+
+// ---- fragment loads: 8 consecutive elements (16 B for 16-bit, 32 B for fp32) --
+template <typename T> __device__ __forceinline__ typename FragOf<T>::type load8(const T *p);
+template <> __device__ __forceinline__ bf16x8 load8<bf16>(const bf16 *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+template <> __device__ __forceinline__ f16x8 load8<f16>(const f16 *p) {
+  return *reinterpret_cast<const f16x8 *>(p);
+}
+template <> __device__ __forceinline__ f32x8 load8<float>(const float *p) {
+  f32x8 r;
+  r.lo = *reinterpret_cast<const f32x4 *>(p);
+  r.hi = *reinterpret_cast<const f32x4 *>(p + 4);
+  return r;
+}
+
+template <typename T> __device__ __forceinline__ typename FragOf<T>::type zero8();
+template <> __device__ __forceinline__ bf16x8 zero8<bf16>() { return bf16x8{}; }
+template <> __device__ __forceinline__ f16x8 zero8<f16>() { return f16x8{}; }
+template <> __device__ __forceinline__ f32x8 zero8<float>() { return f32x8{f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}}; }
+
+// Element e of a fragment, as fp32.
+__device__ __forceinline__ float frag_elem(const bf16x8 &f, int e) { return (float)f[e]; }
+__device__ __forceinline__ float frag_elem(const f16x8 &f, int e) { return (float)f[e]; }
+__device__ __forceinline__ float frag_elem(const f32x8 &f, int e) { return e < 4 ? f.lo[e] : f.hi[e - 4]; }
+
+// Build a fragment from 8 fp32 values.
+template <typename T> __device__ __forceinline__ typename FragOf<T>::type pack8(const float *v);
+template <> __device__ __forceinline__ bf16x8 pack8<bf16>(const float *v) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)v[e];
+  return r;
+}
+template <> __device__ __forceinline__ f16x8 pack8<f16>(const float *v) {
+  f16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (f16)v[e];
+  return r;
+}
+template <> __device__ __forceinline__ f32x8 pack8<float>(const float *v) {
+  return f32x8{f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]}};
+}
+
+// Convert a fragment to another element type (bf16 -> fp16 is exact in range).
+template <typename To, typename From>
+__device__ __forceinline__ typename FragOf<To>::type convert8(const typename FragOf<From>::type &f) {
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = frag_elem(f, e);
+  return pack8<To>(v);
+}
+
+// ---- 16-byte vector copies ---------------------------------------------------
+struct alignas(16) U128 { uint32_t x, y, z, w; };
+
+// ---- wave reductions ---------------------------------------------------------
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+__device__ __forceinline__ float wave_sum_xor(float v, int mask) {
+  return v + __shfl_xor(v, mask, 64);
+}
+
+// Fast hardware transcendentals (about 1 ulp).
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float hw_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace kvs

@@ -1,0 +1,515 @@
+// Pass 2 of the scoring path: LORE-KV's projected deletion score, and the
+// causal column sums H2O's prefill needs.
+//
+// LORE-KV ("Monte Carlo Estimation for KV-Cache Eviction", Method,
+// "Projected deletion score", Eqs. 5-7):
+//   e_{q,i} = a_{q,i} / (1 - a_{q,i} + eps) * ||W_h (v_i - o_q)||,
+//   S_i     = psi(E_{i,W}) + lambda_L sum_m omega_m psi(E_{i,m}),  psi = mean,
+// and the KV head's score is the mean over its query-head group.  The norm is
+// expanded in the Gram form  ||W_h(v - o)||^2 = N_i - 2 x_{q,i} + pi_q  with
+//   G_h = W_h^T W_h (d x d),  N_i = v_i^T G_h v_i,  y_q = G_h o_q,
+//   x_{q,i} = v_i . y_q,  pi_q = o_q^T G_h o_q,
+// so the per-token work is three dense contractions on the matrix cores
+// (S^T = K Q^T recomputing the logits, X^T = V Y^T, and G_h V^T for N) plus a
+// short elementwise epilogue, and W_O (d_model wide) is touched once per call.
+//
+// Kernels, in call order:
+//   gram_kernel        G_h partial sums over d_model slabs (MFMA)
+//   prep_kernel        G_h, y_q (rounded to the value type), pi_q, per-row constants
+//   vnorm_kernel       N_i for every token and query head (MFMA)
+//   score_kernel<0>    recompute a, form e, aggregate rows and group heads -> S
+//   score_kernel<1>    H2O: column sums of the causal prompt probabilities
+#include "common.hpp"
+#include "launch.hpp"
+#include "timing.hpp"
+
+namespace kvs {
+
+// ---------------------------------------------------------------------------
+// G_h = W_h^T W_h, one d_model slab per block.  W_h is the column slice
+// h*D .. h*D+D-1 of W_O [d_model][h_q*D].  A 32-row slab is staged transposed
+// in LDS so both MFMA operands are 16-byte reads.
+template <typename Tin, int D>
+__global__ void __launch_bounds__(256)
+gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
+            float *__restrict__ Gpart) {
+  typedef typename FragOf<Tin>::type FW;
+  constexpr int EPC = 16 / (int)sizeof(Tin);
+  constexpr int CPR = D / EPC;
+  constexpr int WROW = 32 + EPC;
+  constexpr int DB = D / 16;
+  constexpr int RPW = (DB + 3) / 4;  // row blocks per wave
+  __shared__ __align__(16) Tin Wt[D * WROW];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int s = blockIdx.x, h = blockIdx.y;
+  const long ld = (long)h_q * D;
+  const int k_begin = s * rows_per_split;
+  const int k_end = min(dm, k_begin + rows_per_split);
+
+  f32x4 acc[RPW][DB];
+#pragma unroll
+  for (int ri = 0; ri < RPW; ++ri)
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb) acc[ri][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = k_begin; k0 < k_end; k0 += 32) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 32 * CPR; idx += blockDim.x) {
+      const int kr = idx / CPR, ch = idx % CPR;
+      U128 v = {0, 0, 0, 0};
+      if (k0 + kr < k_end) v = *reinterpret_cast<const U128 *>(W + (long)(k0 + kr) * ld + (long)h * D + ch * EPC);
+      const Tin *ve = reinterpret_cast<const Tin *>(&v);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) Wt[(ch * EPC + e) * WROW + kr] = ve[e];
+    }
+    __syncthreads();
+    FW af[RPW];
+#pragma unroll
+    for (int ri = 0; ri < RPW; ++ri) {
+      const int rb = wv + 4 * ri;
+      af[ri] = rb < DB ? load8<Tin>(&Wt[(rb * 16 + col) * WROW + 8 * grp]) : zero8<Tin>();
+    }
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb) {
+      const FW bfr = load8<Tin>(&Wt[(cb * 16 + col) * WROW + 8 * grp]);
+#pragma unroll
+      for (int ri = 0; ri < RPW; ++ri) acc[ri][cb] = mma(af[ri], bfr, acc[ri][cb]);
+    }
+  }
+  float *G = Gpart + ((long)s * h_q + h) * D * D;
+#pragma unroll
+  for (int ri = 0; ri < RPW; ++ri) {
+    const int rb = wv + 4 * ri;
+    if (rb >= DB) continue;
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) G[(rb * 16 + 4 * grp + j) * D + cb * 16 + col] = acc[ri][cb][j];
+  }
+}
+
+int gram_splits(int h_q, int d_model) {
+  int splits = (256 + h_q - 1) / h_q;
+  const int slabs = (d_model + 31) / 32;
+  if (splits > slabs) splits = slabs;
+  if (splits < 1) splits = 1;
+  return splits;
+}
+
+// ---------------------------------------------------------------------------
+// Per (query head, sequence): sum the G_h partials (fixed order), round G_h to
+// the value type once (G~), and form every term of the norm expansion from
+// that same G~: y_q = G~ o_q and pi_q = o_q . y_q here, N_i = v_i^T G~ v_i in
+// vnorm_kernel.  Then N - 2x + pi equals (v - o)^T G~ (v - o) up to fp32
+// accumulation, so no term carries a rounding the others do not share and
+// tokens whose value is close to the attention output (where the three terms
+// nearly cancel) keep their relative accuracy.  y_q is stored as a hi + lo
+// pair of the value type (y = hi + lo to ~22 bits) for the MFMA product V.y.
+// Per-row constants of the score pass:
+//   x = beta2 = row_max*log2(e) + log2(row_sum)   (a = exp2(s*log2e/sqrt(d) - beta2))
+//   y = pi_q,  z = row weight (1/w for window rows, lambda_L omega_m / T for
+//   lookahead rows, 0 for padding rows),  w = bits of the last visible token.
+template <int D, typename TV>
+__global__ void __launch_bounds__(256)
+prep_kernel(const float *__restrict__ Gpart, int gsplits, const float *__restrict__ O,
+            const float *__restrict__ row_max, const float *__restrict__ row_sum,
+            const float *__restrict__ omega, int h_q, int n, int nq, int w, int m, int t,
+            float lambda_l, TV *__restrict__ Gv, TV *__restrict__ Yhi, TV *__restrict__ Ylo,
+            float4 *__restrict__ consts) {
+  constexpr int SLAB = 32;
+  __shared__ float Os[64 * D];
+  __shared__ float Gs[SLAB * (D + 1)];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const long hb = (long)b * h_q + h;
+  for (int idx = threadIdx.x; idx < 64 * D; idx += blockDim.x) {
+    const int r = idx / D;
+    Os[idx] = r < nq ? O[(hb * nq + r) * D + idx % D] : 0.f;
+  }
+  // thread -> (row r = tid/4, 8 consecutive outputs of every 32-row slab)
+  const int r = threadIdx.x >> 2, sub = threadIdx.x & 3;
+  float pi = 0.f;
+  for (int dd0 = 0; dd0 < D; dd0 += SLAB) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < SLAB * D; idx += blockDim.x) {
+      const int row = idx / D, k = idx % D;
+      float g = 0.f;
+      for (int s = 0; s < gsplits; ++s) g += Gpart[(((long)s * h_q + h) * D + dd0 + row) * D + k];
+      const TV gr = from_f32<TV>(g);
+      Gs[row * (D + 1) + k] = to_f32(gr);
+      if (b == 0) Gv[((long)h * D + dd0 + row) * D + k] = gr;
+    }
+    __syncthreads();
+    for (int u = 0; u < SLAB / 4; ++u) {
+      const int row = sub * (SLAB / 4) + u;
+      float y = 0.f;
+      for (int k = 0; k < D; ++k) y += Gs[row * (D + 1) + k] * Os[r * D + k];
+      if (r >= nq) y = 0.f;
+      pi += Os[r * D + dd0 + row] * y;
+      const TV hi = from_f32<TV>(y);
+      Yhi[(hb * 64 + r) * D + dd0 + row] = hi;
+      Ylo[(hb * 64 + r) * D + dd0 + row] = from_f32<TV>(y - to_f32(hi));
+    }
+  }
+  pi += __shfl_xor(pi, 1, 64);
+  pi += __shfl_xor(pi, 2, 64);
+  if (sub == 0) {
+    float beta2 = 0.f, wr = 0.f;
+    int last = -1;
+    if (r < nq) {
+      beta2 = row_max[hb * nq + r] * kLog2e + log2f(row_sum[hb * nq + r]);
+      if (r < w) {
+        wr = 1.f / (float)w;
+        last = n - w + r;
+      } else {
+        wr = lambda_l * omega[(long)b * m + (r - w) / t] / (float)t;
+        last = n - 1;
+      }
+    }
+    consts[hb * 64 + r] = make_float4(beta2, pi, wr, __int_as_float(last));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// N[b][h][i] = v_i^T G_h v_i.  Each wave holds G_h as A fragments with its
+// rows permuted by sigma(db, m) = 32*(db/2) + 8*(m/4) + 4*(db%2) + m%4, which
+// lands output row 4*(lane/16)+j of block db on the head-dim index whose V
+// value the lane already holds in its own B fragment (k-step db/2, element
+// 4*(db%2)+j): the quadratic form then needs no data exchange until the final
+// two cross-lane adds.
+template <typename Tin, int D>
+__global__ void __launch_bounds__(256)
+vnorm_kernel(const Tin *__restrict__ V, const typename ValueType<Tin>::type *__restrict__ Gv,
+             int n, int n_pad, int h_q, int h_kv, int tpwave, float *__restrict__ Nn) {
+  typedef typename ValueType<Tin>::type TV;
+  typedef typename FragOf<TV>::type FV;
+  constexpr int KS = D / 32;
+  constexpr int DB = D / 16;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (h_q / h_kv);
+  FV gf[DB][KS];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int row = 32 * (db >> 1) + 8 * (col >> 2) + 4 * (db & 1) + (col & 3);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      gf[db][ks] = load8<TV>(Gv + ((long)h * D + row) * D + ks * 32 + 8 * grp);
+  }
+  const Tin *Vg = V + ((long)b * h_kv + g) * (long)n * D;
+  float *Nh = Nn + ((long)b * h_q + h) * n_pad;
+  const int t_begin = (blockIdx.x * 4 + wv) * tpwave;
+  const int t_end = min(n_pad, t_begin + tpwave);
+  for (int t0 = t_begin; t0 < t_end; t0 += 16) {
+    const int tok = t0 + col;
+    FV vf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      vf[ks] = tok < n ? convert8<TV, Tin>(load8<Tin>(Vg + (long)tok * D + ks * 32 + 8 * grp))
+                       : zero8<TV>();
+    float np = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mma(gf[db][ks], vf[ks], acc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) np += acc[j] * frag_elem(vf[db >> 1], 4 * (db & 1) + j);
+    }
+    np = wave_sum_xor(np, 16);
+    np = wave_sum_xor(np, 32);
+    if (grp == 0 && tok < t_end) Nh[tok] = np;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Score pass.  One workgroup per (token range, KV head, sequence); each query
+// head's 64 rows are spread over 4/QBW waves.  K (and V, converted to the
+// value type) tiles of 64 tokens are staged in LDS and shared by the group.
+// Logits are formed transposed (S^T = K Q^T): a lane owns one query column
+// (row constants live in registers) and four tokens per 16-token block, so the
+// sum over the query rows is in-lane plus one 16-lane reduction per token; the
+// per-wave partial sums are combined across waves in a fixed order.
+//   MODE 0 (LORE): out = out_scale * sum_h sum_q wr_q * a/(1-a+eps) * sqrt(max(0, N - 2x + pi)),
+//                  x = v . (y_hi + y_lo) as two MFMA products
+//   MODE 1 (H2O):  out = sum over causal rows of a
+template <typename Tin, int D, int MODE, int MAXW, int QBW>
+__global__ void __launch_bounds__(64 * MAXW)
+score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__restrict__ V,
+             const typename ValueType<Tin>::type *__restrict__ Yhi,
+             const typename ValueType<Tin>::type *__restrict__ Ylo,
+             const float4 *__restrict__ consts, const float *__restrict__ Nn, int n_pad,
+             RowGeom geo, int h_kv, int tpw, float eps, float out_scale, float *__restrict__ S) {
+  typedef typename ValueType<Tin>::type TV;
+  typedef typename FragOf<Tin>::type FQ;
+  typedef typename FragOf<TV>::type FV;
+  constexpr bool SPLIT_Y = (MODE == 0) && sizeof(TV) == 2;
+  constexpr int KS = D / 32;
+  constexpr int TN = 64;
+  constexpr int WPH = 4 / QBW;
+  constexpr int EPC = 16 / (int)sizeof(Tin);
+  constexpr int CPR = D / EPC;
+  constexpr int KROW = D + EPC;
+  constexpr int VROW = D + 16 / (int)sizeof(TV);
+  __shared__ __align__(16) Tin Ks[TN * KROW];
+  __shared__ __align__(16) TV Vs[MODE == 0 ? TN * VROW : 8];
+  __shared__ __align__(16) float red[MAXW * TN];
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int hv = wv / WPH, qb0 = (wv % WPH) * QBW;
+  const int nwaves = blockDim.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int n = geo.n, G = geo.group;
+  const long kv_base = ((long)b * h_kv + kvh) * (long)n * D;
+  const long head = ((long)b * h_kv + kvh) * G + hv;  // LORE: b*h_q + h
+  const float c = kLog2e * rsqrtf((float)D);
+
+  FQ qf[QBW][KS];
+  FV yhf[MODE == 0 ? QBW : 1][KS];
+  FV ylf[SPLIT_Y ? QBW : 1][KS];
+  float beta[QBW], pi[QBW], wr[QBW];
+  int lim[QBW];
+  int wave_last = -1;
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) {
+    const int r = (qb0 + qb) * 16 + col;
+    const float4 cs = consts[head * 64 + r];
+    beta[qb] = cs.x;
+    pi[qb] = cs.y;
+    wr[qb] = cs.z;
+    lim[qb] = __float_as_int(cs.w);
+    wave_last = max(wave_last, lim[qb]);
+    long qrow;
+    if (geo.mode == 0) qrow = head * geo.nq + r;
+    else qrow = ((long)b * h_kv + kvh) * n + (long)hv * 64 + r;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[qb][ks] = lim[qb] >= 0 ? load8<Tin>(Q + qrow * D + ks * 32 + 8 * grp) : zero8<Tin>();
+      if (MODE == 0) yhf[qb][ks] = load8<TV>(Yhi + (head * 64 + r) * D + ks * 32 + 8 * grp);
+      if (SPLIT_Y) ylf[qb][ks] = load8<TV>(Ylo + (head * 64 + r) * D + ks * 32 + 8 * grp);
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) wave_last = max(wave_last, __shfl_xor(wave_last, o, 64));
+
+  const int t_begin = blockIdx.x * tpw;
+  const int t_end = min(n, t_begin + tpw);
+  const float *Nh = Nn + head * (long)n_pad;
+  float *Sout = S + ((long)b * h_kv + kvh) * n;
+
+  for (int t0 = t_begin; t0 < t_end; t0 += TN) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < TN * CPR; idx += blockDim.x) {
+      const int row = idx / CPR, ch = idx % CPR;
+      const int tok = t0 + row;
+      U128 kv = {0, 0, 0, 0};
+      if (tok < n) kv = *reinterpret_cast<const U128 *>(K + kv_base + (long)tok * D + ch * EPC);
+      *reinterpret_cast<U128 *>(&Ks[row * KROW + ch * EPC]) = kv;
+      if (MODE == 0) {
+        U128 vv = {0, 0, 0, 0};
+        if (tok < n) vv = *reinterpret_cast<const U128 *>(V + kv_base + (long)tok * D + ch * EPC);
+        const Tin *ve = reinterpret_cast<const Tin *>(&vv);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) Vs[row * VROW + ch * EPC + e] = from_f32<TV>(to_f32(ve[e]));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tb = 0; tb < TN / 16; ++tb) {
+      const int tok0 = t0 + tb * 16;
+      float tacc[4] = {0.f, 0.f, 0.f, 0.f};
+      if (tok0 <= wave_last) {
+        FQ kf[KS];
+        FV vf[MODE == 0 ? KS : 1];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          kf[ks] = load8<Tin>(&Ks[(tb * 16 + col) * KROW + ks * 32 + 8 * grp]);
+          if (MODE == 0) vf[ks] = load8<TV>(&Vs[(tb * 16 + col) * VROW + ks * 32 + 8 * grp]);
+        }
+        float4 nv = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (MODE == 0) nv = *reinterpret_cast<const float4 *>(Nh + tok0 + 4 * grp);
+        const float nva[4] = {nv.x, nv.y, nv.z, nv.w};
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb) {
+          f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) sa = mma(kf[ks], qf[qb][ks], sa);
+          f32x4 xa = {0.f, 0.f, 0.f, 0.f};
+          if (MODE == 0) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) xa = mma(vf[ks], yhf[qb][ks], xa);
+          }
+          if (SPLIT_Y) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) xa = mma(vf[ks], ylf[qb][ks], xa);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int tok = tok0 + 4 * grp + j;
+            const float a = (tok <= lim[qb]) ? hw_exp2(sa[j] * c - beta[qb]) : 0.f;
+            if (MODE == 1) {
+              tacc[j] += a;
+            } else {
+              const float cc = a * hw_rcp(1.f + eps - a);
+              const float q2 = fmaxf(nva[j] - 2.f * xa[j] + pi[qb], 0.f);
+              tacc[j] += wr[qb] * (cc * hw_sqrt(q2));
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v = tacc[j];
+        v = wave_sum_xor(v, 1);
+        v = wave_sum_xor(v, 2);
+        v = wave_sum_xor(v, 4);
+        v = wave_sum_xor(v, 8);
+        tacc[j] = v;
+      }
+      if (col == 0)
+        *reinterpret_cast<float4 *>(&red[wv * TN + tb * 16 + 4 * grp]) =
+            make_float4(tacc[0], tacc[1], tacc[2], tacc[3]);
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < TN; t += blockDim.x) {
+      const int tok = t0 + t;
+      if (tok < t_end) {
+        float sum = 0.f;
+        for (int w = 0; w < nwaves; ++w) sum += red[w * TN + t];
+        Sout[tok] = sum * out_scale;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <typename Tin, int D>
+static hipError_t run_gram(const void *W, int dm, int h_q, int splits, float *Gpart,
+                           hipStream_t st) {
+  const int slabs = (dm + 31) / 32;
+  const int rps = (slabs + splits - 1) / splits * 32;
+  {
+    TimedLaunch tl_("gram", st);
+    hipLaunchKernelGGL((gram_kernel<Tin, D>), dim3(splits, h_q), dim3(256), 0, st, (const Tin *)W,
+                       dm, h_q, rps, Gpart);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gram(int etype, int d, const void *W_O, int d_model, int h_q, int splits,
+                       float *Gpart, hipStream_t st) {
+#define KVS_G(T, DD) return run_gram<T, DD>(W_O, d_model, h_q, splits, Gpart, st)
+  if (etype == E_F32) { if (d == 64) KVS_G(float, 64); KVS_G(float, 128); }
+  if (etype == E_BF16) { if (d == 64) KVS_G(bf16, 64); KVS_G(bf16, 128); }
+  if (d == 64) KVS_G(f16, 64);
+  KVS_G(f16, 128);
+#undef KVS_G
+}
+
+template <int D, typename TV>
+static hipError_t run_prep(const float *Gpart, int gsplits, const float *O, const float *row_max,
+                           const float *row_sum, const float *omega, int batch, int h_q, int n,
+                           int nq, int w, int m, int t, float lambda_l, void *Gv, void *Yhi,
+                           void *Ylo, float4 *consts, hipStream_t st) {
+  {
+    TimedLaunch tl_("deletion_prep", st);
+    hipLaunchKernelGGL((prep_kernel<D, TV>), dim3(h_q, batch), dim3(256), 0, st, Gpart, gsplits,
+                       O, row_max, row_sum, omega, h_q, n, nq, w, m, t, lambda_l, (TV *)Gv,
+                       (TV *)Yhi, (TV *)Ylo, consts);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_deletion_prep(int etype, int d, const float *Gpart, int gsplits, const float *O,
+                                const float *row_max, const float *row_sum, const float *omega,
+                                int batch, int h_q, int n, int nq, int w, int m, int t,
+                                float lambda_l, void *Gv, void *Yhi, void *Ylo, float4 *consts,
+                                hipStream_t st) {
+#define KVS_P(DD, TV) \
+  return run_prep<DD, TV>(Gpart, gsplits, O, row_max, row_sum, omega, batch, h_q, n, nq, w, m, t, \
+                          lambda_l, Gv, Yhi, Ylo, consts, st)
+  if (etype == E_F32) { if (d == 64) KVS_P(64, float); KVS_P(128, float); }
+  if (d == 64) KVS_P(64, f16);
+  KVS_P(128, f16);
+#undef KVS_P
+}
+
+template <typename Tin, int D>
+static hipError_t run_vnorm(const void *V, const void *Gv, int batch, int n, int n_pad, int h_q,
+                            int h_kv, float *Nn, hipStream_t st) {
+  typedef typename ValueType<Tin>::type TV;
+  const int tpwave = 256;
+  const int chunks = (n_pad + 4 * tpwave - 1) / (4 * tpwave);
+  {
+    TimedLaunch tl_("vnorm", st);
+    hipLaunchKernelGGL((vnorm_kernel<Tin, D>), dim3(chunks, h_q, batch), dim3(256), 0, st,
+                       (const Tin *)V, (const TV *)Gv, n, n_pad, h_q, h_kv, tpwave, Nn);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_vnorm(int etype, int d, const void *V, const void *Gv, int batch, int n,
+                        int n_pad, int h_q, int h_kv, float *Nn, hipStream_t st) {
+#define KVS_V(T, DD) return run_vnorm<T, DD>(V, Gv, batch, n, n_pad, h_q, h_kv, Nn, st)
+  if (etype == E_F32) { if (d == 64) KVS_V(float, 64); KVS_V(float, 128); }
+  if (etype == E_BF16) { if (d == 64) KVS_V(bf16, 64); KVS_V(bf16, 128); }
+  if (d == 64) KVS_V(f16, 64);
+  KVS_V(f16, 128);
+#undef KVS_V
+}
+
+template <typename Tin, int D, int MODE, int MAXW, int QBW>
+static hipError_t run_score_w(const void *Q, const void *K, const void *V, const void *Yhi,
+                              const void *Ylo, const float4 *consts, const float *Nn, int n_pad,
+                              RowGeom geo, int batch, int h_kv, float eps, float out_scale,
+                              float *S, hipStream_t st) {
+  typedef typename ValueType<Tin>::type TV;
+  const long units = (long)batch * h_kv;
+  long tpw = ((long)geo.n * units + 1023) / 1024;  // aim for ~1024 workgroups
+  tpw = (tpw + 63) / 64 * 64;
+  if (tpw < 64) tpw = 64;
+  const int blocks = (int)((geo.n + tpw - 1) / tpw);
+  {
+    TimedLaunch tl_((MODE == 0 ? "score_lore" : "score_h2o_colsum"), st);
+    hipLaunchKernelGGL((score_kernel<Tin, D, MODE, MAXW, QBW>), dim3(blocks, h_kv, batch),
+                       dim3(64 * geo.group * (4 / QBW)), 0, st, (const Tin *)Q, (const Tin *)K,
+                       (const Tin *)V, (const TV *)Yhi, (const TV *)Ylo, consts, Nn, n_pad, geo,
+                       h_kv, (int)tpw, eps, out_scale, S);
+  }
+  return hipGetLastError();
+}
+
+// Waves per workgroup = group * 4 / QBW <= 16.
+template <typename Tin, int D>
+static hipError_t run_score(int mode, const void *Q, const void *K, const void *V, const void *Yhi,
+                            const void *Ylo, const float4 *consts, const float *Nn, int n_pad,
+                            RowGeom geo, int batch, int h_kv, float eps, float out_scale, float *S,
+                            hipStream_t st) {
+#define KVS_RS(MODE, MAXW, QBW)                                                                \
+  return run_score_w<Tin, D, MODE, MAXW, QBW>(Q, K, V, Yhi, Ylo, consts, Nn, n_pad, geo, batch, \
+                                              h_kv, eps, out_scale, S, st)
+  if (mode == 1) KVS_RS(1, 16, 4);
+  if (geo.group <= 2) KVS_RS(0, 4, 2);
+  if (geo.group <= 4) KVS_RS(0, 8, 2);
+  if (geo.group <= 8) KVS_RS(0, 16, 2);
+  KVS_RS(0, 16, 4);
+#undef KVS_RS
+}
+
+hipError_t launch_score(int etype, int d, int mode, const void *Q, const void *K, const void *V,
+                        const void *Yhi, const void *Ylo, const float4 *consts, const float *Nn,
+                        int n_pad, RowGeom geo, int batch, int h_kv, float eps, float out_scale,
+                        float *S, hipStream_t st) {
+#define KVS_S(T, DD) \
+  return run_score<T, DD>(mode, Q, K, V, Yhi, Ylo, consts, Nn, n_pad, geo, batch, h_kv, eps, \
+                          out_scale, S, st)
+  if (etype == E_F32) { if (d == 64) KVS_S(float, 64); KVS_S(float, 128); }
+  if (etype == E_BF16) { if (d == 64) KVS_S(bf16, 64); KVS_S(bf16, 128); }
+  if (d == 64) KVS_S(f16, 64);
+  KVS_S(f16, 128);
+#undef KVS_S
+}
+
+}  // namespace kvs

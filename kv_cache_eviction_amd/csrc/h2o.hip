@@ -1,0 +1,240 @@
+// H2O decode step on a preallocated slot cache.
+//
+// H2O ("H2O: Heavy-Hitter Oracle"), 3.4 and System Implementation Details:
+// the new token's key/value go into a free slot of a preallocated cache (an
+// evicted slot is overwritten in place, no data moves); the new query attends
+// over the retained tokens and itself, o_i = softmax over the retained set
+// (Def. 2.2); its probabilities are added to the per-slot accumulators
+// (o~_i = o~_{i-1} + o_i); if the cache exceeds k_heavy + k_recent, the
+// retained token outside the recent window with the lowest accumulated score
+// is evicted (later position first on ties), at most one per step
+// (Def. 2.1).  Rows (sequence, head) are independent, one wavefront each.
+//
+// A row's slots are read as 16-byte lane chunks, D/EPC lanes per slot, so one
+// wave instruction covers 64*16 contiguous-per-slot bytes; invalid slots are
+// never read.  Logits and updated accumulators sit in LDS for the softmax and
+// the arg-min.
+#include "common.hpp"
+#include "launch.hpp"
+#include "timing.hpp"
+
+namespace kvs {
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint32_t order_key_pos(float x) {
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
+                  const T *__restrict__ k_new, const T *__restrict__ v_new,
+                  int32_t *__restrict__ slot_pos, float *__restrict__ acc, T *__restrict__ O,
+                  int32_t *__restrict__ evict_slot, int rows, int cap, int cur_len, int k_heavy,
+                  int k_recent, float c) {
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int LPR = D / EPC;  // lanes per slot row
+  constexpr int RPI = 64 / LPR; // slot rows per wave step
+  extern __shared__ float dsh[];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const long row = (long)blockIdx.x * 4 + wv;
+  if (row >= rows) return;
+  float *prob = dsh + (long)wv * 2 * cap;
+  float *accn = prob + cap;
+  int32_t *pos = slot_pos + row * cap;
+  float *ac = acc + row * cap;
+  T *Kr = K + row * cap * D;
+  T *Vr = V + row * cap * D;
+
+  // lowest free slot, and how many slots hold a token
+  int ws = -1, nvalid = 0;
+  for (int base = 0; base < cap; base += 64) {
+    const int s = base + lane;
+    const int p = s < cap ? pos[s] : 0;
+    const unsigned long long fb = __ballot(s < cap && p < 0);
+    const unsigned long long vb = __ballot(s < cap && p >= 0);
+    nvalid += __popcll(vb);
+    if (ws < 0 && fb) ws = base + __ffsll((long long)fb) - 1;
+  }
+  if (ws < 0) {
+    if (lane == 0 && evict_slot) evict_slot[row] = -2;
+    return;
+  }
+  const int newpos = cur_len - 1;
+  const int sub = lane % LPR, rr = lane / LPR;
+
+  float qv[EPC], kn[EPC], vn[EPC];
+  {
+    const U128 qq = *reinterpret_cast<const U128 *>(q + row * D + sub * EPC);
+    const U128 kk = *reinterpret_cast<const U128 *>(k_new + row * D + sub * EPC);
+    const U128 vv = *reinterpret_cast<const U128 *>(v_new + row * D + sub * EPC);
+    const T *qe = reinterpret_cast<const T *>(&qq);
+    const T *ke = reinterpret_cast<const T *>(&kk);
+    const T *ve = reinterpret_cast<const T *>(&vv);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      qv[e] = to_f32(qe[e]);
+      kn[e] = to_f32(ke[e]);
+      vn[e] = to_f32(ve[e]);
+    }
+  }
+
+  // logits of every valid slot (the new token's from registers)
+  for (int base = 0; base < cap; base += RPI) {
+    const int s = base + rr;
+    const bool inb = s < cap;
+    const int p = inb ? pos[s] : -1;
+    const bool valid = inb && (p >= 0 || s == ws);
+    float part = 0.f;
+    if (valid) {
+      if (s == ws) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) part += qv[e] * kn[e];
+      } else {
+        const U128 kk = *reinterpret_cast<const U128 *>(Kr + (long)s * D + sub * EPC);
+        const T *ke = reinterpret_cast<const T *>(&kk);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) part += qv[e] * to_f32(ke[e]);
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) part += __shfl_xor(part, o, 64);
+    if (sub == 0 && inb) prob[s] = valid ? part * c : -INFINITY;
+  }
+  wave_lds_sync();
+
+  float mx = -INFINITY;
+  for (int s = lane; s < cap; s += 64) mx = fmaxf(mx, prob[s]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  float l = 0.f;
+  for (int s = lane; s < cap; s += 64) l += hw_exp2(prob[s] - mx);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o, 64);
+  const float inv = 1.f / l;
+  for (int s = lane; s < cap; s += 64) {
+    const bool valid = (s == ws) || pos[s] >= 0;
+    float a = 0.f;
+    if (valid) {
+      a = hw_exp2(prob[s] - mx) * inv;
+      const float nw = ((s == ws) ? 0.f : ac[s]) + a;
+      ac[s] = nw;
+      accn[s] = nw;
+    }
+    prob[s] = a;
+  }
+  wave_lds_sync();
+
+  if (O) {
+    float ov[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) ov[e] = 0.f;
+    for (int base = 0; base < cap; base += RPI) {
+      const int s = base + rr;
+      if (s >= cap) continue;
+      const float a = prob[s];
+      if (a == 0.f) continue;
+      if (s == ws) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) ov[e] += a * vn[e];
+      } else {
+        const U128 vv = *reinterpret_cast<const U128 *>(Vr + (long)s * D + sub * EPC);
+        const T *ve = reinterpret_cast<const T *>(&vv);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) ov[e] += a * to_f32(ve[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPC; ++e)
+#pragma unroll
+      for (int o = LPR; o < 64; o <<= 1) ov[e] += __shfl_xor(ov[e], o, 64);
+    if (rr == 0) {
+      U128 out;
+      T *oe = reinterpret_cast<T *>(&out);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) oe[e] = from_f32<T>(ov[e]);
+      *reinterpret_cast<U128 *>(O + row * D + sub * EPC) = out;
+    }
+  }
+
+  // the new token takes its slot
+  if (rr == 0) {
+    *reinterpret_cast<U128 *>(Kr + (long)ws * D + sub * EPC) =
+        *reinterpret_cast<const U128 *>(k_new + row * D + sub * EPC);
+    *reinterpret_cast<U128 *>(Vr + (long)ws * D + sub * EPC) =
+        *reinterpret_cast<const U128 *>(v_new + row * D + sub * EPC);
+  }
+  if (lane == 0) pos[ws] = newpos;
+
+  int ev = -1;
+  if (nvalid + 1 > k_heavy + k_recent) {
+    const int recent_from = cur_len - k_recent;
+    unsigned long long best = ~0ull;
+    for (int s = lane; s < cap; s += 64) {
+      const int p = (s == ws) ? newpos : pos[s];
+      if (p >= 0 && p < recent_from) {
+        const unsigned long long key =
+            ((unsigned long long)order_key_pos(accn[s]) << 32) | (uint32_t)(0x7FFFFFFF - p);
+        best = key < best ? key : best;
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long other = __shfl_xor(best, o, 64);
+      best = other < best ? other : best;
+    }
+    if (best != ~0ull) {
+      const int pev = 0x7FFFFFFF - (int)(uint32_t)(best & 0xFFFFFFFFull);
+      int cand = -1;
+      for (int s = lane; s < cap; s += 64) {
+        const int p = (s == ws) ? newpos : pos[s];
+        if (p == pev) cand = s;
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) cand = max(cand, __shfl_xor(cand, o, 64));
+      ev = cand;
+    }
+  }
+  if (lane == 0) {
+    if (ev >= 0) pos[ev] = -1;
+    if (evict_slot) evict_slot[row] = ev;
+  }
+}
+
+template <typename T, int D>
+static hipError_t run_decode(int rows, int cap, int cur_len, int k_heavy, int k_recent,
+                             const void *q, void *K, void *V, const void *k_new,
+                             const void *v_new, int32_t *slot_pos, float *acc, void *O,
+                             int32_t *evict_slot, hipStream_t st) {
+  const float c = kLog2e / sqrtf((float)D);
+  const size_t shm = sizeof(float) * 2 * (size_t)cap * 4;
+  {
+    TimedLaunch tl_("h2o_decode", st);
+    hipLaunchKernelGGL((h2o_decode_kernel<T, D>), dim3((rows + 3) / 4), dim3(256), shm, st,
+                       (const T *)q, (T *)K, (T *)V, (const T *)k_new, (const T *)v_new, slot_pos,
+                       acc, (T *)O, evict_slot, rows, cap, cur_len, k_heavy, k_recent, c);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_h2o_decode(int etype, int d, int rows, int cap, int cur_len, int k_heavy,
+                             int k_recent, const void *q, void *K, void *V, const void *k_new,
+                             const void *v_new, int32_t *slot_pos, float *acc, void *O,
+                             int32_t *evict_slot, hipStream_t st) {
+#define KVS_D(T, DD)                                                                          \
+  return run_decode<T, DD>(rows, cap, cur_len, k_heavy, k_recent, q, K, V, k_new, v_new,     \
+                           slot_pos, acc, O, evict_slot, st)
+  if (etype == E_F32) { if (d == 64) KVS_D(float, 64); KVS_D(float, 128); }
+  if (etype == E_BF16) { if (d == 64) KVS_D(bf16, 64); KVS_D(bf16, 128); }
+  if (d == 64) KVS_D(f16, 64);
+  KVS_D(f16, 128);
+#undef KVS_D
+}
+
+}  // namespace kvs

@@ -1,0 +1,76 @@
+// Host-side launchers of the gfx950 kernels (one per kernel family).  The C ABI
+// in capi.cpp validates arguments, sizes workspaces and calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvs {
+
+enum ElemType { E_F32 = 0, E_BF16 = 1, E_F16 = 2 };
+
+inline size_t elem_bytes(int t) { return t == E_F32 ? 4 : 2; }
+
+// Geometry of the scoring rows (see attn.hip).
+struct RowGeom {
+  int mode;   // 0: LORE scoring rows; 1: causal prompt rows (H2O prefill)
+  int n;      // keys per KV head (LORE: cache length; H2O: prompt length)
+  int nq;     // LORE: rows per query head
+  int w;      // LORE: window rows
+  int group;  // query heads (H2O: virtual heads of 64 prompt rows) per KV head
+};
+
+// Split-K plan of the attention pass.
+struct SplitPlan {
+  int splits;
+  int tps;  // tokens per split, a multiple of 32
+};
+SplitPlan attn_split_plan(int units, int n);
+
+// Pass 1 partials -> combined statistics.
+// part_m/part_l: [heads][splits][64]; part_O: [heads][splits][d][64].
+hipError_t launch_attn_partial(int etype, int d, bool with_o, const void *Q, const void *K,
+                               const void *V, RowGeom geo, int batch, int h_kv, SplitPlan plan,
+                               float *part_m, float *part_l, float *part_O, hipStream_t st);
+// LORE: writes row_max, row_sum [heads][nq] and O [heads][nq][d].
+hipError_t launch_attn_combine_lore(int d, const float *part_m, const float *part_l,
+                                    const float *part_O, int heads, int splits, int nq,
+                                    float *row_max, float *row_sum, float *O, hipStream_t st);
+// H2O: writes per-row constants {beta2, 0, 1, last-visible bits} [heads][64].
+hipError_t launch_attn_combine_rows(const float *part_m, const float *part_l, int heads,
+                                    int splits, int group, int P, float4 *consts, hipStream_t st);
+
+// Deletion score pieces.
+int gram_splits(int h_q, int d_model);
+hipError_t launch_gram(int etype, int d, const void *W_O, int d_model, int h_q, int splits,
+                       float *Gpart, hipStream_t st);
+hipError_t launch_deletion_prep(int etype, int d, const float *Gpart, int gsplits, const float *O,
+                                const float *row_max, const float *row_sum, const float *omega,
+                                int batch, int h_q, int n, int nq, int w, int m, int t,
+                                float lambda_l, void *Gv, void *Yhi, void *Ylo, float4 *consts,
+                                hipStream_t st);
+hipError_t launch_vnorm(int etype, int d, const void *V, const void *Gv, int batch, int n,
+                        int n_pad, int h_q, int h_kv, float *Nn, hipStream_t st);
+// mode 0: LORE deletion score (Yhi/Ylo, consts, Nn used); mode 1: causal column sums.
+hipError_t launch_score(int etype, int d, int mode, const void *Q, const void *K, const void *V,
+                        const void *Yhi, const void *Ylo, const float4 *consts, const float *Nn,
+                        int n_pad, RowGeom geo, int batch, int h_kv, float eps, float out_scale,
+                        float *S, hipStream_t st);
+
+// Selection and compaction.
+hipError_t launch_topb(const float *S, int rows, int n, int n_sink, int w, int chunk, int budget,
+                       int n_keep, uint32_t *keys_ws, int32_t *kept, float *pooled,
+                       hipStream_t st);
+hipError_t launch_compact(int rows, int n_src, int n_keep, int cap_dst, int row_bytes,
+                          const void *K, const void *V, const int32_t *kept, void *K_out,
+                          void *V_out, int32_t *pos_out, const float *score_in,
+                          float *score_out, hipStream_t st);
+
+// H2O decode step.
+hipError_t launch_h2o_decode(int etype, int d, int rows, int cap, int cur_len, int k_heavy,
+                             int k_recent, const void *q, void *K, void *V, const void *k_new,
+                             const void *v_new, int32_t *slot_pos, float *acc, void *O,
+                             int32_t *evict_slot, hipStream_t st);
+
+}  // namespace kvs

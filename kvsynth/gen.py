@@ -56,9 +56,12 @@ def _facts_sequence(cfg: LoreConfig, gen, device):
     V = _randn(gen, h_kv, n, d, device=device)
     K[:, 0, :] *= 8.0
     n_cand = n - w - 1  # candidates [1, n - w)
-    facts = torch.randperm(n_cand, generator=gen, device=device)[: cfg.n_facts] + 1
+    # tiny caches with fewer candidates than facts draw from every non-sink token
+    pool = n_cand if n_cand >= cfg.n_facts else max(n - 1, 1)
+    k_facts = min(cfg.n_facts, pool)
+    facts = torch.randperm(pool, generator=gen, device=device)[:k_facts] + (1 if n > 1 else 0)
     z = _randn(gen, h_q, nq, d, device=device)
-    pick = torch.randint(0, cfg.n_facts, (h_q, nq), generator=gen, device=device)
+    pick = torch.randint(0, k_facts, (h_q, nq), generator=gen, device=device)
     target = facts[pick]  # [h_q][nq]
     if not cfg.window_from_facts:
         is_fact = torch.zeros(n, dtype=torch.bool, device=device)

@@ -247,7 +247,7 @@ class H2OOracle:
     Slot order is the oracle's own and carries no meaning.
     """
 
-    def __init__(self, Qp, Kp, Vp, heavy_frac, recent_frac, cap):
+    def __init__(self, Qp, Kp, Vp, heavy_frac, recent_frac, cap, kept=None):
         Qp, Kp, Vp = _f64(Qp), _f64(Kp), _f64(Vp)
         P, d = Kp.shape[-2:]
         self.rows = int(np.prod(Kp.shape[:-2]))
@@ -256,7 +256,9 @@ class H2OOracle:
         acc = h2o_prefill_acc(Qp, Kp).reshape(self.rows, P)
         self.prefill_acc = acc.copy()
         k_h, k_r = h2o_budget(P, heavy_frac, recent_frac)
-        kept, _ = topb_select(acc, n_sink=0, w=k_r, chunk=1, budget=k_h)
+        self.own_kept_prompt, _ = topb_select(acc, n_sink=0, w=k_r, chunk=1, budget=k_h)
+        # a caller running in lockstep may hand in its own prompt selection
+        kept = self.own_kept_prompt if kept is None else np.asarray(kept).reshape(self.rows, -1)
         if kept.shape[1] > cap:
             raise ValueError("cap too small for the prompt budget")
         self.pos = np.full((self.rows, cap), -1, dtype=np.int64)

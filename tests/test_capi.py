@@ -1,0 +1,120 @@
+"""The C ABI on the CPU: the library loads, exports every entry point that
+include/kvscore.h declares, and rejects bad arguments on the host before any
+HIP call (no device is touched by these tests)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvscore.h")
+
+
+def _lib():
+    import kv_cache_eviction_amd as kv
+    if not os.path.exists(kv.LIB_PATH):
+        from kv_cache_eviction_amd import build
+        build.build()
+    return kv, kv.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:kvs_status|size_t|int32_t|void|const char\s*\*)\s*(\w+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_exports_match_header():
+    kv, lib = _lib()
+    names = declared_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", kv.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert exported == names
+    assert sorted(kv.EXPORTS) == names
+
+
+def _desc(kv, **kw):
+    base = dict(batch=1, n=1024, h_q=8, h_kv=2, d=128, d_model=1024)
+    base.update(kw)
+    return kv.lore_desc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h_q=6, h_kv=4), 1),          # h_q not a multiple of h_kv
+    (dict(h_q=34, h_kv=2), 2),         # group of 17
+    (dict(d=96), 2),                   # head dim
+    (dict(w=40, m=4, t=8), 2),         # 72 scoring rows
+    (dict(n=20), 1),                   # n < n_sink + w
+    (dict(chunk=0), 1),
+    (dict(eps=float("nan")), 1),
+    (dict(budget=-1), 1),
+])
+def test_bad_descriptor_rejected_before_launch(kw, status):
+    kv, lib = _lib()
+    d = _desc(kv, **kw)
+    assert lib.kvs_lore_workspace_bytes(ctypes.byref(d)) == 0
+    rc = lib.kvscore_probs(ctypes.byref(d), None, None, None, None, None, None, None, 0, None)
+    assert rc == status, kv.last_error()
+    assert kv.last_error()
+
+
+def test_null_pointers_and_workspace():
+    kv, lib = _lib()
+    d = _desc(kv)
+    need = lib.kvs_lore_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    assert lib.kvscore_probs(ctypes.byref(d), None, None, None, None, None, None, None, 0,
+                             None) == 1
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: a host check fails first
+    rc = lib.kvscore_probs(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, 16, None)
+    assert rc == 3 and "workspace" in kv.last_error()
+    rc = lib.kvscore_deletion(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake, fake,
+                              fake, fake, 16, None)
+    assert rc == 1 and "omega" in kv.last_error()
+    rc = lib.kvscore_topb_select(ctypes.byref(d), fake, fake, None, fake, 16, None)
+    assert rc == 3
+    assert lib.kv_compact(1, 1, 10, 11, 11, 128, 1, fake, fake, fake, fake, fake, None, None,
+                          None, None) == 1
+    assert lib.kv_compact(1, 1, 10, 5, 5, 96, 1, fake, fake, fake, fake, fake, None, None,
+                          None, None) == 2
+    assert lib.kv_compact(1, 1, 10, 5, 5, 128, 1, fake, fake, fake, fake, fake, None, fake,
+                          None, None) == 1
+
+
+def test_selection_descriptor_needs_only_selection_fields():
+    kv, lib = _lib()
+    d = kv.lore_desc(batch=2, n=1024, h_q=3, h_kv=3, d=128, d_model=1, w=102, m=0, t=0,
+                     n_sink=0, chunk=1, budget=102)
+    assert lib.kvs_lore_workspace_bytes(ctypes.byref(d)) == 0     # not a scoring descriptor
+    assert lib.kvs_topb_workspace_bytes(ctypes.byref(d)) == 2 * 3 * 1024 * 4
+
+
+def test_h2o_descriptor_checks():
+    kv, lib = _lib()
+    d = kv.h2o_desc(batch=2, heads=3, d=128, cap=1025)
+    assert lib.kvs_h2o_workspace_bytes(ctypes.byref(d), kv.KVS_H2O_PREFILL) == 0
+    d = kv.h2o_desc(batch=2, heads=3, d=128, cap=1024)
+    assert lib.kvs_h2o_workspace_bytes(ctypes.byref(d), kv.KVS_H2O_PREFILL) > 0
+    rc = lib.kvscore_h2o_accumulate(ctypes.byref(d), 7, None, None, None, None, None, None,
+                                    None, None, None, None, 0, None)
+    assert rc == 1
+    d = kv.h2o_desc(batch=2, heads=3, d=128, cap=300, cur_len=0)
+    rc = lib.kvscore_h2o_accumulate(ctypes.byref(d), kv.KVS_H2O_DECODE, None, None, None, None,
+                                    None, None, None, None, None, None, 0, None)
+    assert rc == 1
+
+
+def test_binding_checks_shapes_before_calling():
+    kv, _ = _lib()
+    import torch
+    d = _desc(kv)
+    with pytest.raises(kv.KvsError):
+        kv.kvscore_probs(d, torch.zeros(1), None, None, None, None, None, None)

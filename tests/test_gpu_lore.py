@@ -1,0 +1,160 @@
+"""GPU parity of the LORE-KV path (probs -> deletion -> top-B -> compaction)
+against the fp64 oracle, through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import kv_cache_eviction_amd as kv
+from kvsynth import (TINY, MISTRAL_16K, LLAMA_128K, QWEN_14B_BATCH, lore_inputs, TORCH_DTYPES)
+from parity import (lore_desc_kwargs, check_stats, check_scores, check_kept, check_compaction)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kv.load()
+    return torch.device("cuda")
+
+
+def run_gpu(cfg, inp, dev):
+    desc = kv.lore_desc(dtype=TORCH_DTYPES[cfg.dtype], **lore_desc_kwargs(cfg))
+    ev = kv.LoreEviction(desc, dev)
+    Q, K, V, W, om = (inp[k].to(dev).contiguous() for k in ("Q", "K", "V", "W_O", "omega"))
+    ev.score(Q, K, V, W, om)
+    pooled = torch.empty_like(ev.S)
+    ev.select(pooled)
+    b, hk, nk, d = cfg.batch, cfg.h_kv, desc.n_keep, cfg.d
+    Kc = torch.empty(b, hk, nk, d, dtype=K.dtype, device=dev)
+    Vc = torch.empty_like(Kc)
+    pos = torch.empty(b, hk, nk, dtype=torch.int32, device=dev)
+    ev.compact(K, V, Kc, Vc, pos)
+    torch.cuda.synchronize()
+    check_compaction(K, V, ev.kept, Kc, Vc)
+    assert torch.equal(pos, ev.kept)
+    return {k: getattr(ev, k).cpu().numpy() for k in ("row_max", "row_sum", "O", "S", "kept")} | \
+        {"pooled": pooled.cpu().numpy()}
+
+
+def run_oracle(cfg, inp):
+    r = oracle.lore_scores(inp["Q"], inp["K"], inp["V"], inp["W_O"], inp["omega"], w=cfg.w,
+                           m=cfg.m, t=cfg.t, eps=cfg.eps, lambda_l=cfg.lambda_l)
+    kept, pooled = oracle.topb_select(r["S"], n_sink=cfg.n_sink, w=cfg.w, chunk=cfg.chunk,
+                                      budget=cfg.budget)
+    r["kept"], r["pooled"] = kept, pooled
+    return r
+
+
+def compare(cfg, g, o, o_rtol=1e-3):
+    st = check_stats(g["row_max"], g["row_sum"], g["O"], o["row_max"], o["row_sum"], o["O"], o_rtol)
+    worst = check_scores(g["S"], o["S"], cfg.n_sink, cfg.w)
+    nd = check_kept(g["kept"], o["kept"], o["pooled"], cfg.n_sink, cfg.w, cfg.budget)
+    print("%s: stats %s, worst score rel err %.3g, kept diffs at ties %d" % (cfg.name, st, worst, nd))
+
+
+def test_tiny_fp32(dev):
+    inp = lore_inputs(TINY)
+    g = run_gpu(TINY, inp, dev)
+    o = run_oracle(TINY, inp)
+    compare(TINY, g, o, o_rtol=1e-5)
+    assert np.array_equal(g["kept"], o["kept"])
+
+
+SMALL = [
+    TINY.with_(name="bf16-d128-g4-n1000", dtype="bf16", d=128, h_q=8, h_kv=2, n=1000,
+               d_model=512, budget=64, seed=11),
+    TINY.with_(name="f16-d64-mha-n777-nq11", dtype="f16", d=64, h_q=3, h_kv=3, n=777,
+               d_model=192, w=5, m=2, t=3, chunk=1, budget=50, n_sink=2, seed=12),
+    TINY.with_(name="bf16-d128-g5-b2-n2085", dtype="bf16", d=128, h_q=10, h_kv=2, n=2085,
+               d_model=1280, budget=100, batch=2, seed_per_seq=True, omega_per_seq=True, seed=13),
+    MISTRAL_16K.with_(name="f32-d128-g2-b2-n300", dtype="f32", h_q=4, h_kv=2, n=300,
+                      d_model=512, batch=2, budget=40, seed=14),
+    TINY.with_(name="bf16-d64-g8-n4096", dtype="bf16", d=64, h_q=8, h_kv=1, n=4096,
+               d_model=512, seed=15),
+    TINY.with_(name="bf16-d128-g16-n600", dtype="bf16", d=128, h_q=16, h_kv=1, n=600,
+               d_model=2048, budget=30, seed=16, window_from_facts=False),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=[c.name for c in SMALL])
+def test_small_shapes(dev, cfg):
+    inp = lore_inputs(cfg)
+    compare(cfg, run_gpu(cfg, inp, dev), run_oracle(cfg, inp))
+
+
+def test_mistral_16k_full(dev):
+    inp = lore_inputs(MISTRAL_16K)
+    compare(MISTRAL_16K, run_gpu(MISTRAL_16K, inp, dev), run_oracle(MISTRAL_16K, inp))
+
+
+def _slice_head(cfg, inp, b, g):
+    G = cfg.group
+    d = cfg.d
+    return {"Q": inp["Q"][b:b + 1, g * G:(g + 1) * G].cpu(), "K": inp["K"][b:b + 1, g:g + 1].cpu(),
+            "V": inp["V"][b:b + 1, g:g + 1].cpu(),
+            "W_O": inp["W_O"][:, g * G * d:(g + 1) * G * d].cpu(),
+            "omega": inp["omega"][b:b + 1].cpu()}
+
+
+@pytest.mark.parametrize("cfg,b,g", [(LLAMA_128K, 0, 3), (QWEN_14B_BATCH, 5, 6)],
+                         ids=["llama128k-layer0-kvhead3", "qwen14b-seq5-kvhead6"])
+def test_full_size_sampled_head(dev, cfg, b, g):
+    """Full-size launch (the bench's configuration); the oracle checks one
+    (sequence, KV head) completely: every score, the kept set, the stats."""
+    inp = lore_inputs(cfg, layer=0, device=dev)
+    gr = run_gpu(cfg, inp, dev)
+    one = cfg.with_(batch=1, h_q=cfg.group, h_kv=1)
+    o = run_oracle(one, _slice_head(cfg, inp, b, g))
+    G = cfg.group
+    gs = {"row_max": gr["row_max"][b:b + 1, g * G:(g + 1) * G],
+          "row_sum": gr["row_sum"][b:b + 1, g * G:(g + 1) * G],
+          "O": gr["O"][b:b + 1, g * G:(g + 1) * G],
+          "S": gr["S"][b:b + 1, g:g + 1], "kept": gr["kept"][b:b + 1, g:g + 1]}
+    compare(one.with_(name=cfg.name), gs, o)
+
+
+def _edge_case(dev, cfg, inp):
+    g, o = run_gpu(cfg, inp, dev), run_oracle(cfg, inp)
+    check_scores(g["S"], o["S"], cfg.n_sink, cfg.w)
+    check_kept(g["kept"], o["kept"], o["pooled"], cfg.n_sink, cfg.w, cfg.budget)
+    return g, o
+
+
+@pytest.mark.parametrize("n,budget", [(33, 128), (40, 7), (100, 0), (161, 128), (162, 128)])
+def test_budget_edges(dev, n, budget):
+    """No candidates, fewer candidates than B, B = 0, and n = n_sink + w + B (+1)."""
+    cfg = TINY.with_(name="edge-n%d-b%d" % (n, budget), n=n, budget=budget, n_facts=4,
+                     dtype="bf16", seed=21)
+    g, o = _edge_case(dev, cfg, lore_inputs(cfg))
+    assert g["kept"].shape[-1] == cfg.n_keep
+    assert np.array_equal(g["kept"], o["kept"])
+
+
+def test_exact_ties_keep_lower_indices(dev):
+    """Equal keys everywhere and one shared value vector on every candidate:
+    all candidates score exactly alike, so the selection must be the B lowest
+    candidate indices (n_sink = 4 keeps every chunk whole, so chunk means of
+    equal scores stay exactly equal)."""
+    cfg = TINY.with_(name="ties", n=300, dtype="bf16", budget=20, n_sink=4, seed=22)
+    inp = lore_inputs(cfg)
+    inp["K"][:] = 0.25
+    v0 = inp["V"][:, :, 5:6, :].clone()
+    inp["V"][:, :, : cfg.n - cfg.w, :] = v0
+    g, o = _edge_case(dev, cfg, inp)
+    expect = np.concatenate([np.arange(4), np.arange(4, 24), np.arange(300 - 32, 300)])
+    for row in g["kept"].reshape(-1, g["kept"].shape[-1]):
+        assert np.array_equal(row, expect)
+
+
+def test_deterministic(dev):
+    cfg = MISTRAL_16K.with_(name="det", n=4096)
+    inp = lore_inputs(cfg)
+    runs = [run_gpu(cfg, inp, dev) for _ in range(3)]
+    for r in runs[1:]:
+        assert np.array_equal(r["S"], runs[0]["S"])
+        assert np.array_equal(r["kept"], runs[0]["kept"])
+        assert np.array_equal(r["O"], runs[0]["O"])
