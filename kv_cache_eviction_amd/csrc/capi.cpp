@@ -43,7 +43,7 @@ struct LorePlan {
   int gsplits;
   size_t probs_bytes, deletion_bytes, topb_bytes;
   // deletion layout
-  size_t off_gpart, off_gv, off_yhi, off_ylo, off_consts, off_n;
+  size_t off_gpart, off_gv, off_gr, off_yhi, off_ylo, off_consts, off_n;
   // probs layout
   size_t off_pm, off_pl, off_po;
 };
@@ -87,7 +87,8 @@ LorePlan plan_lore(const kvs_lore_desc *d) {
   p.gsplits = kvs::gram_splits(d->h_q, d->d_model);
   p.off_gpart = 0;
   p.off_gv = align_up(p.off_gpart + (size_t)p.gsplits * d->h_q * D * D * 4);
-  p.off_yhi = align_up(p.off_gv + (size_t)d->h_q * D * D * vbytes);
+  p.off_gr = align_up(p.off_gv + (size_t)d->h_q * D * D * vbytes);
+  p.off_yhi = align_up(p.off_gr + (size_t)d->h_q * D * D * 4);
   p.off_ylo = align_up(p.off_yhi + heads * 64 * D * vbytes);
   p.off_consts = align_up(p.off_ylo + heads * 64 * D * vbytes);
   p.off_n = align_up(p.off_consts + heads * 64 * 16);
@@ -184,6 +185,7 @@ KVS_API kvs_status kvscore_deletion(const kvs_lore_desc *desc, const void *Q, co
   const kvs::RowGeom geo = lore_geom(desc);
   float *gpart = at<float>(ws, p.off_gpart);
   void *gv = at<void>(ws, p.off_gv);
+  float *gr = at<float>(ws, p.off_gr);
   void *yhi = at<void>(ws, p.off_yhi), *ylo = at<void>(ws, p.off_ylo);
   float4 *consts = at<float4>(ws, p.off_consts);
   float *nn = at<float>(ws, p.off_n);
@@ -193,7 +195,7 @@ KVS_API kvs_status kvscore_deletion(const kvs_lore_desc *desc, const void *Q, co
   if (e != hipSuccess) return hip_status(e, "gram");
   e = kvs::launch_deletion_prep(desc->dtype, desc->d, gpart, p.gsplits, O, row_max, row_sum, omega,
                                 desc->batch, desc->h_q, desc->n, geo.nq, desc->w, desc->m, desc->t,
-                                desc->lambda_l, gv, yhi, ylo, consts, s);
+                                desc->lambda_l, gv, gr, yhi, ylo, consts, s);
   if (e != hipSuccess) return hip_status(e, "deletion prep");
   e = kvs::launch_vnorm(desc->dtype, desc->d, V, gv, desc->batch, desc->n, npad, desc->h_q,
                         desc->h_kv, nn, s);

@@ -116,12 +116,87 @@ __device__ __forceinline__ typename FragOf<To>::type convert8(const typename Fra
 // ---- 16-byte vector copies ---------------------------------------------------
 struct alignas(16) U128 { uint32_t x, y, z, w; };
 
+template <typename T> __device__ __forceinline__ uint32_t bits16(T x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, x);
+}
+
+// Stage rows [0, nrows) (nrows <= 32) x D of a row-major matrix with row
+// stride ld into LDS transposed: T[c][r] at T[c * TROW + r], converted to Tout.
+// 16-bit outputs: each thread takes a row pair and one 16-byte chunk and
+// writes packed dwords, so consecutive lanes store consecutive dwords of one
+// LDS row.  Rows past nrows are zero.
+template <typename Tin, typename Tout, int D, int TROW>
+__device__ __forceinline__ void stage_transposed32(const Tin *__restrict__ src, long ld, int nrows,
+                                                   Tout *__restrict__ T) {
+  constexpr int EPC = 16 / (int)sizeof(Tin);
+  constexpr int CPR = D / EPC;
+  if constexpr (sizeof(Tout) == 2) {
+    for (int idx = threadIdx.x; idx < 16 * CPR; idx += blockDim.x) {
+      const int kp = idx % 16, ch = idx / 16;
+      const int r0 = 2 * kp;
+      U128 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+      if (r0 < nrows) a = *reinterpret_cast<const U128 *>(src + (long)r0 * ld + ch * EPC);
+      if (r0 + 1 < nrows) b = *reinterpret_cast<const U128 *>(src + (long)(r0 + 1) * ld + ch * EPC);
+      const Tin *ae = reinterpret_cast<const Tin *>(&a);
+      const Tin *be = reinterpret_cast<const Tin *>(&b);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const uint32_t packed = bits16(from_f32<Tout>(to_f32(ae[e]))) |
+                                (bits16(from_f32<Tout>(to_f32(be[e]))) << 16);
+        *reinterpret_cast<uint32_t *>(&T[(ch * EPC + e) * TROW + r0]) = packed;
+      }
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < 32 * CPR; idx += blockDim.x) {
+      const int r = idx % 32, ch = idx / 32;
+      U128 a = {0, 0, 0, 0};
+      if (r < nrows) a = *reinterpret_cast<const U128 *>(src + (long)r * ld + ch * EPC);
+      const Tin *ae = reinterpret_cast<const Tin *>(&a);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) T[(ch * EPC + e) * TROW + r] = from_f32<Tout>(to_f32(ae[e]));
+    }
+  }
+}
+
+// 16 bytes of Tin converted to Tout and stored as one packed LDS write
+// (8 x bf16 -> 8 x f16, or a plain copy when the types match).
+template <typename Tin, typename Tout>
+__device__ __forceinline__ void store_converted16(const U128 &v, Tout *dst) {
+  if constexpr (sizeof(Tin) == sizeof(Tout) && (sizeof(Tin) == 4 || __is_same(Tin, Tout))) {
+    *reinterpret_cast<U128 *>(dst) = v;
+  } else {
+    const Tin *ve = reinterpret_cast<const Tin *>(&v);
+    U128 o;
+    uint32_t *ow = reinterpret_cast<uint32_t *>(&o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      ow[e] = bits16(from_f32<Tout>(to_f32(ve[2 * e]))) |
+              (bits16(from_f32<Tout>(to_f32(ve[2 * e + 1]))) << 16);
+    *reinterpret_cast<U128 *>(dst) = o;
+  }
+}
+
 // ---- wave reductions ---------------------------------------------------------
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
 __device__ __forceinline__ float wave_sum_xor(float v, int mask) {
   return v + __shfl_xor(v, mask, 64);
+}
+
+// Sum over the 16 lanes of each DPP row (lanes 16r..16r+15); every lane of the
+// row receives the total.  quad_perm [1,0,3,2] and [2,3,0,1] sum each quad,
+// row_half_mirror pairs the two quads of each half-row, row_mirror the halves.
+template <int CTRL> __device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  return v;
 }
 
 // Fast hardware transcendentals (about 1 ulp).

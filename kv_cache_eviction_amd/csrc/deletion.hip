@@ -55,14 +55,8 @@ gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
 
   for (int k0 = k_begin; k0 < k_end; k0 += 32) {
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 32 * CPR; idx += blockDim.x) {
-      const int kr = idx / CPR, ch = idx % CPR;
-      U128 v = {0, 0, 0, 0};
-      if (k0 + kr < k_end) v = *reinterpret_cast<const U128 *>(W + (long)(k0 + kr) * ld + (long)h * D + ch * EPC);
-      const Tin *ve = reinterpret_cast<const Tin *>(&v);
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) Wt[(ch * EPC + e) * WROW + kr] = ve[e];
-    }
+    stage_transposed32<Tin, Tin, D, WROW>(W + (long)k0 * ld + (long)h * D, ld,
+                                          min(32, k_end - k0), Wt);
     __syncthreads();
     FW af[RPW];
 #pragma unroll
@@ -98,61 +92,76 @@ int gram_splits(int h_q, int d_model) {
 }
 
 // ---------------------------------------------------------------------------
-// Per (query head, sequence): sum the G_h partials (fixed order), round G_h to
-// the value type once (G~), and form every term of the norm expansion from
-// that same G~: y_q = G~ o_q and pi_q = o_q . y_q here, N_i = v_i^T G~ v_i in
-// vnorm_kernel.  Then N - 2x + pi equals (v - o)^T G~ (v - o) up to fp32
-// accumulation, so no term carries a rounding the others do not share and
-// tokens whose value is close to the attention output (where the three terms
-// nearly cancel) keep their relative accuracy.  y_q is stored as a hi + lo
-// pair of the value type (y = hi + lo to ~22 bits) for the MFMA product V.y.
-// Per-row constants of the score pass:
+// Sum the G_h partials (fixed order) and round G_h to the value type once:
+// Gv = G~ (value type, for the MFMA in vnorm_kernel) and Gr = float(G~).  Every
+// term of the norm expansion is then formed from that same G~: y_q = G~ o_q
+// and pi_q = o_q . y_q in prep_kernel, N_i = v_i^T G~ v_i in vnorm_kernel.  So
+// N - 2x + pi equals (v - o)^T G~ (v - o) up to fp32 accumulation: no term
+// carries a rounding the others do not share, and tokens whose value is close
+// to the attention output (where the three terms nearly cancel) keep their
+// relative accuracy.
+template <int D, typename TV>
+__global__ void __launch_bounds__(256)
+gram_reduce_kernel(const float *__restrict__ Gpart, int gsplits, int h_q, TV *__restrict__ Gv,
+                   float *__restrict__ Gr) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long total = (long)h_q * D * D;
+  if (idx >= total) return;
+  float g = 0.f;
+  for (int s = 0; s < gsplits; ++s) g += Gpart[(long)s * total + idx];
+  const TV gr = from_f32<TV>(g);
+  Gv[idx] = gr;
+  Gr[idx] = to_f32(gr);
+}
+
+// Per (query head, sequence, 16-row group): y_q = G~ o_q (stored as a hi + lo
+// pair of the value type, y = hi + lo to ~22 bits, for the MFMA product V.y),
+// pi_q = o_q . y_q, and the per-row constants of the score pass:
 //   x = beta2 = row_max*log2(e) + log2(row_sum)   (a = exp2(s*log2e/sqrt(d) - beta2))
 //   y = pi_q,  z = row weight (1/w for window rows, lambda_L omega_m / T for
 //   lookahead rows, 0 for padding rows),  w = bits of the last visible token.
 template <int D, typename TV>
 __global__ void __launch_bounds__(256)
-prep_kernel(const float *__restrict__ Gpart, int gsplits, const float *__restrict__ O,
+prep_kernel(const float *__restrict__ Gr, const float *__restrict__ O,
             const float *__restrict__ row_max, const float *__restrict__ row_sum,
             const float *__restrict__ omega, int h_q, int n, int nq, int w, int m, int t,
-            float lambda_l, TV *__restrict__ Gv, TV *__restrict__ Yhi, TV *__restrict__ Ylo,
+            float lambda_l, TV *__restrict__ Yhi, TV *__restrict__ Ylo,
             float4 *__restrict__ consts) {
   constexpr int SLAB = 32;
-  __shared__ float Os[64 * D];
+  constexpr int RG = 16;  // rows per block
+  __shared__ float Os[RG * D];
   __shared__ float Gs[SLAB * (D + 1)];
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int h = blockIdx.x, b = blockIdx.y, r0 = blockIdx.z * RG;
   const long hb = (long)b * h_q + h;
-  for (int idx = threadIdx.x; idx < 64 * D; idx += blockDim.x) {
-    const int r = idx / D;
+  for (int idx = threadIdx.x; idx < RG * D; idx += blockDim.x) {
+    const int r = r0 + idx / D;
     Os[idx] = r < nq ? O[(hb * nq + r) * D + idx % D] : 0.f;
   }
-  // thread -> (row r = tid/4, 8 consecutive outputs of every 32-row slab)
-  const int r = threadIdx.x >> 2, sub = threadIdx.x & 3;
+  // thread -> (row rl = tid/16, 2 consecutive outputs of every 32-row slab)
+  const int rl = threadIdx.x >> 4, sub = threadIdx.x & 15;
+  const int r = r0 + rl;
   float pi = 0.f;
   for (int dd0 = 0; dd0 < D; dd0 += SLAB) {
     __syncthreads();
     for (int idx = threadIdx.x; idx < SLAB * D; idx += blockDim.x) {
       const int row = idx / D, k = idx % D;
-      float g = 0.f;
-      for (int s = 0; s < gsplits; ++s) g += Gpart[(((long)s * h_q + h) * D + dd0 + row) * D + k];
-      const TV gr = from_f32<TV>(g);
-      Gs[row * (D + 1) + k] = to_f32(gr);
-      if (b == 0) Gv[((long)h * D + dd0 + row) * D + k] = gr;
+      Gs[row * (D + 1) + k] = Gr[((long)h * D + dd0 + row) * D + k];
     }
     __syncthreads();
-    for (int u = 0; u < SLAB / 4; ++u) {
-      const int row = sub * (SLAB / 4) + u;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int row = sub * 2 + u;
       float y = 0.f;
-      for (int k = 0; k < D; ++k) y += Gs[row * (D + 1) + k] * Os[r * D + k];
+      for (int k = 0; k < D; ++k) y += Gs[row * (D + 1) + k] * Os[rl * D + k];
       if (r >= nq) y = 0.f;
-      pi += Os[r * D + dd0 + row] * y;
+      pi += Os[rl * D + dd0 + row] * y;
       const TV hi = from_f32<TV>(y);
       Yhi[(hb * 64 + r) * D + dd0 + row] = hi;
       Ylo[(hb * 64 + r) * D + dd0 + row] = from_f32<TV>(y - to_f32(hi));
     }
   }
-  pi += __shfl_xor(pi, 1, 64);
-  pi += __shfl_xor(pi, 2, 64);
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) pi += __shfl_xor(pi, o, 64);
   if (sub == 0) {
     float beta2 = 0.f, wr = 0.f;
     int last = -1;
@@ -171,66 +180,131 @@ prep_kernel(const float *__restrict__ Gpart, int gsplits, const float *__restric
 }
 
 // ---------------------------------------------------------------------------
-// N[b][h][i] = v_i^T G_h v_i.  Each wave holds G_h as A fragments with its
-// rows permuted by sigma(db, m) = 32*(db/2) + 8*(m/4) + 4*(db%2) + m%4, which
-// lands output row 4*(lane/16)+j of block db on the head-dim index whose V
-// value the lane already holds in its own B fragment (k-step db/2, element
-// 4*(db%2)+j): the quadratic form then needs no data exchange until the final
-// two cross-lane adds.
+// N[b][h][i] = v_i^T G~_h v_i.  A workgroup of 4 waves serves up to 4 query
+// heads of one KV head over a token range: 64-token V tiles are read from
+// global memory once, converted to the value type once and staged in LDS
+// (double-buffered: the next tile's loads are in flight while the current one
+// is computed), and every wave applies its own head's G~_h to the tile.  With
+// fewer than 4 heads in the group the spare waves split the tile's 16-token
+// blocks instead.  Each wave holds G~_h as A fragments with its rows permuted
+// by sigma(db, m) = 32*(db/2) + 8*(m/4) + 4*(db%2) + m%4, which lands output
+// row 4*(lane/16)+j of block db on the head-dim index whose V value the lane
+// already holds in its own B fragment (k-step db/2, element 4*(db%2)+j): the
+// quadratic form then needs no data exchange until the final two cross-lane
+// adds.
 template <typename Tin, int D>
 __global__ void __launch_bounds__(256)
 vnorm_kernel(const Tin *__restrict__ V, const typename ValueType<Tin>::type *__restrict__ Gv,
-             int n, int n_pad, int h_q, int h_kv, int tpwave, float *__restrict__ Nn) {
+             int n, int n_pad, int h_q, int h_kv, int tpw, int nchunk, float *__restrict__ Nn) {
   typedef typename ValueType<Tin>::type TV;
   typedef typename FragOf<TV>::type FV;
   constexpr int KS = D / 32;
   constexpr int DB = D / 16;
+  constexpr int TN = 64;
+  constexpr int EPC = 16 / (int)sizeof(Tin);
+  constexpr int CPR = D / EPC;
+  constexpr int VROW = D + 16 / (int)sizeof(TV);
+  constexpr int PF = (TN * CPR + 255) / 256;
+  __shared__ __align__(16) TV Vs[2][TN * VROW];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (h_q / h_kv);
+  const int G = h_q / h_kv;
+  const int hpw = G < 4 ? G : 4;          // heads per workgroup
+  const int ngrp = (G + hpw - 1) / hpw;   // workgroups per KV head and token range
+  const int tparts = 4 / hpw;             // waves sharing one head's tile
+  // logical (sequence, KV head, head group, token chunk) of this block
+  const long L = blockIdx.x;
+  const int chunk_i = (int)(L % nchunk);
+  const long rest = L / nchunk;
+  const int hgi = (int)(rest % ngrp);
+  const int kvh = (int)((rest / ngrp) % h_kv);
+  const int b = (int)(rest / ((long)ngrp * h_kv));
+  const int tp = wv / hpw;
+  const int hg = hgi * hpw + wv % hpw;
+  const bool active = tp < tparts && hg < G;
+  const int h = kvh * G + (active ? hg : 0);
+
   FV gf[DB][KS];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     const int row = 32 * (db >> 1) + 8 * (col >> 2) + 4 * (db & 1) + (col & 3);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      gf[db][ks] = load8<TV>(Gv + ((long)h * D + row) * D + ks * 32 + 8 * grp);
+      gf[db][ks] = active ? load8<TV>(Gv + ((long)h * D + row) * D + ks * 32 + 8 * grp) : zero8<TV>();
   }
-  const Tin *Vg = V + ((long)b * h_kv + g) * (long)n * D;
+  const Tin *Vg = V + ((long)b * h_kv + kvh) * (long)n * D;
   float *Nh = Nn + ((long)b * h_q + h) * n_pad;
-  const int t_begin = (blockIdx.x * 4 + wv) * tpwave;
-  const int t_end = min(n_pad, t_begin + tpwave);
-  for (int t0 = t_begin; t0 < t_end; t0 += 16) {
-    const int tok = t0 + col;
-    FV vf[KS];
+  const int t_begin = chunk_i * tpw;
+  const int t_end = min(n_pad, t_begin + tpw);
+  const int nt = (t_end - t_begin + TN - 1) / TN;
+
+  U128 pv[PF];
+  auto prefetch = [&](int t0) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      vf[ks] = tok < n ? convert8<TV, Tin>(load8<Tin>(Vg + (long)tok * D + ks * 32 + 8 * grp))
-                       : zero8<TV>();
-    float np = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mma(gf[db][ks], vf[ks], acc);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) np += acc[j] * frag_elem(vf[db >> 1], 4 * (db & 1) + j);
+    for (int u = 0; u < PF; ++u) {
+      const int idx = threadIdx.x + u * 256;
+      const int row = idx / CPR, ch = idx % CPR;
+      pv[u] = U128{0, 0, 0, 0};
+      if (idx < TN * CPR && t0 + row < n)
+        pv[u] = *reinterpret_cast<const U128 *>(Vg + (long)(t0 + row) * D + ch * EPC);
     }
-    np = wave_sum_xor(np, 16);
-    np = wave_sum_xor(np, 32);
-    if (grp == 0 && tok < t_end) Nh[tok] = np;
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int idx = threadIdx.x + u * 256;
+      if (idx < TN * CPR) {
+        const int row = idx / CPR, ch = idx % CPR;
+        store_converted16<Tin, TV>(pv[u], &Vs[buf][row * VROW + ch * EPC]);
+      }
+    }
+  };
+  if (nt > 0) {
+    prefetch(t_begin);
+    stash(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < nt; ++it) {
+    const int t0 = t_begin + it * TN;
+    const int cur = it & 1;
+    if (it + 1 < nt) prefetch(t0 + TN);
+    if (active) {
+      for (int tb = tp; tb < TN / 16; tb += tparts) {
+        const int tok = t0 + tb * 16 + col;
+        FV vf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          vf[ks] = load8<TV>(&Vs[cur][(tb * 16 + col) * VROW + ks * 32 + 8 * grp]);
+        float np = 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc = mma(gf[db][ks], vf[ks], acc);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) np += acc[j] * frag_elem(vf[db >> 1], 4 * (db & 1) + j);
+        }
+        np = wave_sum_xor(np, 16);
+        np = wave_sum_xor(np, 32);
+        if (grp == 0 && tok < t_end) Nh[tok] = np;
+      }
+    }
+    if (it + 1 < nt) stash(cur ^ 1);
+    __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
 // Score pass.  One workgroup per (token range, KV head, sequence); each query
 // head's 64 rows are spread over 4/QBW waves.  K (and V, converted to the
-// value type) tiles of 64 tokens are staged in LDS and shared by the group.
-// Logits are formed transposed (S^T = K Q^T): a lane owns one query column
-// (row constants live in registers) and four tokens per 16-token block, so the
-// sum over the query rows is in-lane plus one 16-lane reduction per token; the
-// per-wave partial sums are combined across waves in a fixed order.
+// value type) tiles of 64 tokens are staged in LDS and shared by the group,
+// double-buffered: the next tile's global loads are issued into registers
+// before the current tile is computed and stored to the other buffer after,
+// so one barrier per tile separates the two.  Logits are formed transposed
+// (S^T = K Q^T): a lane owns one query column (row constants live in
+// registers) and four tokens per 16-token block, so the sum over the query
+// rows is in-lane plus one 16-lane DPP reduction per token; the per-wave
+// partial sums are combined across waves in a fixed order.
 //   MODE 0 (LORE): out = out_scale * sum_h sum_q wr_q * a/(1-a+eps) * sqrt(max(0, N - 2x + pi)),
 //                  x = v . (y_hi + y_lo) as two MFMA products
 //   MODE 1 (H2O):  out = sum over causal rows of a
@@ -252,9 +326,12 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
   constexpr int CPR = D / EPC;
   constexpr int KROW = D + EPC;
   constexpr int VROW = D + 16 / (int)sizeof(TV);
-  __shared__ __align__(16) Tin Ks[TN * KROW];
-  __shared__ __align__(16) TV Vs[MODE == 0 ? TN * VROW : 8];
-  __shared__ __align__(16) float red[MAXW * TN];
+  // 16-byte chunks per thread and tile: the smallest block of a MAXW variant
+  // has at least 32*MAXW threads (host checks)
+  constexpr int PF = (TN * CPR + 32 * MAXW - 1) / (32 * MAXW);
+  __shared__ __align__(16) Tin Ks[2][TN * KROW];
+  __shared__ __align__(16) TV Vs[MODE == 0 ? 2 : 1][MODE == 0 ? TN * VROW : 8];
+  __shared__ __align__(16) float red[2][MAXW * TN];
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int hv = wv / WPH, qb0 = (wv % WPH) * QBW;
@@ -298,24 +375,44 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
   const int t_end = min(n, t_begin + tpw);
   const float *Nh = Nn + head * (long)n_pad;
   float *Sout = S + ((long)b * h_kv + kvh) * n;
+  const int nt = (t_end - t_begin + TN - 1) / TN;
 
-  for (int t0 = t_begin; t0 < t_end; t0 += TN) {
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < TN * CPR; idx += blockDim.x) {
+  U128 pk[PF], pv[MODE == 0 ? PF : 1];
+  auto prefetch = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int idx = threadIdx.x + u * blockDim.x;
       const int row = idx / CPR, ch = idx % CPR;
       const int tok = t0 + row;
-      U128 kv = {0, 0, 0, 0};
-      if (tok < n) kv = *reinterpret_cast<const U128 *>(K + kv_base + (long)tok * D + ch * EPC);
-      *reinterpret_cast<U128 *>(&Ks[row * KROW + ch * EPC]) = kv;
-      if (MODE == 0) {
-        U128 vv = {0, 0, 0, 0};
-        if (tok < n) vv = *reinterpret_cast<const U128 *>(V + kv_base + (long)tok * D + ch * EPC);
-        const Tin *ve = reinterpret_cast<const Tin *>(&vv);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) Vs[row * VROW + ch * EPC + e] = from_f32<TV>(to_f32(ve[e]));
+      pk[u] = U128{0, 0, 0, 0};
+      if (MODE == 0) pv[u] = U128{0, 0, 0, 0};
+      if (idx < TN * CPR && tok < n) {
+        pk[u] = *reinterpret_cast<const U128 *>(K + kv_base + (long)tok * D + ch * EPC);
+        if (MODE == 0) pv[u] = *reinterpret_cast<const U128 *>(V + kv_base + (long)tok * D + ch * EPC);
       }
     }
-    __syncthreads();
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int idx = threadIdx.x + u * blockDim.x;
+      if (idx < TN * CPR) {
+        const int row = idx / CPR, ch = idx % CPR;
+        *reinterpret_cast<U128 *>(&Ks[buf][row * KROW + ch * EPC]) = pk[u];
+        if (MODE == 0) store_converted16<Tin, TV>(pv[u], &Vs[buf][row * VROW + ch * EPC]);
+      }
+    }
+  };
+
+  if (nt > 0) {
+    prefetch(t_begin);
+    stash(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < nt; ++it) {
+    const int t0 = t_begin + it * TN;
+    const int cur = it & 1;
+    if (it + 1 < nt) prefetch(t0 + TN);
 #pragma unroll
     for (int tb = 0; tb < TN / 16; ++tb) {
       const int tok0 = t0 + tb * 16;
@@ -325,8 +422,8 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
         FV vf[MODE == 0 ? KS : 1];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          kf[ks] = load8<Tin>(&Ks[(tb * 16 + col) * KROW + ks * 32 + 8 * grp]);
-          if (MODE == 0) vf[ks] = load8<TV>(&Vs[(tb * 16 + col) * VROW + ks * 32 + 8 * grp]);
+          kf[ks] = load8<Tin>(&Ks[cur][(tb * 16 + col) * KROW + ks * 32 + 8 * grp]);
+          if (MODE == 0) vf[ks] = load8<TV>(&Vs[cur][(tb * 16 + col) * VROW + ks * 32 + 8 * grp]);
         }
         float4 nv = make_float4(0.f, 0.f, 0.f, 0.f);
         if (MODE == 0) nv = *reinterpret_cast<const float4 *>(Nh + tok0 + 4 * grp);
@@ -360,24 +457,18 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
         }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float v = tacc[j];
-        v = wave_sum_xor(v, 1);
-        v = wave_sum_xor(v, 2);
-        v = wave_sum_xor(v, 4);
-        v = wave_sum_xor(v, 8);
-        tacc[j] = v;
-      }
+      for (int j = 0; j < 4; ++j) tacc[j] = row16_sum(tacc[j]);
       if (col == 0)
-        *reinterpret_cast<float4 *>(&red[wv * TN + tb * 16 + 4 * grp]) =
+        *reinterpret_cast<float4 *>(&red[cur][wv * TN + tb * 16 + 4 * grp]) =
             make_float4(tacc[0], tacc[1], tacc[2], tacc[3]);
     }
+    if (it + 1 < nt) stash(cur ^ 1);
     __syncthreads();
     for (int t = threadIdx.x; t < TN; t += blockDim.x) {
       const int tok = t0 + t;
       if (tok < t_end) {
         float sum = 0.f;
-        for (int w = 0; w < nwaves; ++w) sum += red[w * TN + t];
+        for (int w = 0; w < nwaves; ++w) sum += red[cur][w * TN + t];
         Sout[tok] = sum * out_scale;
       }
     }
@@ -411,13 +502,21 @@ hipError_t launch_gram(int etype, int d, const void *W_O, int d_model, int h_q, 
 template <int D, typename TV>
 static hipError_t run_prep(const float *Gpart, int gsplits, const float *O, const float *row_max,
                            const float *row_sum, const float *omega, int batch, int h_q, int n,
-                           int nq, int w, int m, int t, float lambda_l, void *Gv, void *Yhi,
-                           void *Ylo, float4 *consts, hipStream_t st) {
+                           int nq, int w, int m, int t, float lambda_l, void *Gv, float *Gr,
+                           void *Yhi, void *Ylo, float4 *consts, hipStream_t st) {
+  {
+    TimedLaunch tl_("gram_reduce", st);
+    const long total = (long)h_q * D * D;
+    hipLaunchKernelGGL((gram_reduce_kernel<D, TV>), dim3((unsigned)((total + 255) / 256)),
+                       dim3(256), 0, st, Gpart, gsplits, h_q, (TV *)Gv, Gr);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   {
     TimedLaunch tl_("deletion_prep", st);
-    hipLaunchKernelGGL((prep_kernel<D, TV>), dim3(h_q, batch), dim3(256), 0, st, Gpart, gsplits,
-                       O, row_max, row_sum, omega, h_q, n, nq, w, m, t, lambda_l, (TV *)Gv,
-                       (TV *)Yhi, (TV *)Ylo, consts);
+    hipLaunchKernelGGL((prep_kernel<D, TV>), dim3(h_q, batch, 4), dim3(256), 0, st, Gr, O,
+                       row_max, row_sum, omega, h_q, n, nq, w, m, t, lambda_l, (TV *)Yhi,
+                       (TV *)Ylo, consts);
   }
   return hipGetLastError();
 }
@@ -425,11 +524,11 @@ static hipError_t run_prep(const float *Gpart, int gsplits, const float *O, cons
 hipError_t launch_deletion_prep(int etype, int d, const float *Gpart, int gsplits, const float *O,
                                 const float *row_max, const float *row_sum, const float *omega,
                                 int batch, int h_q, int n, int nq, int w, int m, int t,
-                                float lambda_l, void *Gv, void *Yhi, void *Ylo, float4 *consts,
-                                hipStream_t st) {
+                                float lambda_l, void *Gv, float *Gr, void *Yhi, void *Ylo,
+                                float4 *consts, hipStream_t st) {
 #define KVS_P(DD, TV) \
   return run_prep<DD, TV>(Gpart, gsplits, O, row_max, row_sum, omega, batch, h_q, n, nq, w, m, t, \
-                          lambda_l, Gv, Yhi, Ylo, consts, st)
+                          lambda_l, Gv, Gr, Yhi, Ylo, consts, st)
   if (etype == E_F32) { if (d == 64) KVS_P(64, float); KVS_P(128, float); }
   if (d == 64) KVS_P(64, f16);
   KVS_P(128, f16);
@@ -440,12 +539,19 @@ template <typename Tin, int D>
 static hipError_t run_vnorm(const void *V, const void *Gv, int batch, int n, int n_pad, int h_q,
                             int h_kv, float *Nn, hipStream_t st) {
   typedef typename ValueType<Tin>::type TV;
-  const int tpwave = 256;
-  const int chunks = (n_pad + 4 * tpwave - 1) / (4 * tpwave);
+  // about 512 workgroups (two per CU) of whole 64-token tiles
+  const int G = h_q / h_kv;
+  const int hpw = G < 4 ? G : 4;
+  const long units = (long)((G + hpw - 1) / hpw) * h_kv * batch;
+  const int tiles = n_pad / 64;
+  const long want = std::max(1L, 512L / units);
+  const int tpw = 64 * (int)((tiles + want - 1) / want);
+  const int nchunk = (n_pad + tpw - 1) / tpw;
+  const long blocks = (long)nchunk * units;
   {
     TimedLaunch tl_("vnorm", st);
-    hipLaunchKernelGGL((vnorm_kernel<Tin, D>), dim3(chunks, h_q, batch), dim3(256), 0, st,
-                       (const Tin *)V, (const TV *)Gv, n, n_pad, h_q, h_kv, tpwave, Nn);
+    hipLaunchKernelGGL((vnorm_kernel<Tin, D>), dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const Tin *)V, (const TV *)Gv, n, n_pad, h_q, h_kv, tpw, nchunk, Nn);
   }
   return hipGetLastError();
 }
@@ -471,6 +577,8 @@ static hipError_t run_score_w(const void *Q, const void *K, const void *V, const
   tpw = (tpw + 63) / 64 * 64;
   if (tpw < 64) tpw = 64;
   const int blocks = (int)((geo.n + tpw - 1) / tpw);
+  const int threads = 64 * geo.group * (4 / QBW);
+  if (threads < 32 * MAXW || threads > 64 * MAXW) return hipErrorInvalidConfiguration;
   {
     TimedLaunch tl_((MODE == 0 ? "score_lore" : "score_h2o_colsum"), st);
     hipLaunchKernelGGL((score_kernel<Tin, D, MODE, MAXW, QBW>), dim3(blocks, h_kv, batch),
@@ -481,7 +589,8 @@ static hipError_t run_score_w(const void *Q, const void *K, const void *V, const
   return hipGetLastError();
 }
 
-// Waves per workgroup = group * 4 / QBW <= 16.
+// Waves per workgroup = group * 4 / QBW <= 16; MAXW is the next power of two
+// (at least 2), so a block always has between 32*MAXW and 64*MAXW threads.
 template <typename Tin, int D>
 static hipError_t run_score(int mode, const void *Q, const void *K, const void *V, const void *Yhi,
                             const void *Ylo, const float4 *consts, const float *Nn, int n_pad,
@@ -490,7 +599,13 @@ static hipError_t run_score(int mode, const void *Q, const void *K, const void *
 #define KVS_RS(MODE, MAXW, QBW)                                                                \
   return run_score_w<Tin, D, MODE, MAXW, QBW>(Q, K, V, Yhi, Ylo, consts, Nn, n_pad, geo, batch, \
                                               h_kv, eps, out_scale, S, st)
-  if (mode == 1) KVS_RS(1, 16, 4);
+  if (mode == 1) {
+    const int waves = geo.group;  // QBW = 4: one wave per 64 prompt rows
+    if (waves <= 2) KVS_RS(1, 2, 4);
+    if (waves <= 4) KVS_RS(1, 4, 4);
+    if (waves <= 8) KVS_RS(1, 8, 4);
+    KVS_RS(1, 16, 4);
+  }
   if (geo.group <= 2) KVS_RS(0, 4, 2);
   if (geo.group <= 4) KVS_RS(0, 8, 2);
   if (geo.group <= 8) KVS_RS(0, 16, 2);

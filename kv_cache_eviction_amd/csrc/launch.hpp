@@ -48,8 +48,8 @@ hipError_t launch_gram(int etype, int d, const void *W_O, int d_model, int h_q, 
 hipError_t launch_deletion_prep(int etype, int d, const float *Gpart, int gsplits, const float *O,
                                 const float *row_max, const float *row_sum, const float *omega,
                                 int batch, int h_q, int n, int nq, int w, int m, int t,
-                                float lambda_l, void *Gv, void *Yhi, void *Ylo, float4 *consts,
-                                hipStream_t st);
+                                float lambda_l, void *Gv, float *Gr, void *Yhi, void *Ylo,
+                                float4 *consts, hipStream_t st);
 hipError_t launch_vnorm(int etype, int d, const void *V, const void *Gv, int batch, int n,
                         int n_pad, int h_q, int h_kv, float *Nn, hipStream_t st);
 // mode 0: LORE deletion score (Yhi/Ylo, consts, Nn used); mode 1: causal column sums.

@@ -53,71 +53,139 @@ __device__ int block_exclusive_scan(int v, int *sh, int *total) {
   return excl;
 }
 
+// Pooling: one thread per chunk.  keys[row][c] = order_key(mean of the
+// candidates in chunk c), 0 for chunks with no candidate; pooled (optional)
+// gets each candidate's pooled score and NaN for protected tokens.
+__global__ void __launch_bounds__(256)
+topb_pool_kernel(const float *__restrict__ S, int n, int n_sink, int w, int chunk, int nchunks,
+                 uint32_t *__restrict__ keys_ws, float *__restrict__ pooled) {
+  const long row = blockIdx.y;
+  const int cj = blockIdx.x * blockDim.x + threadIdx.x;
+  if (cj >= nchunks) return;
+  const int lo = n_sink, hi = n - w;
+  const float *Sr = S + row * n;
+  const int c0 = cj * chunk, c1 = min(c0 + chunk, n);
+  const int a = max(c0, lo), e = min(c1, hi);
+  uint32_t key = 0;
+  float P = 0.f;
+  if (e > a) {
+    float s = 0.f;
+    for (int i = a; i < e; ++i) s += Sr[i];
+    P = s / (float)(e - a);
+    key = order_key(P);
+  }
+  keys_ws[row * nchunks + cj] = key;
+  if (pooled) {
+    float *pr = pooled + row * n;
+    for (int i = c0; i < c1; ++i) pr[i] = (i >= lo && i < hi) ? P : __int_as_float(0x7FC00000);
+  }
+}
+
+// Selection: one workgroup per row.  The row's chunk keys are staged in LDS
+// when they fit (up to kKeysLds chunks: 128K tokens at chunk 4), else read
+// from the workspace.
+constexpr int kKeysLds = 32768;
+
 __global__ void __launch_bounds__(1024)
-topb_kernel(const float *__restrict__ S, int n, int n_sink, int w, int chunk, int budget,
-            int n_keep, uint32_t *__restrict__ keys_ws, int32_t *__restrict__ kept,
-            float *__restrict__ pooled) {
-  __shared__ int hist[256];
+topb_select_kernel(int n, int n_sink, int w, int chunk, int budget, int n_keep, int nchunks,
+                   const uint32_t *__restrict__ keys_ws, int32_t *__restrict__ kept) {
+  __shared__ uint32_t lds_keys[kKeysLds];
+  const int keys_in_lds = nchunks <= kKeysLds;
+  // one 256-bin histogram per wave: the high digits of nearby scores collide,
+  // and a shared histogram would serialise every atomic on one bin
+  __shared__ int hist[16 * 256];
   __shared__ int scan_sh[17];
   __shared__ uint32_t s_prefix;
   __shared__ int s_rem;
   const int tid = threadIdx.x, bs = blockDim.x;
   const long row = blockIdx.x;
-  const float *Sr = S + row * n;
   const int lo = n_sink, hi = n - w;
   const int n_cand = hi - lo;
   const int B = min(budget, n_cand);
-  const int nchunks = (n + chunk - 1) / chunk;
-  uint32_t *keys = keys_ws + row * nchunks;
   int32_t *kr = kept + row * n_keep;
-  float *pr = pooled ? pooled + row * n : nullptr;
 
   for (int i = tid; i < n_sink; i += bs) kr[i] = i;
   for (int i = tid; i < w; i += bs) kr[n_sink + B + i] = n - w + i;
-  if (pr) {
-    for (int i = tid; i < lo; i += bs) pr[i] = __int_as_float(0x7FC00000);
-    for (int i = hi + tid; i < n; i += bs) pr[i] = __int_as_float(0x7FC00000);
-  }
-  for (int cj = tid; cj < nchunks; cj += bs) {
-    const int a = max(cj * chunk, lo), e = min(cj * chunk + chunk, hi);
-    uint32_t key = 0;
-    if (e > a) {
-      float s = 0.f;
-      for (int i = a; i < e; ++i) s += Sr[i];
-      const float P = s / (float)(e - a);
-      key = order_key(P);
-      if (pr)
-        for (int i = a; i < e; ++i) pr[i] = P;
-    }
-    keys[cj] = key;
-  }
   if (B <= 0) return;
+
+  const uint32_t *gk = keys_ws + row * nchunks;
+  const uint32_t *keys = gk;
+  constexpr int U = 8;
+  if (keys_in_lds) {
+    for (int base = tid; base < nchunks; base += bs * U) {
+      uint32_t kk[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = base + u * bs;
+        kk[u] = c < nchunks ? gk[c] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = base + u * bs;
+        if (c < nchunks) lds_keys[c] = kk[u];
+      }
+    }
+    keys = lds_keys;
+  }
   __syncthreads();
 
+  const int wv = tid >> 6, nw = bs >> 6;
   uint32_t prefix = 0, mask = 0;
   int rem = B;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += bs) hist[i] = 0;
+    for (int i = tid; i < 16 * 256; i += bs) hist[i] = 0;
     __syncthreads();
-    for (int cj = tid; cj < nchunks; cj += bs) {
-      const int cnt = min(cj * chunk + chunk, hi) - max(cj * chunk, lo);
-      if (cnt <= 0) continue;
-      const uint32_t key = keys[cj];
-      if ((key & mask) != prefix) continue;
-      atomicAdd(&hist[(key >> shift) & 255u], cnt);
+    for (int base = tid; base < nchunks; base += bs * U) {
+      uint32_t kk[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = base + u * bs;
+        kk[u] = c < nchunks ? keys[c] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = base + u * bs;
+        if (c >= nchunks) continue;
+        const int cnt = min(c * chunk + chunk, hi) - max(c * chunk, lo);
+        if (cnt <= 0 || (kk[u] & mask) != prefix) continue;
+        atomicAdd(&hist[wv * 256 + ((kk[u] >> shift) & 255u)], cnt);
+      }
     }
     __syncthreads();
-    if (tid == 0) {
-      int cum = 0, sel = 0;
-      for (int dg = 255; dg >= 0; --dg) {
-        if (cum + hist[dg] >= rem) {
-          sel = dg;
-          break;
-        }
-        cum += hist[dg];
+    for (int dg = tid; dg < 256; dg += bs) {
+      int t = 0;
+      for (int w2 = 0; w2 < nw; ++w2) t += hist[w2 * 256 + dg];
+      hist[dg] = t;  // wave 0's bins now hold the totals
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // wave 0 walks the 256 bins from the top: lane l owns bins 255-4l-j
+      int hb[4], ltot = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hb[j] = hist[255 - 4 * tid - j];
+        ltot += hb[j];
       }
-      s_prefix = prefix | ((uint32_t)sel << shift);
-      s_rem = rem - cum;
+      int incl = ltot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (tid >= o) incl += y;
+      }
+      const int before = incl - ltot;  // tokens in bins above this lane's
+      if (before < rem && incl >= rem) {
+        int cum = before, sel = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (cum + hb[j] >= rem) {
+            sel = 255 - 4 * tid - j;
+            break;
+          }
+          cum += hb[j];
+        }
+        s_prefix = prefix | ((uint32_t)sel << shift);
+        s_rem = rem - cum;
+      }
     }
     __syncthreads();
     prefix = s_prefix;
@@ -126,53 +194,100 @@ topb_kernel(const float *__restrict__ S, int n, int n_sink, int w, int chunk, in
   }
   const uint32_t tau = prefix;
 
-  const int per = (nchunks + bs - 1) / bs;
-  const int c_lo = min(nchunks, tid * per), c_hi = min(nchunks, c_lo + per);
+  // Emit in ascending order.  Wave v owns the contiguous chunk range
+  // [v*per, (v+1)*per), walked 64 chunks at a time (one per lane, so LDS reads
+  // are conflict-free); tau-chunks are taken in index order until rem tokens,
+  // using in-wave prefix sums and one block scan over the wave totals.
+  const int lane = tid & 63;
+  const int per = ((nchunks + nw - 1) / nw + 63) / 64 * 64;
+  const int c_lo = min(nchunks, wv * per), c_hi = min(nchunks, c_lo + per);
+  auto chunk_cnt = [&](int cj) { return min(cj * chunk + chunk, hi) - max(cj * chunk, lo); };
+  auto wave_incl = [&](int x) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    return x;
+  };
+  // pass 1: tau-tokens per wave
   int ties = 0;
-  for (int cj = c_lo; cj < c_hi; ++cj) {
-    const int cnt = min(cj * chunk + chunk, hi) - max(cj * chunk, lo);
-    if (cnt > 0 && keys[cj] == tau) ties += cnt;
+  for (int base = c_lo; base < c_hi; base += 64) {
+    const int cj = base + lane;
+    if (cj < c_hi) {
+      const int cnt = chunk_cnt(cj);
+      if (cnt > 0 && keys[cj] == tau) ties += cnt;
+    }
   }
+  ties = __shfl(wave_incl(ties), 63, 64);
   int total;
-  const int tie_before = block_exclusive_scan(ties, scan_sh, &total);
-  int sel = 0, tb = tie_before;
-  for (int cj = c_lo; cj < c_hi; ++cj) {
-    const int cnt = min(cj * chunk + chunk, hi) - max(cj * chunk, lo);
-    if (cnt <= 0) continue;
-    const uint32_t key = keys[cj];
-    if (key > tau) {
-      sel += cnt;
-    } else if (key == tau) {
-      sel += min(max(rem - tb, 0), cnt);
-      tb += cnt;
+  const int tie_before_wave = block_exclusive_scan(lane == 0 ? ties : 0, scan_sh, &total);
+  const int tie_wave0 = __shfl(tie_before_wave, 0, 64);
+  // pass 2: selected tokens per wave
+  int sel = 0, tie_run = tie_wave0;
+  for (int base = c_lo; base < c_hi; base += 64) {
+    const int cj = base + lane;
+    int cnt = 0, tcnt = 0;
+    uint32_t key = 0;
+    if (cj < c_hi) {
+      cnt = max(chunk_cnt(cj), 0);
+      key = keys[cj];
+      tcnt = (cnt > 0 && key == tau) ? cnt : 0;
     }
+    const int tincl = wave_incl(tcnt);
+    const int tb = tie_run + tincl - tcnt;  // tau-tokens before this chunk
+    if (cnt > 0) {
+      if (key > tau) sel += cnt;
+      else if (key == tau) sel += min(max(rem - tb, 0), cnt);
+    }
+    tie_run += __shfl(tincl, 63, 64);
   }
-  int out = n_sink + block_exclusive_scan(sel, scan_sh, &total);
-  tb = tie_before;
-  for (int cj = c_lo; cj < c_hi; ++cj) {
-    const int a = max(cj * chunk, lo), e = min(cj * chunk + chunk, hi);
-    const int cnt = e - a;
-    if (cnt <= 0) continue;
-    const uint32_t key = keys[cj];
-    int take = 0;
-    if (key > tau) {
-      take = cnt;
-    } else if (key == tau) {
-      take = min(max(rem - tb, 0), cnt);
-      tb += cnt;
+  sel = __shfl(wave_incl(sel), 63, 64);
+  const int out_before_wave = block_exclusive_scan(lane == 0 ? sel : 0, scan_sh, &total);
+  int out_run = n_sink + __shfl(out_before_wave, 0, 64);
+  // pass 3: write
+  tie_run = tie_wave0;
+  for (int base = c_lo; base < c_hi; base += 64) {
+    const int cj = base + lane;
+    int cnt = 0, tcnt = 0, a = 0;
+    uint32_t key = 0;
+    if (cj < c_hi) {
+      cnt = max(chunk_cnt(cj), 0);
+      a = max(cj * chunk, lo);
+      key = keys[cj];
+      tcnt = (cnt > 0 && key == tau) ? cnt : 0;
     }
+    const int tincl = wave_incl(tcnt);
+    const int tb = tie_run + tincl - tcnt;
+    int take = 0;
+    if (cnt > 0) {
+      if (key > tau) take = cnt;
+      else if (key == tau) take = min(max(rem - tb, 0), cnt);
+    }
+    const int oincl = wave_incl(take);
+    int out = out_run + oincl - take;
     for (int i = a; i < a + take; ++i, ++out)
       if (out < n_sink + B) kr[out] = i;
+    out_run += __shfl(oincl, 63, 64);
+    tie_run += __shfl(tincl, 63, 64);
   }
 }
 
 hipError_t launch_topb(const float *S, int rows, int n, int n_sink, int w, int chunk, int budget,
                        int n_keep, uint32_t *keys_ws, int32_t *kept, float *pooled,
                        hipStream_t st) {
+  const int nchunks = (n + chunk - 1) / chunk;
+  {
+    TimedLaunch tl_("topb_pool", st);
+    hipLaunchKernelGGL(topb_pool_kernel, dim3((nchunks + 255) / 256, rows), dim3(256), 0, st, S,
+                       n, n_sink, w, chunk, nchunks, keys_ws, pooled);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   {
     TimedLaunch tl_("topb_select", st);
-    hipLaunchKernelGGL(topb_kernel, dim3(rows), dim3(1024), 0, st, S, n, n_sink, w, chunk, budget,
-                       n_keep, keys_ws, kept, pooled);
+    hipLaunchKernelGGL(topb_select_kernel, dim3(rows), dim3(1024), 0, st, n, n_sink, w, chunk,
+                       budget, n_keep, nchunks, keys_ws, kept);
   }
   return hipGetLastError();
 }
