@@ -150,6 +150,9 @@ def main():
     ap.add_argument("--config", default="llama3.1-8b-128k-32layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-h2o", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy (3 launches), the "
+                         "known-size kernel that scales HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the scoring path needs no collectives, and this "
@@ -163,6 +166,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
     cfg = LORE_CONFIGS[args.config]
     layers = args.layers or cfg.layers
     dt = TORCH_DTYPES[cfg.dtype]

@@ -42,41 +42,57 @@ __device__ __forceinline__ long q_row(const RowGeom &g, int b, int h_kv, int kvh
 }
 
 // QBW = 16-row query blocks per wave: a query head's 64 rows are spread over
-// 4/QBW waves (QBW = 2 keeps the per-wave register set small).  Tiles of 64
-// tokens are double-buffered in LDS: the next tile's global loads go to
-// registers before the current tile is computed and into the other buffer
-// after, so one barrier per tile separates the two.
+// 4/QBW waves.  Tiles of 64 tokens are double-buffered in LDS: the next tile's
+// global loads go to registers before the current tile is computed and into
+// the other buffer after, so one barrier per tile separates the two.
+//
+// Online softmax with a lazy reference: p = 2^(s*c - m_ref) is formed against
+// a per-row reference m_ref that is raised (and O, l rescaled) only when a
+// tile's maximum exceeds it by more than kSlack, so most tiles skip the
+// rescale; p then stays below 2^kSlack, well inside fp16.  The exact running
+// maximum is tracked beside it and the partial (l, O) are brought to it once
+// at the end, so the split outputs are the plain (max, sum, unnormalised O).
+// The visibility mask is applied only on tiles that cross some row's last
+// visible key (or the end of the cache).
 template <typename Tin, int D, bool WITH_O, int MAXW, int QBW>
 __global__ void __launch_bounds__(64 * MAXW)
 attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__restrict__ V,
-                    RowGeom geo, int h_kv, int tps, int splits, float *__restrict__ pm,
-                    float *__restrict__ pl, float *__restrict__ pO) {
+                    RowGeom geo, int h_kv, int hsplit, int hpw, int tps, int splits,
+                    float *__restrict__ pm, float *__restrict__ pl, float *__restrict__ pO) {
   typedef typename ValueType<Tin>::type TV;
   typedef typename FragOf<Tin>::type FQ;
   typedef typename FragOf<TV>::type FV;
   constexpr int KS = D / 32;
   constexpr int DB = D / 16;
   constexpr int TN = 64;
+  constexpr int TB = TN / 16;                 // 16-token blocks per tile
   constexpr int WPH = 4 / QBW;                // waves per query head
   constexpr int EPC = 16 / (int)sizeof(Tin);  // elements per 16-byte chunk
   constexpr int CPR = D / EPC;                // chunks per row
   constexpr int KROW = D + EPC;               // padded LDS row (elements)
   constexpr int VROW = TN + 16 / (int)sizeof(TV);
   constexpr bool V16 = sizeof(TV) == 2;
+  constexpr float kSlack = 8.f;
   // K items: one 16-byte chunk; V items: a row pair (16-bit) or one row (fp32)
   constexpr int KITEMS = TN * CPR;
   constexpr int VITEMS = V16 ? (TN / 2) * CPR : TN * CPR;
-  constexpr int PFK = (KITEMS + 32 * MAXW - 1) / (32 * MAXW);
-  constexpr int PFV = (VITEMS + 32 * MAXW - 1) / (32 * MAXW);
+  constexpr int NT = 64 * MAXW;  // threads per workgroup
+  constexpr int PFK = (KITEMS + NT - 1) / NT;
+  constexpr int PFV = (VITEMS + NT - 1) / NT;
   __shared__ __align__(16) Tin Ks[2][TN * KROW];
   __shared__ __align__(16) TV Vt[WITH_O ? 2 : 1][WITH_O ? D * VROW : 8];
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int hv = wv / WPH, qb0 = (wv % WPH) * QBW;
+  const int s = blockIdx.x, kvh = blockIdx.y / hsplit, b = blockIdx.z;
+  // this workgroup serves query heads [hs*hpw, hs*hpw + hpw) of the group
+  const int hs = blockIdx.y % hsplit, hl = wv / WPH;
+  const int hv = hs * hpw + hl, qb0 = (wv % WPH) * QBW;
+  const bool spare = hl >= hpw || hv >= geo.group;
   const int col = lane & 15, grp = lane >> 4;
-  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int n = geo.n;
   const long kv_base = ((long)b * h_kv + kvh) * (long)n * D;
+  const Tin *Kb = K + kv_base;
+  const Tin *Vb = V + kv_base;
   const int t_begin = s * tps;
   const int t_end = min(n, t_begin + tps);
   const int nt = (t_end - t_begin + TN - 1) / TN;
@@ -84,13 +100,14 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
 
   FQ qf[QBW][KS];
   int lim[QBW];
-  int wave_last = -1;
+  int wave_last = -1, wave_first = 0x7FFFFFFF;  // over this wave's visible rows
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
     const int r = (qb0 + qb) * 16 + col;
-    lim[qb] = row_last(geo, hv, r);
-    wave_last = max(wave_last, lim[qb]);
+    lim[qb] = spare ? -1 : row_last(geo, hv, r);  // spare waves only stage tiles
     if (lim[qb] >= 0) {
+      wave_last = max(wave_last, lim[qb]);
+      wave_first = min(wave_first, lim[qb]);
       const Tin *qp = Q + q_row(geo, b, h_kv, kvh, hv, r) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = load8<Tin>(qp + ks * 32 + 8 * grp);
@@ -100,13 +117,21 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
     }
   }
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) wave_last = max(wave_last, __shfl_xor(wave_last, o, 64));
+  for (int o = 1; o < 64; o <<= 1) {
+    wave_last = max(wave_last, __shfl_xor(wave_last, o, 64));
+    wave_first = min(wave_first, __shfl_xor(wave_first, o, 64));
+  }
 
-  float m2[QBW], lsum[QBW];
+  // mref: reference max of the exponentials (log2 units), negm = -mref (0
+  // while no key has been visible); mtop: exact running max; lsum: this
+  // lane's share of the row sum against mref.
+  float mref[QBW], negm[QBW], mtop[QBW], lsum[QBW];
   f32x4 oacc[WITH_O ? DB : 1][QBW];
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
-    m2[qb] = -INFINITY;
+    mref[qb] = -INFINITY;
+    negm[qb] = 0.f;
+    mtop[qb] = -INFINITY;
     lsum[qb] = 0.f;
   }
   if (WITH_O) {
@@ -118,34 +143,34 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
 
   U128 pk[PFK];
   U128 pv[WITH_O ? PFV : 1][V16 ? 2 : 1];
+  // Tile loads go through a buffer resource over the tile's valid rows: rows
+  // past the end of the cache read as zeros (their logits are masked).
+  constexpr uint32_t RB = D * sizeof(Tin);  // row bytes
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (long)t_begin * D, range_bytes(t_begin, t_end, RB));
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc(Vb + (long)t_begin * D, WITH_O ? range_bytes(t_begin, t_end, RB) : 0u);
   auto prefetch = [&](int t0) {
+    const uint32_t toff = (uint32_t)(t0 - t_begin) * RB;
 #pragma unroll
     for (int u = 0; u < PFK; ++u) {
-      const int idx = threadIdx.x + u * blockDim.x;
+      const int idx = threadIdx.x + u * NT;
       const int row = idx / CPR, ch = idx % CPR;
-      pk[u] = U128{0, 0, 0, 0};
-      if (idx < KITEMS && t0 + row < n)
-        pk[u] = *reinterpret_cast<const U128 *>(K + kv_base + (long)(t0 + row) * D + ch * EPC);
+      if (KITEMS % NT == 0 || idx < KITEMS)
+        pk[u] = buf_load16(rk, toff + (uint32_t)(row * D + ch * EPC) * sizeof(Tin));
     }
     if (WITH_O) {
 #pragma unroll
       for (int u = 0; u < PFV; ++u) {
-        const int idx = threadIdx.x + u * blockDim.x;
+        const int idx = threadIdx.x + u * NT;
+        if (VITEMS % NT != 0 && idx >= VITEMS) continue;
         if constexpr (V16) {
           const int kp = idx % (TN / 2), ch = idx / (TN / 2);
-          const int r0 = t0 + 2 * kp;
-          pv[u][0] = U128{0, 0, 0, 0};
-          pv[u][V16 ? 1 : 0] = U128{0, 0, 0, 0};
-          if (idx < VITEMS && r0 < n)
-            pv[u][0] = *reinterpret_cast<const U128 *>(V + kv_base + (long)r0 * D + ch * EPC);
-          if (idx < VITEMS && r0 + 1 < n)
-            pv[u][V16 ? 1 : 0] =
-                *reinterpret_cast<const U128 *>(V + kv_base + (long)(r0 + 1) * D + ch * EPC);
+          const uint32_t off = toff + (uint32_t)(2 * kp * D + ch * EPC) * sizeof(Tin);
+          pv[u][0] = buf_load16(rv, off);
+          pv[u][V16 ? 1 : 0] = buf_load16(rv, off + D * sizeof(Tin));
         } else {
           const int r = idx % TN, ch = idx / TN;
-          pv[u][0] = U128{0, 0, 0, 0};
-          if (idx < VITEMS && t0 + r < n)
-            pv[u][0] = *reinterpret_cast<const U128 *>(V + kv_base + (long)(t0 + r) * D + ch * EPC);
+          pv[u][0] = buf_load16(rv, toff + (uint32_t)(r * D + ch * EPC) * sizeof(Tin));
         }
       }
     }
@@ -153,8 +178,8 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
   auto stash = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < PFK; ++u) {
-      const int idx = threadIdx.x + u * blockDim.x;
-      if (idx < KITEMS) {
+      const int idx = threadIdx.x + u * NT;
+      if (KITEMS % NT == 0 || idx < KITEMS) {
         const int row = idx / CPR, ch = idx % CPR;
         *reinterpret_cast<U128 *>(&Ks[buf][row * KROW + ch * EPC]) = pk[u];
       }
@@ -162,8 +187,8 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
     if (WITH_O) {
 #pragma unroll
       for (int u = 0; u < PFV; ++u) {
-        const int idx = threadIdx.x + u * blockDim.x;
-        if (idx >= VITEMS) continue;
+        const int idx = threadIdx.x + u * NT;
+        if (VITEMS % NT != 0 && idx >= VITEMS) continue;
         if constexpr (V16) {
           const int kp = idx % (TN / 2), ch = idx / (TN / 2);
           const Tin *ae = reinterpret_cast<const Tin *>(&pv[u][0]);
@@ -184,24 +209,20 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
     }
   };
 
-  if (nt > 0) {
-    prefetch(t_begin);
-    stash(0);
-  }
+  wait_vmem_all();
+  prefetch(t_begin);
+  stash(0);
   __syncthreads();
   for (int it = 0; it < nt; ++it) {
     const int t0 = t_begin + it * TN;
     const int cur = it & 1;
-    if (it + 1 < nt) prefetch(t0 + TN);
+    prefetch(t0 + TN);  // past the split end this reads nothing
+    if (t0 <= wave_last) {
+      // S^T for the tile: block tb holds tokens (tb/2)*32 + 8*(row/4) + 4*(tb%2) + row%4
+      f32x4 sacc[TB][QBW];
 #pragma unroll
-    for (int sub = 0; sub < TN / 32; ++sub) {
-      const int ts = t0 + sub * 32;
-      if (ts > wave_last) continue;  // this wave's rows see none of these tokens
-
-      f32x4 sacc[2][QBW];
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int trow = sub * 32 + 8 * (col >> 2) + 4 * tb + (col & 3);
+      for (int tb = 0; tb < TB; ++tb) {
+        const int trow = (tb >> 1) * 32 + 8 * (col >> 2) + 4 * (tb & 1) + (col & 3);
         FQ kf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kf[ks] = load8<Tin>(&Ks[cur][trow * KROW + ks * 32 + 8 * grp]);
@@ -213,77 +234,95 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
           sacc[tb][qb] = acc;
         }
       }
+      // Lane (col, grp) holds tokens t0 + (tb/2)*32 + 8*grp + 4*(tb%2) + j.
+      if (t0 + TN - 1 > wave_first) {
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+          for (int qb = 0; qb < QBW; ++qb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int tok = t0 + (tb >> 1) * 32 + 8 * grp + 4 * (tb & 1) + j;
+              if (tok > lim[qb]) sacc[tb][qb][j] = -INFINITY;
+            }
+      }
 
-      typename FragOf<TV>::type pf[QBW];
+      FV pf[TB / 2][QBW];
 #pragma unroll
       for (int qb = 0; qb < QBW; ++qb) {
-        float sv[8];
         float mx = -INFINITY;
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+        for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int tok = ts + 8 * grp + 4 * tb + j;
-            float x = sacc[tb][qb][j] * c;
-            x = (tok <= lim[qb]) ? x : -INFINITY;
-            sv[4 * tb + j] = x;
-            mx = fmaxf(mx, x);
-          }
+          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sacc[tb][qb][j]);
         mx = wave_max_xor(mx, 16);
         mx = wave_max_xor(mx, 32);
-        const float mnew = fmaxf(m2[qb], mx);
-        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = hw_exp2(m2[qb] - muse);
-        float p[8];
+        const float mxs = mx * c;
+        mtop[qb] = fmaxf(mtop[qb], mxs);
+        if (__any(mxs > mref[qb] + kSlack)) {
+          const float mnew = fmaxf(mref[qb], mxs);
+          const float alpha = (mnew == -INFINITY) ? 1.f : hw_exp2(mref[qb] - mnew);
+          mref[qb] = mnew;
+          negm[qb] = (mnew == -INFINITY) ? 0.f : -mnew;
+          lsum[qb] *= alpha;
+          if (WITH_O) {
+#pragma unroll
+            for (int db = 0; db < (WITH_O ? DB : 1); ++db) oacc[db][qb] *= alpha;
+          }
+        }
+        float p[TB * 4];
         float psum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = hw_exp2(sv[e] - muse);
-          psum += p[e];
-        }
-        lsum[qb] = lsum[qb] * alpha + psum;
-        m2[qb] = mnew;
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p[4 * tb + j] = hw_exp2(fmaf(sacc[tb][qb][j], c, negm[qb]));
+            psum += p[4 * tb + j];
+          }
+        lsum[qb] += psum;
         if (WITH_O) {
 #pragma unroll
-          for (int db = 0; db < (WITH_O ? DB : 1); ++db) oacc[db][qb] *= alpha;
-          pf[qb] = pack8<TV>(p);
+          for (int h = 0; h < TB / 2; ++h) pf[h][qb] = pack8<TV>(&p[8 * h]);
         }
       }
       if (WITH_O) {
 #pragma unroll
-        for (int db = 0; db < (WITH_O ? DB : 1); ++db) {
-          const FV vf = load8<TV>(&Vt[cur][(db * 16 + col) * VROW + sub * 32 + 8 * grp]);
+        for (int h = 0; h < TB / 2; ++h)
 #pragma unroll
-          for (int qb = 0; qb < QBW; ++qb) oacc[db][qb] = mma(vf, pf[qb], oacc[db][qb]);
-        }
+          for (int db = 0; db < (WITH_O ? DB : 1); ++db) {
+            const FV vf = load8<TV>(&Vt[cur][(db * 16 + col) * VROW + h * 32 + 8 * grp]);
+#pragma unroll
+            for (int qb = 0; qb < QBW; ++qb) oacc[db][qb] = mma(vf, pf[h][qb], oacc[db][qb]);
+          }
       }
     }
-    if (it + 1 < nt) stash(cur ^ 1);
+    stash(cur ^ 1);
     __syncthreads();
   }
 
+  if (spare) return;
   const long head = ((long)b * h_kv + kvh) * geo.group + hv;
   const long pbase = (head * splits + s) * 64;
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
-    float l = lsum[qb];
+    // bring (l, O) from the reference max to the exact max
+    const float fix = (mtop[qb] == -INFINITY) ? 1.f : hw_exp2(mref[qb] - mtop[qb]);
+    float l = lsum[qb] * fix;
     l = wave_sum_xor(l, 16);
     l = wave_sum_xor(l, 32);
     const int r = (qb0 + qb) * 16 + col;
     if (grp == 0) {
-      pm[pbase + r] = m2[qb];
+      pm[pbase + r] = mtop[qb];
       pl[pbase + r] = l;
     }
-  }
-  if (WITH_O) {
-    float *po = pO + (head * splits + s) * (long)D * 64;
+    if (WITH_O) {
+      float *po = pO + (head * splits + s) * (long)D * 64;
 #pragma unroll
-    for (int db = 0; db < (WITH_O ? DB : 1); ++db)
-#pragma unroll
-      for (int qb = 0; qb < QBW; ++qb)
+      for (int db = 0; db < (WITH_O ? DB : 1); ++db)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          po[(db * 16 + 4 * grp + j) * 64 + (qb0 + qb) * 16 + col] = oacc[db][qb][j];
+          po[(db * 16 + 4 * grp + j) * 64 + (qb0 + qb) * 16 + col] = oacc[db][qb][j] * fix;
+    }
   }
 }
 
@@ -352,51 +391,68 @@ attn_combine_rows_kernel(const float *__restrict__ pm, const float *__restrict__
 }
 
 SplitPlan attn_split_plan(int units, int n) {
-  const int target = 256;  // one workgroup per CU: splits share nothing, and fewer splits mean less partial-O traffic
+  const int target = 256;  // about one workgroup per CU; fewer splits mean less partial-O traffic
   int splits = (target + units - 1) / units;
   const int max_splits = (n + 511) / 512;
   if (splits > max_splits) splits = max_splits;
   if (splits > 128) splits = 128;
   if (splits < 1) splits = 1;
+  if (splits < (n + kMaxRangeTokens - 1) / kMaxRangeTokens)
+    splits = (n + kMaxRangeTokens - 1) / kMaxRangeTokens;
   int tps = (n + splits - 1) / splits;
   tps = (tps + 63) / 64 * 64;
   splits = (n + tps - 1) / tps;
   return SplitPlan{splits, tps};
 }
 
+// A workgroup holds at most 8 waves: a group needing more (G query heads x
+// 4/QBW waves each) is served by hsplit workgroups of hpw heads.  With O the
+// waves take 2 query blocks each (the O accumulators fill the registers),
+// without O 4.
+HeadSplit attn_head_split(int group, bool with_o) {
+  HeadSplit h;
+  h.qbw = with_o ? 2 : 4;
+  const int wph = 4 / h.qbw;
+  h.hsplit = (group * wph + 7) / 8;
+  h.hpw = (group + h.hsplit - 1) / h.hsplit;
+  h.maxw = 2;
+  while (h.maxw < h.hpw * wph) h.maxw *= 2;
+  return h;
+}
+
 template <typename Tin, int D, bool WITH_O, int MAXW, int QBW>
 static hipError_t run_partial(const void *Q, const void *K, const void *V, RowGeom geo, int batch,
-                              int h_kv, SplitPlan plan, float *pm, float *pl, float *pO,
-                              hipStream_t st) {
-  dim3 grid(plan.splits, h_kv, batch), block(64 * geo.group * (4 / QBW));
-  if ((int)block.x < 32 * MAXW || (int)block.x > 64 * MAXW) return hipErrorInvalidConfiguration;
+                              int h_kv, HeadSplit hs, SplitPlan plan, float *pm, float *pl,
+                              float *pO, hipStream_t st) {
+  // The block is always MAXW waves; waves beyond the heads' share stage
+  // tiles but compute nothing.
+  dim3 grid(plan.splits, h_kv * hs.hsplit, batch), block(64 * MAXW);
+  const int need = hs.hpw * (4 / QBW);
+  if (need < 1 || need > MAXW || hs.hsplit * hs.hpw < geo.group) return hipErrorInvalidConfiguration;
   {
     TimedLaunch tl_("attn_partial", st);
     hipLaunchKernelGGL((attn_partial_kernel<Tin, D, WITH_O, MAXW, QBW>), grid, block, 0, st,
-                       (const Tin *)Q, (const Tin *)K, (const Tin *)V, geo, h_kv, plan.tps,
-                       plan.splits, pm, pl, pO);
+                       (const Tin *)Q, (const Tin *)K, (const Tin *)V, geo, h_kv, hs.hsplit,
+                       hs.hpw, plan.tps, plan.splits, pm, pl, pO);
   }
   return hipGetLastError();
 }
 
-// Waves per workgroup = group * 4 / QBW <= 16; MAXW is the next power of two
-// (at least 2), so a block has between 32*MAXW and 64*MAXW threads.
 template <typename Tin, int D>
 static hipError_t run_partial_d(bool with_o, const void *Q, const void *K, const void *V,
                                 RowGeom geo, int batch, int h_kv, SplitPlan plan, float *pm,
                                 float *pl, float *pO, hipStream_t st) {
+  const HeadSplit hs = attn_head_split(geo.group, with_o);
 #define KVS_RP(O, MAXW, QBW) \
-  return run_partial<Tin, D, O, MAXW, QBW>(Q, K, V, geo, batch, h_kv, plan, pm, pl, pO, st)
+  return run_partial<Tin, D, O, MAXW, QBW>(Q, K, V, geo, batch, h_kv, hs, plan, pm, pl, pO, st)
   if (!with_o) {
-    if (geo.group <= 2) KVS_RP(false, 2, 4);
-    if (geo.group <= 4) KVS_RP(false, 4, 4);
-    if (geo.group <= 8) KVS_RP(false, 8, 4);
-    KVS_RP(false, 16, 4);
+    if (hs.maxw == 2) KVS_RP(false, 2, 4);
+    if (hs.maxw == 4) KVS_RP(false, 4, 4);
+    KVS_RP(false, 8, 4);
   }
-  if (geo.group <= 2) KVS_RP(true, 4, 2);
-  if (geo.group <= 4) KVS_RP(true, 8, 2);
-  if (geo.group <= 8) KVS_RP(true, 16, 2);
-  KVS_RP(true, 16, 4);
+  if (hs.maxw == 2) KVS_RP(true, 2, 2);
+  if (hs.maxw == 4) KVS_RP(true, 4, 2);
+  KVS_RP(true, 8, 2);
 #undef KVS_RP
 }
 

@@ -77,7 +77,8 @@ LorePlan plan_lore(const kvs_lore_desc *d) {
   const size_t heads = (size_t)d->batch * d->h_q;
   const size_t D = d->d;
   const size_t vbytes = d->dtype == KVS_F32 ? 4 : 2;  // value-side element type
-  p.split = kvs::attn_split_plan(d->batch * d->h_kv, d->n);
+  p.split = kvs::attn_split_plan(
+      d->batch * d->h_kv * kvs::attn_head_split(d->h_q / d->h_kv, true).hsplit, d->n);
   const size_t S = p.split.splits;
   p.off_pm = 0;
   p.off_pl = align_up(p.off_pm + heads * S * 64 * 4);
@@ -279,7 +280,8 @@ struct H2OPlan {
 H2OPlan plan_h2o(const kvs_h2o_desc *d) {
   H2OPlan p{};
   p.group = (d->cap + 63) / 64;
-  p.split = kvs::attn_split_plan(d->batch * d->heads, d->cap);
+  p.split = kvs::attn_split_plan(
+      d->batch * d->heads * kvs::attn_head_split(p.group, false).hsplit, d->cap);
   const size_t heads = (size_t)d->batch * d->heads * p.group;
   p.off_pm = 0;
   p.off_pl = align_up(heads * p.split.splits * 64 * 4);

@@ -176,6 +176,43 @@ __device__ __forceinline__ void store_converted16(const U128 &v, Tout *dst) {
   }
 }
 
+// ---- raw buffer loads ----------------------------------------------------------
+// A buffer resource covers [base, base + bytes); loads at byte offsets past
+// `bytes` return zeros (the hardware range check), so ragged tails need no
+// branches and the lane address is a 32-bit offset from a wave-uniform base.
+// Word 3 = 0x00020000 is the raw (untyped, unswizzled) format of the gfx9
+// family.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// The base and size must be wave-uniform; they are read from the first lane
+// so the resource lives in scalar registers (a per-lane resource would make
+// the compiler loop over lanes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void *p = (void *)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
+}
+__device__ __forceinline__ U128 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+  return U128{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0));
+}
+// A kernel's token range [t_begin, t_end) is covered by one resource built
+// once; tile t0 is addressed with the lane offset plus (t0 - t_begin) * row
+// bytes, and tiles past t_end read zeros without touching memory.  The range
+// times the row size must stay below 2^32 bytes (hosts cap the range).
+__device__ __forceinline__ uint32_t range_bytes(int t_begin, int t_end, uint32_t row_bytes) {
+  return (uint32_t)max(t_end - t_begin, 0) * row_bytes;
+}
+// s_waitcnt vmcnt(0): every vector memory load issued so far has landed.
+// Issued once after loop-invariant loads, it keeps the compiler from waiting
+// on them (and so on the tile loads in flight) inside the tile loop.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---- wave reductions ---------------------------------------------------------
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
@@ -203,6 +240,7 @@ __device__ __forceinline__ float row16_sum(float v) {
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float hw_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+__device__ __forceinline__ float hw_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

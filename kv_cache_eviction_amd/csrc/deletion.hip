@@ -19,6 +19,9 @@
 //   vnorm_kernel       N_i for every token and query head (MFMA)
 //   score_kernel<0>    recompute a, form e, aggregate rows and group heads -> S
 //   score_kernel<1>    H2O: column sums of the causal prompt probabilities
+#include <algorithm>
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "timing.hpp"
@@ -238,75 +241,99 @@ vnorm_kernel(const Tin *__restrict__ V, const typename ValueType<Tin>::type *__r
   const int t_end = min(n_pad, t_begin + tpw);
   const int nt = (t_end - t_begin + TN - 1) / TN;
 
-  U128 pv[PF];
-  auto prefetch = [&](int t0) {
+  // Loads run two tiles ahead: tile k's registers are set k % 2, issued while
+  // tile k - 2 is computed and stored to LDS after tile k - 1.
+  U128 pv[2][PF];
+  constexpr uint32_t RB = D * sizeof(Tin);
+  // V has n rows; tokens n..n_pad-1 read as zeros (N = 0 there)
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc(Vg + (long)t_begin * D, range_bytes(t_begin, min(t_end, n), RB));
+  auto prefetch = [&](U128 *regs, int t0) {
+    const uint32_t toff = (uint32_t)(t0 - t_begin) * RB;
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       const int idx = threadIdx.x + u * 256;
       const int row = idx / CPR, ch = idx % CPR;
-      pv[u] = U128{0, 0, 0, 0};
-      if (idx < TN * CPR && t0 + row < n)
-        pv[u] = *reinterpret_cast<const U128 *>(Vg + (long)(t0 + row) * D + ch * EPC);
+      if ((TN * CPR) % 256 == 0 || idx < TN * CPR)
+        regs[u] = buf_load16(rv, toff + (uint32_t)(row * D + ch * EPC) * sizeof(Tin));
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](const U128 *regs, int buf) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       const int idx = threadIdx.x + u * 256;
-      if (idx < TN * CPR) {
+      if ((TN * CPR) % 256 == 0 || idx < TN * CPR) {
         const int row = idx / CPR, ch = idx % CPR;
-        store_converted16<Tin, TV>(pv[u], &Vs[buf][row * VROW + ch * EPC]);
+        store_converted16<Tin, TV>(regs[u], &Vs[buf][row * VROW + ch * EPC]);
       }
     }
   };
-  if (nt > 0) {
-    prefetch(t_begin);
-    stash(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < nt; ++it) {
-    const int t0 = t_begin + it * TN;
-    const int cur = it & 1;
-    if (it + 1 < nt) prefetch(t0 + TN);
-    if (active) {
-      for (int tb = tp; tb < TN / 16; tb += tparts) {
-        const int tok = t0 + tb * 16 + col;
-        FV vf[KS];
+  auto compute = [&](int cur, int t0) {
+    if (!active) return;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          vf[ks] = load8<TV>(&Vs[cur][(tb * 16 + col) * VROW + ks * 32 + 8 * grp]);
-        float np = 0.f;
+    for (int tb = 0; tb < TN / 16; ++tb) {
+      if (tb % tparts != tp) continue;
+      const int tok = t0 + tb * 16 + col;
+      FV vf[KS];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < KS; ++ks)
+        vf[ks] = load8<TV>(&Vs[cur][(tb * 16 + col) * VROW + ks * 32 + 8 * grp]);
+      float np = 0.f;
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) acc = mma(gf[db][ks], vf[ks], acc);
+      for (int db = 0; db < DB; ++db) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) np += acc[j] * frag_elem(vf[db >> 1], 4 * (db & 1) + j);
-        }
-        np = wave_sum_xor(np, 16);
-        np = wave_sum_xor(np, 32);
-        if (grp == 0 && tok < t_end) Nh[tok] = np;
+        for (int ks = 0; ks < KS; ++ks) acc = mma(gf[db][ks], vf[ks], acc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) np += acc[j] * frag_elem(vf[db >> 1], 4 * (db & 1) + j);
       }
+      np = wave_sum_xor(np, 16);
+      np = wave_sum_xor(np, 32);
+      if (grp == 0 && tok < t_end) Nh[tok] = np;
     }
-    if (it + 1 < nt) stash(cur ^ 1);
-    __syncthreads();
+  };
+  // (loads of tiles past the range read nothing, so they are unconditional)
+  wait_vmem_all();
+  prefetch(pv[0], t_begin);
+  prefetch(pv[1], t_begin + TN);
+  stash(pv[0], 0);
+  __syncthreads();
+  for (int it = 0; it < nt; it += 2) {
+    // even tile: registers set 0, LDS buffer 0
+    {
+      const int t0 = t_begin + it * TN;
+      prefetch(pv[0], t0 + 2 * TN);
+      compute(0, t0);
+      stash(pv[1], 1);
+      __syncthreads();
+    }
+    if (it + 1 < nt) {
+      const int t0 = t_begin + (it + 1) * TN;
+      prefetch(pv[1], t0 + 2 * TN);
+      compute(1, t0);
+      stash(pv[0], 0);
+      __syncthreads();
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Score pass.  One workgroup per (token range, KV head, sequence); each query
-// head's 64 rows are spread over 4/QBW waves.  K (and V, converted to the
-// value type) tiles of 64 tokens are staged in LDS and shared by the group,
-// double-buffered: the next tile's global loads are issued into registers
-// before the current tile is computed and stored to the other buffer after,
-// so one barrier per tile separates the two.  Logits are formed transposed
-// (S^T = K Q^T): a lane owns one query column (row constants live in
-// registers) and four tokens per 16-token block, so the sum over the query
-// rows is in-lane plus one 16-lane DPP reduction per token; the per-wave
-// partial sums are combined across waves in a fixed order.
+// Score pass.  One workgroup per (token range, KV head, sequence) serves a
+// subset of the group's query heads (all of them when they fit in 8 waves;
+// otherwise the host launches the subsets one after another, the later ones
+// adding to S).  Each query head's 64 rows are spread over 4/QBW waves.  K
+// (and V, converted to the value type) tiles of 64 tokens are staged in LDS
+// and shared by the workgroup, double-buffered: the next tile's loads are in
+// flight while the current one is computed.  Logits are formed as S = Q K^T
+// with tokens across the 16 MFMA columns: a lane owns one token and four
+// query rows of each 16-row block, so the sum over query rows is in-lane
+// plus two cross-lane adds per 16 tokens; the per-wave partial sums are
+// combined across waves in a fixed order.
 //   MODE 0 (LORE): out = out_scale * sum_h sum_q wr_q * a/(1-a+eps) * sqrt(max(0, N - 2x + pi)),
-//                  x = v . (y_hi + y_lo) as two MFMA products
+//                  x = v . (y_hi + y_lo) as two MFMA products whose accumulator
+//                  starts at -pi/2, so N - 2*acc = N - 2x + pi;
+//                  sqrt(q2)/(1+eps-a) is formed as q2 * rsqrt(q2 (1+eps-a)^2)
+//                  with q2 clamped at 1e-30 instead of 0.
 //   MODE 1 (H2O):  out = sum over causal rows of a
 template <typename Tin, int D, int MODE, int MAXW, int QBW>
 __global__ void __launch_bounds__(64 * MAXW)
@@ -314,62 +341,86 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
              const typename ValueType<Tin>::type *__restrict__ Yhi,
              const typename ValueType<Tin>::type *__restrict__ Ylo,
              const float4 *__restrict__ consts, const float *__restrict__ Nn, int n_pad,
-             RowGeom geo, int h_kv, int tpw, float eps, float out_scale, float *__restrict__ S) {
+             RowGeom geo, int h_kv, int hv0, int hcount, int accumulate, int tpw, float eps,
+             float out_scale, float *__restrict__ S) {
   typedef typename ValueType<Tin>::type TV;
   typedef typename FragOf<Tin>::type FQ;
   typedef typename FragOf<TV>::type FV;
   constexpr bool SPLIT_Y = (MODE == 0) && sizeof(TV) == 2;
   constexpr int KS = D / 32;
   constexpr int TN = 64;
+  constexpr int NT = 64 * MAXW;
   constexpr int WPH = 4 / QBW;
   constexpr int EPC = 16 / (int)sizeof(Tin);
   constexpr int CPR = D / EPC;
   constexpr int KROW = D + EPC;
   constexpr int VROW = D + 16 / (int)sizeof(TV);
-  // 16-byte chunks per thread and tile: the smallest block of a MAXW variant
-  // has at least 32*MAXW threads (host checks)
-  constexpr int PF = (TN * CPR + 32 * MAXW - 1) / (32 * MAXW);
+  constexpr int ITEMS = TN * CPR;
+  constexpr int PF = (ITEMS + NT - 1) / NT;
+  constexpr float kTiny = 1e-30f;
   __shared__ __align__(16) Tin Ks[2][TN * KROW];
   __shared__ __align__(16) TV Vs[MODE == 0 ? 2 : 1][MODE == 0 ? TN * VROW : 8];
   __shared__ __align__(16) float red[2][MAXW * TN];
+  // N of the tile's tokens for each wave's own query head
+  __shared__ float Ns[MODE == 0 ? 2 : 1][MODE == 0 ? MAXW : 1][MODE == 0 ? TN : 1];
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int hv = wv / WPH, qb0 = (wv % WPH) * QBW;
-  const int nwaves = blockDim.x >> 6;
+  const int hl = wv / WPH, qb0 = (wv % WPH) * QBW;
+  const int hv = hv0 + hl;
+  const bool spare = hl >= hcount;
   const int col = lane & 15, grp = lane >> 4;
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int n = geo.n, G = geo.group;
   const long kv_base = ((long)b * h_kv + kvh) * (long)n * D;
-  const long head = ((long)b * h_kv + kvh) * G + hv;  // LORE: b*h_q + h
+  const Tin *Kb = K + kv_base;
+  const Tin *Vb = V + kv_base;
+  const long head = ((long)b * h_kv + kvh) * G + (spare ? 0 : hv);  // LORE: b*h_q + h
   const float c = kLog2e * rsqrtf((float)D);
 
+  // A fragments: lane (col, grp) supplies query row 16*qb + col.  Results:
+  // lane holds query rows 16*qb + 4*grp + j (j = 0..3) for token column col.
   FQ qf[QBW][KS];
   FV yhf[MODE == 0 ? QBW : 1][KS];
   FV ylf[SPLIT_Y ? QBW : 1][KS];
-  float beta[QBW], pi[QBW], wr[QBW];
-  int lim[QBW];
-  int wave_last = -1;
+  float beta[QBW][4], wr[QBW][4];
+  f32x4 xinit[QBW];
+  int lim[QBW][4];
+  int wave_last = -1, wave_first = 0x7FFFFFFF;
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = (qb0 + qb) * 16 + 4 * grp + j;
+      const float4 cs = spare ? make_float4(0.f, 0.f, 0.f, __int_as_float(-1)) : consts[head * 64 + r];
+      lim[qb][j] = __float_as_int(cs.w);
+      // rows without keys get a = 2^-inf = 0 on every path, masked or not
+      beta[qb][j] = lim[qb][j] >= 0 ? cs.x : INFINITY;
+      xinit[qb][j] = -0.5f * cs.y;
+      wr[qb][j] = cs.z;
+      if (lim[qb][j] >= 0) {
+        wave_last = max(wave_last, lim[qb][j]);
+        wave_first = min(wave_first, lim[qb][j]);
+      }
+    }
     const int r = (qb0 + qb) * 16 + col;
-    const float4 cs = consts[head * 64 + r];
-    beta[qb] = cs.x;
-    pi[qb] = cs.y;
-    wr[qb] = cs.z;
-    lim[qb] = __float_as_int(cs.w);
-    wave_last = max(wave_last, lim[qb]);
+    const bool valid = !spare && (geo.mode == 0 ? r < geo.nq : hv * 64 + r < n);
     long qrow;
     if (geo.mode == 0) qrow = head * geo.nq + r;
     else qrow = ((long)b * h_kv + kvh) * n + (long)hv * 64 + r;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qf[qb][ks] = lim[qb] >= 0 ? load8<Tin>(Q + qrow * D + ks * 32 + 8 * grp) : zero8<Tin>();
-      if (MODE == 0) yhf[qb][ks] = load8<TV>(Yhi + (head * 64 + r) * D + ks * 32 + 8 * grp);
-      if (SPLIT_Y) ylf[qb][ks] = load8<TV>(Ylo + (head * 64 + r) * D + ks * 32 + 8 * grp);
+      qf[qb][ks] = valid ? load8<Tin>(Q + qrow * D + ks * 32 + 8 * grp) : zero8<Tin>();
+      if (MODE == 0)
+        yhf[qb][ks] = spare ? zero8<TV>() : load8<TV>(Yhi + (head * 64 + r) * D + ks * 32 + 8 * grp);
+      if (SPLIT_Y)
+        ylf[qb][ks] = spare ? zero8<TV>() : load8<TV>(Ylo + (head * 64 + r) * D + ks * 32 + 8 * grp);
     }
   }
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) wave_last = max(wave_last, __shfl_xor(wave_last, o, 64));
+  for (int o = 1; o < 64; o <<= 1) {
+    wave_last = max(wave_last, __shfl_xor(wave_last, o, 64));
+    wave_first = min(wave_first, __shfl_xor(wave_first, o, 64));
+  }
 
   const int t_begin = blockIdx.x * tpw;
   const int t_end = min(n, t_begin + tpw);
@@ -378,98 +429,116 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
   const int nt = (t_end - t_begin + TN - 1) / TN;
 
   U128 pk[PF], pv[MODE == 0 ? PF : 1];
+  float pn = 0.f;  // N of token t0 + lane for this wave's head
+  constexpr uint32_t RB = D * sizeof(Tin);
+  const uint32_t rbytes = range_bytes(t_begin, t_end, RB);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (long)t_begin * D, rbytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (long)t_begin * D, MODE == 0 ? rbytes : 0u);
+  const __amdgpu_buffer_rsrc_t rn =
+      make_rsrc(Nh + t_begin, MODE == 0 ? range_bytes(t_begin, t_end, 4) : 0u);
   auto prefetch = [&](int t0) {
+    const uint32_t toff = (uint32_t)(t0 - t_begin) * RB;
+    if (MODE == 0) pn = buf_load_f32(rn, (uint32_t)(t0 - t_begin + lane) * 4u);
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
-      const int idx = threadIdx.x + u * blockDim.x;
+      const int idx = threadIdx.x + u * NT;
       const int row = idx / CPR, ch = idx % CPR;
-      const int tok = t0 + row;
-      pk[u] = U128{0, 0, 0, 0};
-      if (MODE == 0) pv[u] = U128{0, 0, 0, 0};
-      if (idx < TN * CPR && tok < n) {
-        pk[u] = *reinterpret_cast<const U128 *>(K + kv_base + (long)tok * D + ch * EPC);
-        if (MODE == 0) pv[u] = *reinterpret_cast<const U128 *>(V + kv_base + (long)tok * D + ch * EPC);
+      const uint32_t off = toff + (uint32_t)(row * D + ch * EPC) * sizeof(Tin);
+      if (ITEMS % NT == 0 || idx < ITEMS) {
+        pk[u] = buf_load16(rk, off);
+        if (MODE == 0) pv[u] = buf_load16(rv, off);
       }
     }
   };
   auto stash = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
-      const int idx = threadIdx.x + u * blockDim.x;
-      if (idx < TN * CPR) {
+      const int idx = threadIdx.x + u * NT;
+      if (ITEMS % NT == 0 || idx < ITEMS) {
         const int row = idx / CPR, ch = idx % CPR;
         *reinterpret_cast<U128 *>(&Ks[buf][row * KROW + ch * EPC]) = pk[u];
         if (MODE == 0) store_converted16<Tin, TV>(pv[u], &Vs[buf][row * VROW + ch * EPC]);
       }
     }
+    if (MODE == 0) Ns[buf][wv][lane] = pn;
   };
 
-  if (nt > 0) {
-    prefetch(t_begin);
-    stash(0);
-  }
+  // One 16-token block: the sum over this wave's rows for token tok0 + col.
+  auto block_sum = [&](auto masked, int cur, int tb, int tok0) -> float {
+    constexpr bool MASKED = decltype(masked)::value;
+    FQ kf[KS];
+    FV vf[MODE == 0 ? KS : 1];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = load8<Tin>(&Ks[cur][(tb * 16 + col) * KROW + ks * 32 + 8 * grp]);
+      if (MODE == 0) vf[ks] = load8<TV>(&Vs[cur][(tb * 16 + col) * VROW + ks * 32 + 8 * grp]);
+    }
+    const int tok = tok0 + col;
+    const float nv = (MODE == 0) ? Ns[cur][wv][tb * 16 + col] : 0.f;
+    float tacc = 0.f;
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+      f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sa = mma(qf[qb][ks], kf[ks], sa);
+      f32x4 xa = xinit[qb];
+      if (MODE == 0) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) xa = mma(yhf[qb][ks], vf[ks], xa);
+      }
+      if (SPLIT_Y) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) xa = mma(ylf[qb][ks], vf[ks], xa);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float e = fmaf(sa[j], c, -beta[qb][j]);
+        if (MASKED && tok > lim[qb][j]) e = -INFINITY;
+        const float a = hw_exp2(e);
+        if (MODE == 1) {
+          tacc += a;
+        } else {
+          const float den = (1.f + eps) - a;
+          const float q2 = fmaxf(fmaf(-2.f, xa[j], nv), kTiny);
+          const float u = q2 * hw_rsq(q2 * den * den);
+          tacc = fmaf(a * wr[qb][j], u, tacc);
+        }
+      }
+    }
+    tacc += __shfl_xor(tacc, 16, 64);
+    tacc += __shfl_xor(tacc, 32, 64);
+    return tacc;
+  };
+
+  wait_vmem_all();
+  prefetch(t_begin);
+  stash(0);
   __syncthreads();
   for (int it = 0; it < nt; ++it) {
     const int t0 = t_begin + it * TN;
     const int cur = it & 1;
-    if (it + 1 < nt) prefetch(t0 + TN);
+    prefetch(t0 + TN);  // past the range this reads nothing
 #pragma unroll
     for (int tb = 0; tb < TN / 16; ++tb) {
       const int tok0 = t0 + tb * 16;
-      float tacc[4] = {0.f, 0.f, 0.f, 0.f};
+      float tsum = 0.f;
       if (tok0 <= wave_last) {
-        FQ kf[KS];
-        FV vf[MODE == 0 ? KS : 1];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          kf[ks] = load8<Tin>(&Ks[cur][(tb * 16 + col) * KROW + ks * 32 + 8 * grp]);
-          if (MODE == 0) vf[ks] = load8<TV>(&Vs[cur][(tb * 16 + col) * VROW + ks * 32 + 8 * grp]);
-        }
-        float4 nv = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (MODE == 0) nv = *reinterpret_cast<const float4 *>(Nh + tok0 + 4 * grp);
-        const float nva[4] = {nv.x, nv.y, nv.z, nv.w};
-#pragma unroll
-        for (int qb = 0; qb < QBW; ++qb) {
-          f32x4 sa = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) sa = mma(kf[ks], qf[qb][ks], sa);
-          f32x4 xa = {0.f, 0.f, 0.f, 0.f};
-          if (MODE == 0) {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) xa = mma(vf[ks], yhf[qb][ks], xa);
-          }
-          if (SPLIT_Y) {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) xa = mma(vf[ks], ylf[qb][ks], xa);
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int tok = tok0 + 4 * grp + j;
-            const float a = (tok <= lim[qb]) ? hw_exp2(sa[j] * c - beta[qb]) : 0.f;
-            if (MODE == 1) {
-              tacc[j] += a;
-            } else {
-              const float cc = a * hw_rcp(1.f + eps - a);
-              const float q2 = fmaxf(nva[j] - 2.f * xa[j] + pi[qb], 0.f);
-              tacc[j] += wr[qb] * (cc * hw_sqrt(q2));
-            }
-          }
-        }
+        if (tok0 + 15 > wave_first)
+          tsum = block_sum(std::true_type{}, cur, tb, tok0);
+        else
+          tsum = block_sum(std::false_type{}, cur, tb, tok0);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) tacc[j] = row16_sum(tacc[j]);
-      if (col == 0)
-        *reinterpret_cast<float4 *>(&red[cur][wv * TN + tb * 16 + 4 * grp]) =
-            make_float4(tacc[0], tacc[1], tacc[2], tacc[3]);
+      if (grp == 0) red[cur][wv * TN + tb * 16 + col] = tsum;
     }
-    if (it + 1 < nt) stash(cur ^ 1);
+    stash(cur ^ 1);
     __syncthreads();
-    for (int t = threadIdx.x; t < TN; t += blockDim.x) {
-      const int tok = t0 + t;
+    if (threadIdx.x < TN) {
+      const int tok = t0 + threadIdx.x;
       if (tok < t_end) {
         float sum = 0.f;
-        for (int w = 0; w < nwaves; ++w) sum += red[cur][w * TN + t];
-        Sout[tok] = sum * out_scale;
+        for (int w = 0; w < MAXW; ++w) sum += red[cur][w * TN + threadIdx.x];
+        sum *= out_scale;
+        Sout[tok] = accumulate ? Sout[tok] + sum : sum;
       }
     }
   }
@@ -545,7 +614,7 @@ static hipError_t run_vnorm(const void *V, const void *Gv, int batch, int n, int
   const long units = (long)((G + hpw - 1) / hpw) * h_kv * batch;
   const int tiles = n_pad / 64;
   const long want = std::max(1L, 512L / units);
-  const int tpw = 64 * (int)((tiles + want - 1) / want);
+  const int tpw = std::min(64 * (int)((tiles + want - 1) / want), kMaxRangeTokens);
   const int nchunk = (n_pad + tpw - 1) / tpw;
   const long blocks = (long)nchunk * units;
   {
@@ -569,47 +638,56 @@ hipError_t launch_vnorm(int etype, int d, const void *V, const void *Gv, int bat
 template <typename Tin, int D, int MODE, int MAXW, int QBW>
 static hipError_t run_score_w(const void *Q, const void *K, const void *V, const void *Yhi,
                               const void *Ylo, const float4 *consts, const float *Nn, int n_pad,
-                              RowGeom geo, int batch, int h_kv, float eps, float out_scale,
-                              float *S, hipStream_t st) {
+                              RowGeom geo, int batch, int h_kv, int hpw, float eps,
+                              float out_scale, float *S, hipStream_t st) {
   typedef typename ValueType<Tin>::type TV;
+  if (hpw < 1 || hpw * (4 / QBW) > MAXW) return hipErrorInvalidConfiguration;
   const long units = (long)batch * h_kv;
   long tpw = ((long)geo.n * units + 1023) / 1024;  // aim for ~1024 workgroups
   tpw = (tpw + 63) / 64 * 64;
   if (tpw < 64) tpw = 64;
+  if (tpw > kMaxRangeTokens) tpw = kMaxRangeTokens;
   const int blocks = (int)((geo.n + tpw - 1) / tpw);
-  const int threads = 64 * geo.group * (4 / QBW);
-  if (threads < 32 * MAXW || threads > 64 * MAXW) return hipErrorInvalidConfiguration;
-  {
-    TimedLaunch tl_((MODE == 0 ? "score_lore" : "score_h2o_colsum"), st);
-    hipLaunchKernelGGL((score_kernel<Tin, D, MODE, MAXW, QBW>), dim3(blocks, h_kv, batch),
-                       dim3(64 * geo.group * (4 / QBW)), 0, st, (const Tin *)Q, (const Tin *)K,
-                       (const Tin *)V, (const TV *)Yhi, (const TV *)Ylo, consts, Nn, n_pad, geo,
-                       h_kv, (int)tpw, eps, out_scale, S);
+  // head subsets in stream order; the later ones add to S
+  for (int hv0 = 0; hv0 < geo.group; hv0 += hpw) {
+    const int hcount = std::min(hpw, geo.group - hv0);
+    {
+      TimedLaunch tl_((MODE == 0 ? "score_lore" : "score_h2o_colsum"), st);
+      hipLaunchKernelGGL((score_kernel<Tin, D, MODE, MAXW, QBW>), dim3(blocks, h_kv, batch),
+                         dim3(64 * MAXW), 0, st, (const Tin *)Q, (const Tin *)K, (const Tin *)V,
+                         (const TV *)Yhi, (const TV *)Ylo, consts, Nn, n_pad, geo, h_kv, hv0,
+                         hcount, hv0 > 0 ? 1 : 0, (int)tpw, eps, out_scale, S);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
-// Waves per workgroup = group * 4 / QBW <= 16; MAXW is the next power of two
-// (at least 2), so a block always has between 32*MAXW and 64*MAXW threads.
+// At most 8 waves per workgroup: a query head takes 4/QBW waves (QBW = 2 for
+// LORE, whose row constants and y fragments fill the registers; 4 for H2O),
+// and larger groups run as several launches over head subsets of balanced size.
 template <typename Tin, int D>
 static hipError_t run_score(int mode, const void *Q, const void *K, const void *V, const void *Yhi,
                             const void *Ylo, const float4 *consts, const float *Nn, int n_pad,
                             RowGeom geo, int batch, int h_kv, float eps, float out_scale, float *S,
                             hipStream_t st) {
+  const int wph = mode == 1 ? 1 : 2;
+  const int hmax = 8 / wph;
+  const int nl = (geo.group + hmax - 1) / hmax;
+  const int hpw = (geo.group + nl - 1) / nl;
+  const int waves = hpw * wph;
 #define KVS_RS(MODE, MAXW, QBW)                                                                \
   return run_score_w<Tin, D, MODE, MAXW, QBW>(Q, K, V, Yhi, Ylo, consts, Nn, n_pad, geo, batch, \
-                                              h_kv, eps, out_scale, S, st)
+                                              h_kv, hpw, eps, out_scale, S, st)
   if (mode == 1) {
-    const int waves = geo.group;  // QBW = 4: one wave per 64 prompt rows
     if (waves <= 2) KVS_RS(1, 2, 4);
     if (waves <= 4) KVS_RS(1, 4, 4);
-    if (waves <= 8) KVS_RS(1, 8, 4);
-    KVS_RS(1, 16, 4);
+    KVS_RS(1, 8, 4);
   }
-  if (geo.group <= 2) KVS_RS(0, 4, 2);
-  if (geo.group <= 4) KVS_RS(0, 8, 2);
-  if (geo.group <= 8) KVS_RS(0, 16, 2);
-  KVS_RS(0, 16, 4);
+  if (waves <= 2) KVS_RS(0, 2, 2);
+  if (waves <= 4) KVS_RS(0, 4, 2);
+  KVS_RS(0, 8, 2);
 #undef KVS_RS
 }
 

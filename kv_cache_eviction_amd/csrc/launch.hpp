@@ -26,7 +26,13 @@ struct SplitPlan {
   int splits;
   int tps;  // tokens per split, a multiple of 32
 };
+// Token ranges handled by one workgroup stay below this many tokens, so a
+// range's rows (at most 512 bytes each) fit a 32-bit buffer offset.
+constexpr int kMaxRangeTokens = 1 << 22;
+
 SplitPlan attn_split_plan(int units, int n);
+struct HeadSplit { int hsplit, hpw, maxw, qbw; };
+HeadSplit attn_head_split(int group, bool with_o);
 
 // Pass 1 partials -> combined statistics.
 // part_m/part_l: [heads][splits][64]; part_O: [heads][splits][d][64].
