@@ -218,14 +218,28 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
     const int cur = it & 1;
     prefetch(t0 + TN);  // past the split end this reads nothing
     if (t0 <= wave_last) {
-      // S^T for the tile: block tb holds tokens (tb/2)*32 + 8*(row/4) + 4*(tb%2) + row%4
-      f32x4 sacc[TB][QBW];
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb) {
+      // S^T for the tile: block tb holds tokens (tb/2)*32 + 8*(row/4) + 4*(tb%2) + row%4.
+      // LDS fragments are read one step ahead of the products that use them.
+      auto load_k = [&](int tb, FQ (&kf)[KS]) {
         const int trow = (tb >> 1) * 32 + 8 * (col >> 2) + 4 * (tb & 1) + (col & 3);
-        FQ kf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kf[ks] = load8<Tin>(&Ks[cur][trow * KROW + ks * 32 + 8 * grp]);
+      };
+      // P.V steps: (half h of the tile, 16-row block db of d), step = h * DB + db
+      constexpr int PVS = WITH_O ? (TB / 2) * DB : 1;
+      constexpr int VW = 4;  // V fragments in flight
+      auto load_v = [&](int step) -> FV {
+        const int h = step / DB, db = step % DB;
+        return load8<TV>(&Vt[cur][(db * 16 + col) * VROW + h * 32 + 8 * grp]);
+      };
+      f32x4 sacc[TB][QBW];
+      FQ kb[2][KS];
+      load_k(0, kb[0]);
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        if (tb + 1 < TB) load_k(tb + 1, kb[(tb + 1) & 1]);
+        sched_fence();
+        const FQ (&kf)[KS] = kb[tb & 1];
 #pragma unroll
         for (int qb = 0; qb < QBW; ++qb) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -247,6 +261,13 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
             }
       }
 
+      // the first V fragments land while the softmax runs
+      FV vq[VW];
+      if (WITH_O) {
+#pragma unroll
+        for (int k = 0; k < VW; ++k) vq[k] = load_v(k);
+      }
+      sched_fence();
       FV pf[TB / 2][QBW];
 #pragma unroll
       for (int qb = 0; qb < QBW; ++qb) {
@@ -287,13 +308,14 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
       }
       if (WITH_O) {
 #pragma unroll
-        for (int h = 0; h < TB / 2; ++h)
+        for (int step = 0; step < PVS; ++step) {
+          const int h = step / DB, db = step % DB;
+          const FV vf = vq[step % VW];
+          if (step + VW < PVS) vq[step % VW] = load_v(step + VW);
 #pragma unroll
-          for (int db = 0; db < (WITH_O ? DB : 1); ++db) {
-            const FV vf = load8<TV>(&Vt[cur][(db * 16 + col) * VROW + h * 32 + 8 * grp]);
-#pragma unroll
-            for (int qb = 0; qb < QBW; ++qb) oacc[db][qb] = mma(vf, pf[h][qb], oacc[db][qb]);
-          }
+          for (int qb = 0; qb < QBW; ++qb)
+            oacc[db % (WITH_O ? DB : 1)][qb] = mma(vf, pf[h][qb], oacc[db % (WITH_O ? DB : 1)][qb]);
+        }
       }
     }
     stash(cur ^ 1);

@@ -120,44 +120,6 @@ template <typename T> __device__ __forceinline__ uint32_t bits16(T x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x);
 }
 
-// Stage rows [0, nrows) (nrows <= 32) x D of a row-major matrix with row
-// stride ld into LDS transposed: T[c][r] at T[c * TROW + r], converted to Tout.
-// 16-bit outputs: each thread takes a row pair and one 16-byte chunk and
-// writes packed dwords, so consecutive lanes store consecutive dwords of one
-// LDS row.  Rows past nrows are zero.
-template <typename Tin, typename Tout, int D, int TROW>
-__device__ __forceinline__ void stage_transposed32(const Tin *__restrict__ src, long ld, int nrows,
-                                                   Tout *__restrict__ T) {
-  constexpr int EPC = 16 / (int)sizeof(Tin);
-  constexpr int CPR = D / EPC;
-  if constexpr (sizeof(Tout) == 2) {
-    for (int idx = threadIdx.x; idx < 16 * CPR; idx += blockDim.x) {
-      const int kp = idx % 16, ch = idx / 16;
-      const int r0 = 2 * kp;
-      U128 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-      if (r0 < nrows) a = *reinterpret_cast<const U128 *>(src + (long)r0 * ld + ch * EPC);
-      if (r0 + 1 < nrows) b = *reinterpret_cast<const U128 *>(src + (long)(r0 + 1) * ld + ch * EPC);
-      const Tin *ae = reinterpret_cast<const Tin *>(&a);
-      const Tin *be = reinterpret_cast<const Tin *>(&b);
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        const uint32_t packed = bits16(from_f32<Tout>(to_f32(ae[e]))) |
-                                (bits16(from_f32<Tout>(to_f32(be[e]))) << 16);
-        *reinterpret_cast<uint32_t *>(&T[(ch * EPC + e) * TROW + r0]) = packed;
-      }
-    }
-  } else {
-    for (int idx = threadIdx.x; idx < 32 * CPR; idx += blockDim.x) {
-      const int r = idx % 32, ch = idx / 32;
-      U128 a = {0, 0, 0, 0};
-      if (r < nrows) a = *reinterpret_cast<const U128 *>(src + (long)r * ld + ch * EPC);
-      const Tin *ae = reinterpret_cast<const Tin *>(&a);
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) T[(ch * EPC + e) * TROW + r] = from_f32<Tout>(to_f32(ae[e]));
-    }
-  }
-}
-
 // 16 bytes of Tin converted to Tout and stored as one packed LDS write
 // (8 x bf16 -> 8 x f16, or a plain copy when the types match).
 template <typename Tin, typename Tout>
@@ -212,6 +174,9 @@ __device__ __forceinline__ uint32_t range_bytes(int t_begin, int t_end, uint32_t
 // Issued once after loop-invariant loads, it keeps the compiler from waiting
 // on them (and so on the tile loads in flight) inside the tile loop.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Keep the instruction scheduler from moving code across this point (used to
+// pin early LDS fragment reads ahead of the work that hides their latency).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // ---- wave reductions ---------------------------------------------------------
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {

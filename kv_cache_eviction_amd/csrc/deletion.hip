@@ -29,9 +29,10 @@
 namespace kvs {
 
 // ---------------------------------------------------------------------------
-// G_h = W_h^T W_h, one d_model slab per block.  W_h is the column slice
-// h*D .. h*D+D-1 of W_O [d_model][h_q*D].  A 32-row slab is staged transposed
-// in LDS so both MFMA operands are 16-byte reads.
+// G_h = W_h^T W_h, one range of d_model rows per block.  W_h is the column
+// slice h*D .. h*D+D-1 of W_O [d_model][h_q*D].  32-row slabs are staged
+// transposed in LDS so both MFMA operands are 16-byte reads; the next slab's
+// loads are in flight while the current one is multiplied.
 template <typename Tin, int D>
 __global__ void __launch_bounds__(256)
 gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
@@ -42,13 +43,60 @@ gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
   constexpr int WROW = 32 + EPC;
   constexpr int DB = D / 16;
   constexpr int RPW = (DB + 3) / 4;  // row blocks per wave
-  __shared__ __align__(16) Tin Wt[D * WROW];
+  constexpr bool P16 = sizeof(Tin) == 2;
+  // staging items: 16-bit -> (row pair, chunk), fp32 -> (row, chunk)
+  constexpr int ITEMS = P16 ? 16 * CPR : 32 * CPR;
+  constexpr int PFG = (ITEMS + 255) / 256;
+  __shared__ __align__(16) Tin Wt[2][D * WROW];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int s = blockIdx.x, h = blockIdx.y;
   const long ld = (long)h_q * D;
   const int k_begin = s * rows_per_split;
   const int k_end = min(dm, k_begin + rows_per_split);
+  const int nslab = (k_end - k_begin + 31) / 32;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(
+      W + (long)k_begin * ld + (long)h * D,
+      (uint32_t)max(k_end - k_begin, 0) * (uint32_t)(ld * sizeof(Tin)));
+
+  U128 pw[PFG][P16 ? 2 : 1];
+  auto prefetch = [&](int slab) {
+#pragma unroll
+    for (int u = 0; u < PFG; ++u) {
+      const int idx = threadIdx.x + u * 256;
+      if (ITEMS % 256 != 0 && idx >= ITEMS) continue;
+      if constexpr (P16) {
+        const int kp = idx % 16, ch = idx / 16;
+        const uint32_t r0 = (uint32_t)(slab * 32 + 2 * kp);
+        pw[u][0] = buf_load16(rw, (uint32_t)((r0 * ld + ch * EPC) * sizeof(Tin)));
+        pw[u][P16 ? 1 : 0] = buf_load16(rw, (uint32_t)(((r0 + 1) * ld + ch * EPC) * sizeof(Tin)));
+      } else {
+        const int r = idx % 32, ch = idx / 32;
+        pw[u][0] = buf_load16(rw, (uint32_t)(((uint32_t)(slab * 32 + r) * ld + ch * EPC) * sizeof(Tin)));
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PFG; ++u) {
+      const int idx = threadIdx.x + u * 256;
+      if (ITEMS % 256 != 0 && idx >= ITEMS) continue;
+      if constexpr (P16) {
+        const int kp = idx % 16, ch = idx / 16;
+        const Tin *ae = reinterpret_cast<const Tin *>(&pw[u][0]);
+        const Tin *be = reinterpret_cast<const Tin *>(&pw[u][P16 ? 1 : 0]);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+          *reinterpret_cast<uint32_t *>(&Wt[buf][(ch * EPC + e) * WROW + 2 * kp]) =
+              bits16(ae[e]) | (bits16(be[e]) << 16);
+      } else {
+        const int r = idx % 32, ch = idx / 32;
+        const Tin *ae = reinterpret_cast<const Tin *>(&pw[u][0]);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) Wt[buf][(ch * EPC + e) * WROW + r] = ae[e];
+      }
+    }
+  };
 
   f32x4 acc[RPW][DB];
 #pragma unroll
@@ -56,33 +104,41 @@ gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
 #pragma unroll
     for (int cb = 0; cb < DB; ++cb) acc[ri][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = k_begin; k0 < k_end; k0 += 32) {
-    __syncthreads();
-    stage_transposed32<Tin, Tin, D, WROW>(W + (long)k0 * ld + (long)h * D, ld,
-                                          min(32, k_end - k0), Wt);
-    __syncthreads();
+  prefetch(0);
+  stash(0);
+  __syncthreads();
+  for (int sl = 0; sl < nslab; ++sl) {
+    const int cur = sl & 1;
+    prefetch(sl + 1);  // past the range this reads zeros
     FW af[RPW];
 #pragma unroll
     for (int ri = 0; ri < RPW; ++ri) {
       const int rb = wv + 4 * ri;
-      af[ri] = rb < DB ? load8<Tin>(&Wt[(rb * 16 + col) * WROW + 8 * grp]) : zero8<Tin>();
+      af[ri] = rb < DB ? load8<Tin>(&Wt[cur][(rb * 16 + col) * WROW + 8 * grp]) : zero8<Tin>();
     }
 #pragma unroll
     for (int cb = 0; cb < DB; ++cb) {
-      const FW bfr = load8<Tin>(&Wt[(cb * 16 + col) * WROW + 8 * grp]);
+      const FW bfr = load8<Tin>(&Wt[cur][(cb * 16 + col) * WROW + 8 * grp]);
 #pragma unroll
-      for (int ri = 0; ri < RPW; ++ri) acc[ri][cb] = mma(af[ri], bfr, acc[ri][cb]);
+      for (int ri = 0; ri < RPW; ++ri)
+        if (cb >= wv + 4 * ri) acc[ri][cb] = mma(af[ri], bfr, acc[ri][cb]);
     }
+    stash(cur ^ 1);
+    __syncthreads();
   }
+  // G is symmetric: only the 16x16 blocks on and above the diagonal are
+  // formed and written (the reduction mirrors them).
   float *G = Gpart + ((long)s * h_q + h) * D * D;
 #pragma unroll
   for (int ri = 0; ri < RPW; ++ri) {
     const int rb = wv + 4 * ri;
     if (rb >= DB) continue;
 #pragma unroll
-    for (int cb = 0; cb < DB; ++cb)
+    for (int cb = 0; cb < DB; ++cb) {
+      if (cb < rb) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) G[(rb * 16 + 4 * grp + j) * D + cb * 16 + col] = acc[ri][cb][j];
+    }
   }
 }
 
@@ -96,7 +152,8 @@ int gram_splits(int h_q, int d_model) {
 
 // ---------------------------------------------------------------------------
 // Sum the G_h partials (fixed order) and round G_h to the value type once:
-// Gv = G~ (value type, for the MFMA in vnorm_kernel) and Gr = float(G~).  Every
+// Gv = G~ (value type, for the MFMA in vnorm_kernel) and Gr = float(G~),
+// exactly symmetric (mirrored from the upper triangle).  Every
 // term of the norm expansion is then formed from that same G~: y_q = G~ o_q
 // and pi_q = o_q . y_q in prep_kernel, N_i = v_i^T G~ v_i in vnorm_kernel.  So
 // N - 2x + pi equals (v - o)^T G~ (v - o) up to fp32 accumulation: no term
@@ -104,17 +161,32 @@ int gram_splits(int h_q, int d_model) {
 // to the attention output (where the three terms nearly cancel) keep their
 // relative accuracy.
 template <int D, typename TV>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(D)
 gram_reduce_kernel(const float *__restrict__ Gpart, int gsplits, int h_q, TV *__restrict__ Gv,
                    float *__restrict__ Gr) {
-  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  // block (row i, head h); thread j >= i sums entry (i, j) over the splits in
+  // a fixed order and writes it to (i, j) and (j, i): G~ is exactly symmetric
+  const int i = blockIdx.x, h = blockIdx.y, j = threadIdx.x;
+  if (j < i) return;
   const long total = (long)h_q * D * D;
-  if (idx >= total) return;
+  const long idx = ((long)h * D + i) * D + j;
   float g = 0.f;
-  for (int s = 0; s < gsplits; ++s) g += Gpart[(long)s * total + idx];
+  int s = 0;
+  for (; s + 4 <= gsplits; s += 4) {
+    const float a0 = Gpart[(long)s * total + idx], a1 = Gpart[(long)(s + 1) * total + idx];
+    const float a2 = Gpart[(long)(s + 2) * total + idx], a3 = Gpart[(long)(s + 3) * total + idx];
+    g += a0;
+    g += a1;
+    g += a2;
+    g += a3;
+  }
+  for (; s < gsplits; ++s) g += Gpart[(long)s * total + idx];
   const TV gr = from_f32<TV>(g);
+  const long tdx = ((long)h * D + j) * D + i;
   Gv[idx] = gr;
   Gr[idx] = to_f32(gr);
+  Gv[tdx] = gr;
+  Gr[tdx] = to_f32(gr);
 }
 
 // Per (query head, sequence, 16-row group): y_q = G~ o_q (stored as a hi + lo
@@ -194,8 +266,10 @@ prep_kernel(const float *__restrict__ Gr, const float *__restrict__ O,
 // row 4*(lane/16)+j of block db on the head-dim index whose V value the lane
 // already holds in its own B fragment (k-step db/2, element 4*(db%2)+j): the
 // quadratic form then needs no data exchange until the final two cross-lane
-// adds.
-template <typename Tin, int D>
+// adds.  G~ is symmetric, so only its block upper triangle is used (32x32
+// blocks: the diagonal blocks whole, the blocks above them doubled, exact in
+// the value type): 20 of the 32 products per 16 tokens.
+template <typename Tin, int D, int TPARTS>
 __global__ void __launch_bounds__(256)
 vnorm_kernel(const Tin *__restrict__ V, const typename ValueType<Tin>::type *__restrict__ Gv,
              int n, int n_pad, int h_q, int h_kv, int tpw, int nchunk, float *__restrict__ Nn) {
@@ -214,7 +288,7 @@ vnorm_kernel(const Tin *__restrict__ V, const typename ValueType<Tin>::type *__r
   const int G = h_q / h_kv;
   const int hpw = G < 4 ? G : 4;          // heads per workgroup
   const int ngrp = (G + hpw - 1) / hpw;   // workgroups per KV head and token range
-  const int tparts = 4 / hpw;             // waves sharing one head's tile
+  static_assert(TPARTS == 1 || TPARTS == 2 || TPARTS == 4, "waves per head's tile");
   // logical (sequence, KV head, head group, token chunk) of this block
   const long L = blockIdx.x;
   const int chunk_i = (int)(L % nchunk);
@@ -222,18 +296,28 @@ vnorm_kernel(const Tin *__restrict__ V, const typename ValueType<Tin>::type *__r
   const int hgi = (int)(rest % ngrp);
   const int kvh = (int)((rest / ngrp) % h_kv);
   const int b = (int)(rest / ((long)ngrp * h_kv));
-  const int tp = wv / hpw;
+  const int tp = wv / hpw;  // (launch: TPARTS == 4 / hpw)
   const int hg = hgi * hpw + wv % hpw;
-  const bool active = tp < tparts && hg < G;
+  const bool active = tp < TPARTS && hg < G;
   const int h = kvh * G + (active ? hg : 0);
 
+  // block (db, ks) is used when ks >= db/2 and doubled when ks > db/2
   FV gf[DB][KS];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     const int row = 32 * (db >> 1) + 8 * (col >> 2) + 4 * (db & 1) + (col & 3);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      gf[db][ks] = active ? load8<TV>(Gv + ((long)h * D + row) * D + ks * 32 + 8 * grp) : zero8<TV>();
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks < (db >> 1)) continue;
+      FV f = active ? load8<TV>(Gv + ((long)h * D + row) * D + ks * 32 + 8 * grp) : zero8<TV>();
+      if (ks > (db >> 1)) {
+        float t[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = 2.f * frag_elem(f, e);
+        f = pack8<TV>(t);
+      }
+      gf[db][ks] = f;
+    }
   }
   const Tin *Vg = V + ((long)b * h_kv + kvh) * (long)n * D;
   float *Nh = Nn + ((long)b * h_q + h) * n_pad;
@@ -241,24 +325,25 @@ vnorm_kernel(const Tin *__restrict__ V, const typename ValueType<Tin>::type *__r
   const int t_end = min(n_pad, t_begin + tpw);
   const int nt = (t_end - t_begin + TN - 1) / TN;
 
-  // Loads run two tiles ahead: tile k's registers are set k % 2, issued while
-  // tile k - 2 is computed and stored to LDS after tile k - 1.
-  U128 pv[2][PF];
+  // Tile loads run one tile ahead (issued before the current tile is
+  // computed, stored to the other LDS buffer after it).
+  U128 pv[PF];
   constexpr uint32_t RB = D * sizeof(Tin);
   // V has n rows; tokens n..n_pad-1 read as zeros (N = 0 there)
   const __amdgpu_buffer_rsrc_t rv =
       make_rsrc(Vg + (long)t_begin * D, range_bytes(t_begin, min(t_end, n), RB));
-  auto prefetch = [&](U128 *regs, int t0) {
+  auto prefetch = [&](int t0) {
     const uint32_t toff = (uint32_t)(t0 - t_begin) * RB;
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       const int idx = threadIdx.x + u * 256;
       const int row = idx / CPR, ch = idx % CPR;
       if ((TN * CPR) % 256 == 0 || idx < TN * CPR)
-        regs[u] = buf_load16(rv, toff + (uint32_t)(row * D + ch * EPC) * sizeof(Tin));
+        pv[u] = buf_load16(rv, toff + (uint32_t)(row * D + ch * EPC) * sizeof(Tin));
     }
   };
-  auto stash = [&](const U128 *regs, int buf) {
+  auto stash = [&](int buf) {
+    const U128 *regs = pv;
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       const int idx = threadIdx.x + u * 256;
@@ -268,22 +353,31 @@ vnorm_kernel(const Tin *__restrict__ V, const typename ValueType<Tin>::type *__r
       }
     }
   };
+  // A wave takes blocks tb = tp, tp + TPARTS, ...; the V fragments of the
+  // next block are read from LDS while the current block's products run.
+  constexpr int NB = 4 / TPARTS;
   auto compute = [&](int cur, int t0) {
     if (!active) return;
-#pragma unroll
-    for (int tb = 0; tb < TN / 16; ++tb) {
-      if (tb % tparts != tp) continue;
-      const int tok = t0 + tb * 16 + col;
-      FV vf[KS];
+    FV vb[2][KS];
+    auto load_v = [&](int tb, FV (&vf)[KS]) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         vf[ks] = load8<TV>(&Vs[cur][(tb * 16 + col) * VROW + ks * 32 + 8 * grp]);
+    };
+    load_v(tp, vb[0]);
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int tb = tp + k * TPARTS;
+      if (k + 1 < NB) load_v(tb + TPARTS, vb[(k + 1) & 1]);
+      sched_fence();
+      const FV (&vf)[KS] = vb[k & 1];
+      const int tok = t0 + tb * 16 + col;
       float np = 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mma(gf[db][ks], vf[ks], acc);
+        for (int ks = db >> 1; ks < KS; ++ks) acc = mma(gf[db][ks], vf[ks], acc);
 #pragma unroll
         for (int j = 0; j < 4; ++j) np += acc[j] * frag_elem(vf[db >> 1], 4 * (db & 1) + j);
       }
@@ -292,28 +386,19 @@ vnorm_kernel(const Tin *__restrict__ V, const typename ValueType<Tin>::type *__r
       if (grp == 0 && tok < t_end) Nh[tok] = np;
     }
   };
+
   // (loads of tiles past the range read nothing, so they are unconditional)
   wait_vmem_all();
-  prefetch(pv[0], t_begin);
-  prefetch(pv[1], t_begin + TN);
-  stash(pv[0], 0);
+  prefetch(t_begin);
+  stash(0);
   __syncthreads();
-  for (int it = 0; it < nt; it += 2) {
-    // even tile: registers set 0, LDS buffer 0
-    {
-      const int t0 = t_begin + it * TN;
-      prefetch(pv[0], t0 + 2 * TN);
-      compute(0, t0);
-      stash(pv[1], 1);
-      __syncthreads();
-    }
-    if (it + 1 < nt) {
-      const int t0 = t_begin + (it + 1) * TN;
-      prefetch(pv[1], t0 + 2 * TN);
-      compute(1, t0);
-      stash(pv[0], 0);
-      __syncthreads();
-    }
+  for (int it = 0; it < nt; ++it) {
+    const int t0 = t_begin + it * TN;
+    const int cur = it & 1;
+    prefetch(t0 + TN);
+    compute(cur, t0);
+    stash(cur ^ 1);
+    __syncthreads();
   }
 }
 
@@ -464,42 +549,54 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
   };
 
   // One 16-token block: the sum over this wave's rows for token tok0 + col.
-  auto block_sum = [&](auto masked, int cur, int tb, int tok0) -> float {
-    constexpr bool MASKED = decltype(masked)::value;
-    FQ kf[KS];
-    FV vf[MODE == 0 ? KS : 1];
+  // The K and V fragments of a block are read from LDS one block ahead, so
+  // their latency hides behind the previous block's products and terms.
+  auto load_frags = [&](int cur, int tb, FQ (&kf)[KS], FV (&vf)[MODE == 0 ? KS : 1]) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       kf[ks] = load8<Tin>(&Ks[cur][(tb * 16 + col) * KROW + ks * 32 + 8 * grp]);
       if (MODE == 0) vf[ks] = load8<TV>(&Vs[cur][(tb * 16 + col) * VROW + ks * 32 + 8 * grp]);
+    }
+  };
+  auto block = [&](auto masked, int cur, int tb, int tok0, const FQ (&kf)[KS],
+                   const FV (&vf)[MODE == 0 ? KS : 1]) -> float {
+    constexpr bool MASKED = decltype(masked)::value;
+    f32x4 sa[QBW], xa[QBW];
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+      f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s4 = mma(qf[qb][ks], kf[ks], s4);
+      sa[qb] = s4;
+    }
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+      f32x4 x4 = xinit[qb];
+      if (MODE == 0) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) x4 = mma(yhf[qb][ks], vf[ks], x4);
+      }
+      if (SPLIT_Y) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) x4 = mma(ylf[qb][ks], vf[ks], x4);
+      }
+      xa[qb] = x4;
     }
     const int tok = tok0 + col;
     const float nv = (MODE == 0) ? Ns[cur][wv][tb * 16 + col] : 0.f;
     float tacc = 0.f;
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) {
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sa = mma(qf[qb][ks], kf[ks], sa);
-      f32x4 xa = xinit[qb];
-      if (MODE == 0) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) xa = mma(yhf[qb][ks], vf[ks], xa);
-      }
-      if (SPLIT_Y) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) xa = mma(ylf[qb][ks], vf[ks], xa);
-      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float e = fmaf(sa[j], c, -beta[qb][j]);
+        float e = fmaf(sa[qb][j], c, -beta[qb][j]);
         if (MASKED && tok > lim[qb][j]) e = -INFINITY;
         const float a = hw_exp2(e);
         if (MODE == 1) {
           tacc += a;
         } else {
           const float den = (1.f + eps) - a;
-          const float q2 = fmaxf(fmaf(-2.f, xa[j], nv), kTiny);
+          const float q2 = fmaxf(fmaf(-2.f, xa[qb][j], nv), kTiny);
           const float u = q2 * hw_rsq(q2 * den * den);
           tacc = fmaf(a * wr[qb][j], u, tacc);
         }
@@ -508,6 +605,18 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
     tacc += __shfl_xor(tacc, 16, 64);
     tacc += __shfl_xor(tacc, 32, 64);
     return tacc;
+  };
+  auto tile = [&](auto masked, int cur, int t0) {
+    FQ kb[2][KS];
+    FV vb[2][MODE == 0 ? KS : 1];
+    load_frags(cur, 0, kb[0], vb[0]);
+#pragma unroll
+    for (int tb = 0; tb < TN / 16; ++tb) {
+      if (tb + 1 < TN / 16) load_frags(cur, tb + 1, kb[(tb + 1) & 1], vb[(tb + 1) & 1]);
+      sched_fence();
+      const float tsum = block(masked, cur, tb, t0 + tb * 16, kb[tb & 1], vb[tb & 1]);
+      if (grp == 0) red[cur][wv * TN + tb * 16 + col] = tsum;
+    }
   };
 
   wait_vmem_all();
@@ -518,17 +627,14 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
     const int t0 = t_begin + it * TN;
     const int cur = it & 1;
     prefetch(t0 + TN);  // past the range this reads nothing
+    if (t0 > wave_last) {
+      if (grp == 0)
 #pragma unroll
-    for (int tb = 0; tb < TN / 16; ++tb) {
-      const int tok0 = t0 + tb * 16;
-      float tsum = 0.f;
-      if (tok0 <= wave_last) {
-        if (tok0 + 15 > wave_first)
-          tsum = block_sum(std::true_type{}, cur, tb, tok0);
-        else
-          tsum = block_sum(std::false_type{}, cur, tb, tok0);
-      }
-      if (grp == 0) red[cur][wv * TN + tb * 16 + col] = tsum;
+        for (int tb = 0; tb < TN / 16; ++tb) red[cur][wv * TN + tb * 16 + col] = 0.f;
+    } else if (t0 + TN - 1 > wave_first) {
+      tile(std::true_type{}, cur, t0);
+    } else {
+      tile(std::false_type{}, cur, t0);
     }
     stash(cur ^ 1);
     __syncthreads();
@@ -575,9 +681,8 @@ static hipError_t run_prep(const float *Gpart, int gsplits, const float *O, cons
                            void *Yhi, void *Ylo, float4 *consts, hipStream_t st) {
   {
     TimedLaunch tl_("gram_reduce", st);
-    const long total = (long)h_q * D * D;
-    hipLaunchKernelGGL((gram_reduce_kernel<D, TV>), dim3((unsigned)((total + 255) / 256)),
-                       dim3(256), 0, st, Gpart, gsplits, h_q, (TV *)Gv, Gr);
+    hipLaunchKernelGGL((gram_reduce_kernel<D, TV>), dim3(D, h_q), dim3(D), 0, st, Gpart, gsplits,
+                       h_q, (TV *)Gv, Gr);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -608,19 +713,24 @@ template <typename Tin, int D>
 static hipError_t run_vnorm(const void *V, const void *Gv, int batch, int n, int n_pad, int h_q,
                             int h_kv, float *Nn, hipStream_t st) {
   typedef typename ValueType<Tin>::type TV;
-  // about 512 workgroups (two per CU) of whole 64-token tiles
+  // about 768 workgroups (three per CU at <= 168 VGPRs) of whole 64-token tiles
   const int G = h_q / h_kv;
   const int hpw = G < 4 ? G : 4;
   const long units = (long)((G + hpw - 1) / hpw) * h_kv * batch;
   const int tiles = n_pad / 64;
-  const long want = std::max(1L, 512L / units);
+  const long want = std::max(1L, 768L / units);  // three workgroups per CU
   const int tpw = std::min(64 * (int)((tiles + want - 1) / want), kMaxRangeTokens);
   const int nchunk = (n_pad + tpw - 1) / tpw;
   const long blocks = (long)nchunk * units;
   {
     TimedLaunch tl_("vnorm", st);
-    hipLaunchKernelGGL((vnorm_kernel<Tin, D>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const Tin *)V, (const TV *)Gv, n, n_pad, h_q, h_kv, tpw, nchunk, Nn);
+#define KVS_VN(TP)                                                                            \
+  hipLaunchKernelGGL((vnorm_kernel<Tin, D, TP>), dim3((unsigned)blocks), dim3(256), 0, st,    \
+                     (const Tin *)V, (const TV *)Gv, n, n_pad, h_q, h_kv, tpw, nchunk, Nn)
+    if (4 / hpw == 4) KVS_VN(4);
+    else if (4 / hpw == 2) KVS_VN(2);
+    else KVS_VN(1);
+#undef KVS_VN
   }
   return hipGetLastError();
 }
