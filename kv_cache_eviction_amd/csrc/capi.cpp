@@ -113,8 +113,7 @@ kvs_status check_select(const kvs_lore_desc *d) {
 }
 
 size_t topb_bytes_of(const kvs_lore_desc *d) {
-  const size_t nchunks = ((size_t)d->n + d->chunk - 1) / d->chunk;
-  return align_up((size_t)d->batch * d->h_kv * nchunks * 4);
+  return align_up(kvs::topb_workspace_bytes(d->batch * d->h_kv, d->n, d->chunk));
 }
 
 kvs_status check_ws(void *ws, size_t ws_bytes, size_t need) {
@@ -222,7 +221,7 @@ KVS_API kvs_status kvscore_topb_select(const kvs_lore_desc *desc, const float *S
   const int B = desc->budget < n_cand ? desc->budget : n_cand;
   const int n_keep = desc->n_sink + B + desc->w;
   hipError_t e = kvs::launch_topb(S, desc->batch * desc->h_kv, desc->n, desc->n_sink, desc->w,
-                                  desc->chunk, desc->budget, n_keep, at<uint32_t>(ws, 0), kept,
+                                  desc->chunk, desc->budget, n_keep, ws, kept,
                                   pooled, static_cast<hipStream_t>(stream));
   return hip_status(e, "top-B select");
 }

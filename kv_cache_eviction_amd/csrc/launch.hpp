@@ -65,9 +65,9 @@ hipError_t launch_score(int etype, int d, int mode, const void *Q, const void *K
                         float *S, hipStream_t st);
 
 // Selection and compaction.
+size_t topb_workspace_bytes(int rows, int n, int chunk);
 hipError_t launch_topb(const float *S, int rows, int n, int n_sink, int w, int chunk, int budget,
-                       int n_keep, uint32_t *keys_ws, int32_t *kept, float *pooled,
-                       hipStream_t st);
+                       int n_keep, void *ws, int32_t *kept, float *pooled, hipStream_t st);
 hipError_t launch_compact(int rows, int n_src, int n_keep, int cap_dst, int row_bytes,
                           const void *K, const void *V, const int32_t *kept, void *K_out,
                           void *V_out, int32_t *pos_out, const float *score_in,

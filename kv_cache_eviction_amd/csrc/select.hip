@@ -7,11 +7,15 @@
 // score of the candidates in its aligned chunk, ties going to the lower index.
 //
 // Because every candidate of a chunk shares the pooled score, ranking tokens is
-// ranking chunks weighted by their candidate count: one workgroup per row
-// turns each chunk's mean into an order-preserving 32-bit key, runs a 4-pass
-// 8-bit radix select with token-count weights to find the threshold key tau
-// and how many tokens of the tau-chunks are still needed, then writes the
-// selection in ascending index order with two block-wide scans.
+// ranking chunks weighted by their candidate count.  Each chunk's mean becomes
+// an order-preserving 32-bit key.  Selection runs in two levels so a row is
+// spread over many workgroups: every segment of kSeg chunks keeps the chunks
+// whose key reaches its own top-B threshold (a superset of the row's
+// selection within that segment), then one workgroup per row runs a 4-pass
+// 8-bit radix select with token-count weights over the surviving candidates
+// to find the threshold key tau and how many tokens of the tau-chunks are
+// still needed, and writes the selection in ascending index order with
+// block-wide scans.
 #include "common.hpp"
 #include "launch.hpp"
 #include "timing.hpp"
@@ -81,75 +85,26 @@ topb_pool_kernel(const float *__restrict__ S, int n, int n_sink, int w, int chun
   }
 }
 
-// Selection: one workgroup per row.  The row's chunk keys are staged in LDS
-// when they fit (up to kKeysLds chunks: 128K tokens at chunk 4), else read
-// from the workspace.
-constexpr int kKeysLds = 32768;
-
-__global__ void __launch_bounds__(1024)
-topb_select_kernel(int n, int n_sink, int w, int chunk, int budget, int n_keep, int nchunks,
-                   const uint32_t *__restrict__ keys_ws, int32_t *__restrict__ kept) {
-  __shared__ uint32_t lds_keys[kKeysLds];
-  const int keys_in_lds = nchunks <= kKeysLds;
-  // one 256-bin histogram per wave: the high digits of nearby scores collide,
-  // and a shared histogram would serialise every atomic on one bin
-  __shared__ int hist[16 * 256];
-  __shared__ int scan_sh[17];
-  __shared__ uint32_t s_prefix;
-  __shared__ int s_rem;
+// ---------------------------------------------------------------------------
+// Weighted radix select over a list of items (item i: key(i), tokens cnt(i)):
+// the largest key tau such that the items with key >= tau hold at least rem
+// tokens, and how many tokens of the tau-items are still needed (*rem_out).
+// The caller guarantees the list holds at least rem tokens.  hist holds
+// nw * 256 ints (one histogram per wave: the high digits of nearby scores
+// collide, and one shared histogram would serialise every atomic on one bin).
+template <class KeyF, class CntF>
+__device__ uint32_t radix_threshold(int n_items, KeyF key, CntF cnt, int rem, int *hist,
+                                    uint32_t *s_prefix, int *s_rem, int *rem_out) {
   const int tid = threadIdx.x, bs = blockDim.x;
-  const long row = blockIdx.x;
-  const int lo = n_sink, hi = n - w;
-  const int n_cand = hi - lo;
-  const int B = min(budget, n_cand);
-  int32_t *kr = kept + row * n_keep;
-
-  for (int i = tid; i < n_sink; i += bs) kr[i] = i;
-  for (int i = tid; i < w; i += bs) kr[n_sink + B + i] = n - w + i;
-  if (B <= 0) return;
-
-  const uint32_t *gk = keys_ws + row * nchunks;
-  const uint32_t *keys = gk;
-  constexpr int U = 8;
-  if (keys_in_lds) {
-    for (int base = tid; base < nchunks; base += bs * U) {
-      uint32_t kk[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = base + u * bs;
-        kk[u] = c < nchunks ? gk[c] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = base + u * bs;
-        if (c < nchunks) lds_keys[c] = kk[u];
-      }
-    }
-    keys = lds_keys;
-  }
-  __syncthreads();
-
   const int wv = tid >> 6, nw = bs >> 6;
   uint32_t prefix = 0, mask = 0;
-  int rem = B;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 16 * 256; i += bs) hist[i] = 0;
+    for (int i = tid; i < nw * 256; i += bs) hist[i] = 0;
     __syncthreads();
-    for (int base = tid; base < nchunks; base += bs * U) {
-      uint32_t kk[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = base + u * bs;
-        kk[u] = c < nchunks ? keys[c] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = base + u * bs;
-        if (c >= nchunks) continue;
-        const int cnt = min(c * chunk + chunk, hi) - max(c * chunk, lo);
-        if (cnt <= 0 || (kk[u] & mask) != prefix) continue;
-        atomicAdd(&hist[wv * 256 + ((kk[u] >> shift) & 255u)], cnt);
-      }
+    for (int i = tid; i < n_items; i += bs) {
+      const int c = cnt(i);
+      const uint32_t k = key(i);
+      if (c > 0 && (k & mask) == prefix) atomicAdd(&hist[wv * 256 + ((k >> shift) & 255u)], c);
     }
     __syncthreads();
     for (int dg = tid; dg < 256; dg += bs) {
@@ -183,25 +138,138 @@ topb_select_kernel(int n, int n_sink, int w, int chunk, int budget, int n_keep, 
           }
           cum += hb[j];
         }
-        s_prefix = prefix | ((uint32_t)sel << shift);
-        s_rem = rem - cum;
+        *s_prefix = prefix | ((uint32_t)sel << shift);
+        *s_rem = rem - cum;
       }
     }
     __syncthreads();
-    prefix = s_prefix;
-    rem = s_rem;
+    prefix = *s_prefix;
+    rem = *s_rem;
     mask |= 255u << shift;
+    __syncthreads();
   }
-  const uint32_t tau = prefix;
+  *rem_out = rem;
+  return prefix;
+}
 
-  // Emit in ascending order.  Wave v owns the contiguous chunk range
-  // [v*per, (v+1)*per), walked 64 chunks at a time (one per lane, so LDS reads
-  // are conflict-free); tau-chunks are taken in index order until rem tokens,
-  // using in-wave prefix sums and one block scan over the wave totals.
-  const int lane = tid & 63;
-  const int per = ((nchunks + nw - 1) / nw + 63) / 64 * 64;
-  const int c_lo = min(nchunks, wv * per), c_hi = min(nchunks, c_lo + per);
-  auto chunk_cnt = [&](int cj) { return min(cj * chunk + chunk, hi) - max(cj * chunk, lo); };
+__device__ __forceinline__ int chunk_tokens(int cj, int chunk, int lo, int hi) {
+  return min(cj * chunk + chunk, hi) - max(cj * chunk, lo);
+}
+
+// Level 1: one workgroup of 256 threads per (segment of kSeg chunks, row);
+// thread t owns chunks 4t..4t+3 of the segment.  Keeps, in index order, the
+// chunks whose key is at least the segment's own top-B threshold (all of
+// them when the segment holds at most B tokens).
+constexpr int kSeg = 1024;
+
+__global__ void __launch_bounds__(256)
+topb_local_kernel(const uint32_t *__restrict__ keys_ws, int n, int n_sink, int w, int chunk,
+                  int nchunks, int B, int nseg, int32_t *__restrict__ cand,
+                  int32_t *__restrict__ cand_n) {
+  __shared__ int hist[4 * 256];
+  __shared__ int scan_sh[5];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_rem;
+  __shared__ uint32_t seg_keys[kSeg];
+  const int seg = blockIdx.x;
+  const long row = blockIdx.y;
+  const int lo = n_sink, hi = n - w;
+  const int c0 = seg * kSeg;
+  const int items = min(kSeg, nchunks - c0);
+  const uint32_t *gk = keys_ws + row * nchunks + c0;
+  for (int i = threadIdx.x; i < kSeg; i += blockDim.x) seg_keys[i] = i < items ? gk[i] : 0u;
+  int toks = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = 4 * threadIdx.x + k;
+    if (i < items) toks += max(chunk_tokens(c0 + i, chunk, lo, hi), 0);
+  }
+  int total;
+  block_exclusive_scan(toks, scan_sh, &total);  // (also orders the seg_keys writes)
+  uint32_t tau = 0;
+  if (total > B) {
+    int rem_unused;
+    tau = radix_threshold(
+        items, [&](int i) { return seg_keys[i]; },
+        [&](int i) { return chunk_tokens(c0 + i, chunk, lo, hi); }, B, hist, &s_prefix, &s_rem,
+        &rem_unused);
+  }
+  int keep[4], nk = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = 4 * threadIdx.x + k;
+    keep[k] = i < items && chunk_tokens(c0 + i, chunk, lo, hi) > 0 && seg_keys[i] >= tau;
+    nk += keep[k];
+  }
+  int kept_total;
+  int pos = block_exclusive_scan(nk, scan_sh, &kept_total);
+  int32_t *out = cand + row * (long)nchunks + c0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (keep[k]) out[pos++] = c0 + 4 * threadIdx.x + k;
+  if (threadIdx.x == 0) cand_n[row * nseg + seg] = kept_total;
+}
+
+// Level 2: one workgroup per row over the candidates of all segments (staged
+// in LDS when they fit, else the row's chunks are scanned directly).
+constexpr int kCandLds = 12288;
+
+__global__ void __launch_bounds__(1024)
+topb_final_kernel(int n, int n_sink, int w, int chunk, int budget, int n_keep, int nchunks,
+                  int nseg, const uint32_t *__restrict__ keys_ws,
+                  const int32_t *__restrict__ cand, const int32_t *__restrict__ cand_n,
+                  int32_t *__restrict__ kept) {
+  __shared__ uint32_t c_key[kCandLds];
+  __shared__ int32_t c_idx[kCandLds];
+  __shared__ int hist[16 * 256];
+  __shared__ int scan_sh[17];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_rem;
+  const int tid = threadIdx.x, bs = blockDim.x;
+  const long row = blockIdx.x;
+  const int lo = n_sink, hi = n - w;
+  const int n_cand = hi - lo;
+  const int B = min(budget, n_cand);
+  int32_t *kr = kept + row * n_keep;
+
+  for (int i = tid; i < n_sink; i += bs) kr[i] = i;
+  for (int i = tid; i < w; i += bs) kr[n_sink + B + i] = n - w + i;
+  if (B <= 0) return;
+
+  const uint32_t *rk = keys_ws + row * nchunks;
+  const int32_t *rc = cand + row * (long)nchunks;
+  // gather the segments' candidate lists in order
+  int total = 0;
+  for (int base = 0; base < nseg; base += bs) {
+    const int sg = base + tid;
+    const int cn = sg < nseg ? cand_n[row * nseg + sg] : 0;
+    int part;
+    const int at = total + block_exclusive_scan(cn, scan_sh, &part);
+    if (sg < nseg && at + cn <= kCandLds)
+      for (int j = 0; j < cn; ++j) {
+        const int ci = rc[sg * kSeg + j];
+        c_idx[at + j] = ci;
+        c_key[at + j] = rk[ci];
+      }
+    total += part;
+  }
+  __syncthreads();
+  const bool in_lds = total <= kCandLds;
+  const int n_items = in_lds ? total : nchunks;
+  auto idx_of = [&](int i) { return in_lds ? (int)c_idx[i] : i; };
+  auto key_of = [&](int i) { return in_lds ? c_key[i] : rk[i]; };
+  auto cnt_of = [&](int i) { return chunk_tokens(idx_of(i), chunk, lo, hi); };
+
+  int rem;
+  const uint32_t tau = radix_threshold(n_items, key_of, cnt_of, B, hist, &s_prefix, &s_rem, &rem);
+
+  // Emit in ascending order.  Wave v owns the contiguous item range
+  // [v*per, (v+1)*per), walked 64 items at a time (one per lane);
+  // tau-items are taken in index order until rem tokens, using in-wave prefix
+  // sums and block scans over the wave totals.
+  const int lane = tid & 63, wv = tid >> 6, nw = bs >> 6;
+  const int per = ((n_items + nw - 1) / nw + 63) / 64 * 64;
+  const int c_lo = min(n_items, wv * per), c_hi = min(n_items, c_lo + per);
   auto wave_incl = [&](int x) {
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -213,29 +281,29 @@ topb_select_kernel(int n, int n_sink, int w, int chunk, int budget, int n_keep, 
   // pass 1: tau-tokens per wave
   int ties = 0;
   for (int base = c_lo; base < c_hi; base += 64) {
-    const int cj = base + lane;
-    if (cj < c_hi) {
-      const int cnt = chunk_cnt(cj);
-      if (cnt > 0 && keys[cj] == tau) ties += cnt;
+    const int it = base + lane;
+    if (it < c_hi) {
+      const int cnt = cnt_of(it);
+      if (cnt > 0 && key_of(it) == tau) ties += cnt;
     }
   }
   ties = __shfl(wave_incl(ties), 63, 64);
-  int total;
-  const int tie_before_wave = block_exclusive_scan(lane == 0 ? ties : 0, scan_sh, &total);
+  int tot;
+  const int tie_before_wave = block_exclusive_scan(lane == 0 ? ties : 0, scan_sh, &tot);
   const int tie_wave0 = __shfl(tie_before_wave, 0, 64);
   // pass 2: selected tokens per wave
   int sel = 0, tie_run = tie_wave0;
   for (int base = c_lo; base < c_hi; base += 64) {
-    const int cj = base + lane;
+    const int it = base + lane;
     int cnt = 0, tcnt = 0;
     uint32_t key = 0;
-    if (cj < c_hi) {
-      cnt = max(chunk_cnt(cj), 0);
-      key = keys[cj];
+    if (it < c_hi) {
+      cnt = max(cnt_of(it), 0);
+      key = key_of(it);
       tcnt = (cnt > 0 && key == tau) ? cnt : 0;
     }
     const int tincl = wave_incl(tcnt);
-    const int tb = tie_run + tincl - tcnt;  // tau-tokens before this chunk
+    const int tb = tie_run + tincl - tcnt;  // tau-tokens before this item
     if (cnt > 0) {
       if (key > tau) sel += cnt;
       else if (key == tau) sel += min(max(rem - tb, 0), cnt);
@@ -243,18 +311,19 @@ topb_select_kernel(int n, int n_sink, int w, int chunk, int budget, int n_keep, 
     tie_run += __shfl(tincl, 63, 64);
   }
   sel = __shfl(wave_incl(sel), 63, 64);
-  const int out_before_wave = block_exclusive_scan(lane == 0 ? sel : 0, scan_sh, &total);
+  const int out_before_wave = block_exclusive_scan(lane == 0 ? sel : 0, scan_sh, &tot);
   int out_run = n_sink + __shfl(out_before_wave, 0, 64);
   // pass 3: write
   tie_run = tie_wave0;
   for (int base = c_lo; base < c_hi; base += 64) {
-    const int cj = base + lane;
+    const int it = base + lane;
     int cnt = 0, tcnt = 0, a = 0;
     uint32_t key = 0;
-    if (cj < c_hi) {
-      cnt = max(chunk_cnt(cj), 0);
+    if (it < c_hi) {
+      const int cj = idx_of(it);
+      cnt = max(chunk_tokens(cj, chunk, lo, hi), 0);
       a = max(cj * chunk, lo);
-      key = keys[cj];
+      key = key_of(it);
       tcnt = (cnt > 0 && key == tau) ? cnt : 0;
     }
     const int tincl = wave_incl(tcnt);
@@ -273,10 +342,23 @@ topb_select_kernel(int n, int n_sink, int w, int chunk, int budget, int n_keep, 
   }
 }
 
+size_t topb_workspace_bytes(int rows, int n, int chunk) {
+  const size_t nchunks = ((size_t)n + chunk - 1) / chunk;
+  const size_t nseg = (nchunks + kSeg - 1) / kSeg;
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  return al((size_t)rows * nchunks * 4) + al((size_t)rows * nchunks * 4) + al((size_t)rows * nseg * 4);
+}
+
 hipError_t launch_topb(const float *S, int rows, int n, int n_sink, int w, int chunk, int budget,
-                       int n_keep, uint32_t *keys_ws, int32_t *kept, float *pooled,
-                       hipStream_t st) {
+                       int n_keep, void *ws, int32_t *kept, float *pooled, hipStream_t st) {
   const int nchunks = (n + chunk - 1) / chunk;
+  const int nseg = (nchunks + kSeg - 1) / kSeg;
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  uint32_t *keys_ws = static_cast<uint32_t *>(ws);
+  int32_t *cand = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + al((size_t)rows * nchunks * 4));
+  int32_t *cand_n = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + 2 * al((size_t)rows * nchunks * 4));
+  const int n_cand = n - n_sink - w;
+  const int B = budget < n_cand ? budget : n_cand;
   {
     TimedLaunch tl_("topb_pool", st);
     hipLaunchKernelGGL(topb_pool_kernel, dim3((nchunks + 255) / 256, rows), dim3(256), 0, st, S,
@@ -284,15 +366,21 @@ hipError_t launch_topb(const float *S, int rows, int n, int n_sink, int w, int c
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (B > 0) {
+    TimedLaunch tl_("topb_local", st);
+    hipLaunchKernelGGL(topb_local_kernel, dim3(nseg, rows), dim3(256), 0, st, keys_ws, n, n_sink,
+                       w, chunk, nchunks, B, nseg, cand, cand_n);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   {
     TimedLaunch tl_("topb_select", st);
-    hipLaunchKernelGGL(topb_select_kernel, dim3(rows), dim3(1024), 0, st, n, n_sink, w, chunk,
-                       budget, n_keep, nchunks, keys_ws, kept);
+    hipLaunchKernelGGL(topb_final_kernel, dim3(rows), dim3(1024), 0, st, n, n_sink, w, chunk,
+                       budget, n_keep, nchunks, nseg, keys_ws, cand, cand_n, kept);
   }
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
 // Compaction: K'[row][r] = K[row][kept[r]] (and V), 16 bytes per thread.
 __global__ void __launch_bounds__(256)
 compact_kernel(const uint8_t *__restrict__ K, const uint8_t *__restrict__ V,

@@ -94,7 +94,10 @@ def test_selection_descriptor_needs_only_selection_fields():
     d = kv.lore_desc(batch=2, n=1024, h_q=3, h_kv=3, d=128, d_model=1, w=102, m=0, t=0,
                      n_sink=0, chunk=1, budget=102)
     assert lib.kvs_lore_workspace_bytes(ctypes.byref(d)) == 0     # not a scoring descriptor
-    assert lib.kvs_topb_workspace_bytes(ctypes.byref(d)) == 2 * 3 * 1024 * 4
+    # chunk keys + per-segment candidate lists (one int per chunk each) + one
+    # count per 1024-chunk segment, each region 256-byte aligned
+    rows, nchunks = 2 * 3, 1024
+    assert lib.kvs_topb_workspace_bytes(ctypes.byref(d)) == 2 * rows * nchunks * 4 + 256
 
 
 def test_h2o_descriptor_checks():

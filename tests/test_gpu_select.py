@@ -1,0 +1,97 @@
+"""Top-B selection alone on the GPU, from given score arrays, against the
+fp64 oracle (LORE-KV page, "Evict and decode", Eq. 8, chunk pooling from the
+Hyperparameters table).
+
+The selection runs in two levels (segments of 1024 chunks keep the chunks at
+or above their own top-B threshold, then one workgroup per row selects among
+the survivors).  These cases cover one segment, many segments, a row whose
+survivors overflow the final level's LDS staging (all scores tied), budgets
+covering every candidate, and protected ranges that cut chunks.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import kv_cache_eviction_amd as kv
+from parity import check_kept
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available()
+    return torch.device("cuda:0")
+
+
+def run_select(dev, S, n_sink, w, chunk, budget):
+    b, hk, n = S.shape
+    desc = kv.lore_desc(batch=b, n=n, h_q=hk, h_kv=hk, d=128, d_model=1, w=w, m=0, t=0,
+                        n_sink=n_sink, chunk=chunk, budget=budget)
+    ws = torch.empty(kv.kvs_topb_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    kept = torch.empty(b, hk, desc.n_keep, dtype=torch.int32, device=dev)
+    Sd = S.to(dev).contiguous()
+    kv.kvscore_topb_select(desc, Sd, kept, None, ws)
+    torch.cuda.synchronize()
+    return kept.cpu().numpy()
+
+
+def check(dev, S, n_sink, w, chunk, budget):
+    g = run_select(dev, S, n_sink, w, chunk, budget)
+    o, pooled = oracle.topb_select(S.double().numpy(), n_sink=n_sink, w=w, chunk=chunk,
+                                   budget=budget)
+    return check_kept(g, o, pooled, n_sink, w, budget)
+
+
+def test_single_segment_random(dev):
+    g = torch.Generator().manual_seed(71)
+    S = torch.rand(2, 3, 2000, generator=g)
+    check(dev, S, n_sink=1, w=32, chunk=4, budget=64)
+
+
+def test_many_segments_heavy_tail(dev):
+    """131072 tokens (32 segments of 1024 chunks), a few large scores."""
+    g = torch.Generator().manual_seed(72)
+    S = torch.rand(1, 4, 131072, generator=g) * 0.01
+    hot = torch.randint(0, 131072, (4, 300), generator=g)
+    for r in range(4):
+        S[0, r, hot[r]] = torch.rand(300, generator=g) * 5
+    check(dev, S, n_sink=1, w=32, chunk=4, budget=128)
+
+
+def test_all_tied_overflows_final_staging(dev):
+    """Equal scores everywhere: every segment keeps all its chunks (16384 >
+    the 12288 the final level stages), and the answer is the lowest indices."""
+    n, n_sink, w, budget = 65536, 4, 32, 300
+    S = torch.full((1, 2, n), 0.5)
+    kept = run_select(dev, S, n_sink, w, 4, budget)
+    expect = np.concatenate([np.arange(n_sink), np.arange(n_sink, n_sink + budget),
+                             np.arange(n - w, n)])
+    for row in kept.reshape(-1, kept.shape[-1]):
+        assert np.array_equal(row, expect)
+
+
+def test_budget_covers_all_candidates(dev):
+    g = torch.Generator().manual_seed(73)
+    S = torch.rand(1, 2, 5000, generator=g)
+    check(dev, S, n_sink=3, w=17, chunk=4, budget=5000)
+
+
+@pytest.mark.parametrize("n,n_sink,w,chunk,budget", [
+    (4099, 3, 5, 4, 1000),      # ragged last segment, sink and window cut chunks
+    (70000, 2, 31, 4, 9000),    # large budget: survivors of many segments
+    (9000, 0, 1, 1, 777),       # chunk 1 (token-level ranking)
+    (20000, 1, 32, 8, 257),     # chunk 8
+])
+def test_edges(dev, n, n_sink, w, chunk, budget):
+    g = torch.Generator().manual_seed(n + budget)
+    S = torch.rand(1, 2, n, generator=g) ** 4
+    check(dev, S, n_sink, w, chunk, budget)
+
+
+def test_quantized_scores_many_ties(dev):
+    """Scores on a coarse grid: ties inside and across segments."""
+    g = torch.Generator().manual_seed(74)
+    S = torch.randint(0, 8, (1, 3, 40000), generator=g).float() / 8
+    check(dev, S, n_sink=1, w=32, chunk=4, budget=2000)
