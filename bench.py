@@ -53,6 +53,38 @@ def kernel_work(cfg):
     }
 
 
+def _csrc_digest():
+    """sha256 over the library sources (csrc/ and include/): HBM byte counts
+    taken with rocprofv3 are reported only while this matches the digest
+    recorded with them."""
+    import hashlib
+    h = hashlib.sha256()
+    for sub in ("kv_cache_eviction_amd/csrc", "include"):
+        d = os.path.join(ROOT, sub)
+        for f in sorted(os.listdir(d)):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from profiles/pmc_traffic.json (two
+    rocprofv3 --pmc passes, FETCH_SIZE and WRITE_SIZE in KiB per dispatch,
+    each scaled by what the counter reads for a plain copy of known size), or
+    None when the record is missing or the sources changed since."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != _csrc_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if k is None:
+        return None
+    return int(round((k["fetch_kib"] * rec["fetch_scale"] + k["write_kib"] * rec["write_scale"]) * 1024))
+
+
 def roofline_of(name, work, avg_ms):
     w = work.get(name)
     if w is None:
@@ -61,11 +93,11 @@ def roofline_of(name, work, avg_ms):
         achieved = w["flops"] / (avg_ms * 1e-3) / 1e12
         return {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(name),
                 "algorithmic_per_launch": w["flops"], "avg_launch_ms": round(avg_ms, 4)}
     achieved = w["bytes"] / (avg_ms * 1e-3) / 1e9
     return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
-            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(name),
             "algorithmic_per_launch": w["bytes"], "avg_launch_ms": round(avg_ms, 4)}
 
 
@@ -138,7 +170,7 @@ def bench_h2o(kv, torch, dev):
             "slots_attended_per_s": round(rows * slots / (e1.elapsed_time(e2) * 1e-3), 1),
             "roofline": {"kernel": "h2o_decode", "bound": "hbm", "achieved": round(hbm, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(hbm / PEAK_HBM_GBS, 4),
-                         "traffic": None}}
+                         "traffic": measured_traffic("h2o_decode")}}
 
 
 def main():
