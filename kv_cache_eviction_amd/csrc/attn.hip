@@ -9,9 +9,10 @@
 // H2O ("H2O: Heavy-Hitter Oracle", 3.4): a causal prompt row r attends to keys
 // 0..r; only its max and normaliser are needed here.
 //
-// One workgroup per (token split, KV head, sequence) holds one wavefront per
-// query head of the group, so a K/V tile staged in LDS is read once for the
-// whole group.  The logits are formed transposed, S^T = K Q^T (tokens down the
+// One workgroup per (token split, KV head, sequence) holds 4/QBW wavefronts
+// per query head for up to 8 waves (larger groups are split over several
+// workgroups), so a K/V tile staged in LDS is read once for all the query
+// heads it serves.  The logits are formed transposed, S^T = K Q^T (tokens down the
 // rows, query rows across the 16 columns): every lane then owns one query
 // column, keeps that row's running max/sum in registers, and its eight
 // accumulator values are eight tokens of that row.  Loading the K rows in the

@@ -10,12 +10,13 @@
 //   G_h = W_h^T W_h (d x d),  N_i = v_i^T G_h v_i,  y_q = G_h o_q,
 //   x_{q,i} = v_i . y_q,  pi_q = o_q^T G_h o_q,
 // so the per-token work is three dense contractions on the matrix cores
-// (S^T = K Q^T recomputing the logits, X^T = V Y^T, and G_h V^T for N) plus a
+// (S = Q K^T recomputing the logits, X = Y V^T, and G_h V^T for N) plus a
 // short elementwise epilogue, and W_O (d_model wide) is touched once per call.
 //
 // Kernels, in call order:
-//   gram_kernel        G_h partial sums over d_model slabs (MFMA)
-//   prep_kernel        G_h, y_q (rounded to the value type), pi_q, per-row constants
+//   gram_kernel        G_h partial sums over d_model ranges, upper blocks (MFMA)
+//   gram_reduce_kernel G~_h = G_h rounded to the value type, mirrored (symmetric)
+//   prep_kernel        y_q = G~_h o_q (hi + lo), pi_q, per-row constants
 //   vnorm_kernel       N_i for every token and query head (MFMA)
 //   score_kernel<0>    recompute a, form e, aggregate rows and group heads -> S
 //   score_kernel<1>    H2O: column sums of the causal prompt probabilities
