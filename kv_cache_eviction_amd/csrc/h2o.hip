@@ -11,9 +11,12 @@
 // (Def. 2.1).  Rows (sequence, head) are independent, one wavefront each.
 //
 // A row's slots are read as 16-byte lane chunks, D/EPC lanes per slot, so one
-// wave instruction covers 64*16 contiguous-per-slot bytes; invalid slots are
-// never read.  Logits and updated accumulators sit in LDS for the softmax and
-// the arg-min.
+// wave instruction covers 64*16 contiguous-per-slot bytes, and eight such
+// instructions are in flight before any is used; invalid slots (and slots
+// whose probability is 0 in the P.V pass) are never read: their loads take an
+// offset past the buffer resource's range, which returns zeros without a
+// memory access.  The slot map and the logits sit in LDS for the softmax; the
+// updated accumulators are read back (same lane) for the arg-min.
 #include "common.hpp"
 #include "launch.hpp"
 #include "timing.hpp"
@@ -41,22 +44,28 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
   constexpr int EPC = 16 / (int)sizeof(T);
   constexpr int LPR = D / EPC;  // lanes per slot row
   constexpr int RPI = 64 / LPR; // slot rows per wave step
+  constexpr int U = 8;          // wave steps whose loads are in flight together
+  constexpr uint32_t kNoLoad = 0xFFFFFFF0u;  // offset past every range: reads 0, no access
   extern __shared__ float dsh[];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const long row = (long)blockIdx.x * 4 + wv;
   if (row >= rows) return;
   float *prob = dsh + (long)wv * 2 * cap;
-  float *accn = prob + cap;
+  int32_t *pos_s = reinterpret_cast<int32_t *>(prob + cap);
   int32_t *pos = slot_pos + row * cap;
   float *ac = acc + row * cap;
   T *Kr = K + row * cap * D;
   T *Vr = V + row * cap * D;
+  const uint32_t row_bytes = (uint32_t)cap * (uint32_t)(D * sizeof(T));
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kr, row_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vr, row_bytes);
 
-  // lowest free slot, and how many slots hold a token
+  // slot map into LDS; lowest free slot, and how many slots hold a token
   int ws = -1, nvalid = 0;
   for (int base = 0; base < cap; base += 64) {
     const int s = base + lane;
     const int p = s < cap ? pos[s] : 0;
+    if (s < cap) pos_s[s] = p;
     const unsigned long long fb = __ballot(s < cap && p < 0);
     const unsigned long long vb = __ballot(s < cap && p >= 0);
     nvalid += __popcll(vb);
@@ -66,6 +75,7 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
     if (lane == 0 && evict_slot) evict_slot[row] = -2;
     return;
   }
+  wave_lds_sync();
   const int newpos = cur_len - 1;
   const int sub = lane % LPR, rr = lane / LPR;
 
@@ -85,27 +95,34 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
     }
   }
 
-  // logits of every valid slot (the new token's from registers)
-  for (int base = 0; base < cap; base += RPI) {
-    const int s = base + rr;
-    const bool inb = s < cap;
-    const int p = inb ? pos[s] : -1;
-    const bool valid = inb && (p >= 0 || s == ws);
-    float part = 0.f;
-    if (valid) {
-      if (s == ws) {
+  // logits of every valid slot (the new token's from registers); U wave steps
+  // of K rows are loaded before any is used
+  for (int base = 0; base < cap; base += RPI * U) {
+    U128 kk[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = base + u * RPI + rr;
+      const bool ld = s < cap && s != ws && pos_s[s] >= 0;
+      kk[u] = buf_load16(rk, ld ? (uint32_t)(s * D + sub * EPC) * (uint32_t)sizeof(T) : kNoLoad);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = base + u * RPI + rr;
+      const bool inb = s < cap;
+      const bool valid = inb && (s == ws || pos_s[s] >= 0);
+      const T *ke = reinterpret_cast<const T *>(&kk[u]);
+      float part = 0.f;
+      if (inb && s == ws) {
 #pragma unroll
         for (int e = 0; e < EPC; ++e) part += qv[e] * kn[e];
       } else {
-        const U128 kk = *reinterpret_cast<const U128 *>(Kr + (long)s * D + sub * EPC);
-        const T *ke = reinterpret_cast<const T *>(&kk);
 #pragma unroll
         for (int e = 0; e < EPC; ++e) part += qv[e] * to_f32(ke[e]);
       }
-    }
 #pragma unroll
-    for (int o = 1; o < LPR; o <<= 1) part += __shfl_xor(part, o, 64);
-    if (sub == 0 && inb) prob[s] = valid ? part * c : -INFINITY;
+      for (int o = 1; o < LPR; o <<= 1) part += __shfl_xor(part, o, 64);
+      if (sub == 0 && inb) prob[s] = valid ? part * c : -INFINITY;
+    }
   }
   wave_lds_sync();
 
@@ -119,13 +136,11 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
   for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o, 64);
   const float inv = 1.f / l;
   for (int s = lane; s < cap; s += 64) {
-    const bool valid = (s == ws) || pos[s] >= 0;
+    const bool valid = (s == ws) || pos_s[s] >= 0;
     float a = 0.f;
     if (valid) {
       a = hw_exp2(prob[s] - mx) * inv;
-      const float nw = ((s == ws) ? 0.f : ac[s]) + a;
-      ac[s] = nw;
-      accn[s] = nw;
+      ac[s] = ((s == ws) ? 0.f : ac[s]) + a;  // read back by this same lane below
     }
     prob[s] = a;
   }
@@ -135,19 +150,27 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
     float ov[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) ov[e] = 0.f;
-    for (int base = 0; base < cap; base += RPI) {
-      const int s = base + rr;
-      if (s >= cap) continue;
-      const float a = prob[s];
-      if (a == 0.f) continue;
-      if (s == ws) {
+    for (int base = 0; base < cap; base += RPI * U) {
+      U128 vv[U];
+      float av[U];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) ov[e] += a * vn[e];
-      } else {
-        const U128 vv = *reinterpret_cast<const U128 *>(Vr + (long)s * D + sub * EPC);
-        const T *ve = reinterpret_cast<const T *>(&vv);
+      for (int u = 0; u < U; ++u) {
+        const int s = base + u * RPI + rr;
+        av[u] = s < cap ? prob[s] : 0.f;
+        const bool ld = av[u] != 0.f && s != ws;
+        vv[u] = buf_load16(rv, ld ? (uint32_t)(s * D + sub * EPC) * (uint32_t)sizeof(T) : kNoLoad);
+      }
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) ov[e] += a * to_f32(ve[e]);
+      for (int u = 0; u < U; ++u) {
+        const int s = base + u * RPI + rr;
+        const T *ve = reinterpret_cast<const T *>(&vv[u]);
+        if (s == ws) {
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) ov[e] += av[u] * vn[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) ov[e] += av[u] * to_f32(ve[e]);
+        }
       }
     }
 #pragma unroll
@@ -177,10 +200,10 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
     const int recent_from = cur_len - k_recent;
     unsigned long long best = ~0ull;
     for (int s = lane; s < cap; s += 64) {
-      const int p = (s == ws) ? newpos : pos[s];
+      const int p = (s == ws) ? newpos : pos_s[s];
       if (p >= 0 && p < recent_from) {
         const unsigned long long key =
-            ((unsigned long long)order_key_pos(accn[s]) << 32) | (uint32_t)(0x7FFFFFFF - p);
+            ((unsigned long long)order_key_pos(ac[s]) << 32) | (uint32_t)(0x7FFFFFFF - p);
         best = key < best ? key : best;
       }
     }
@@ -193,7 +216,7 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
       const int pev = 0x7FFFFFFF - (int)(uint32_t)(best & 0xFFFFFFFFull);
       int cand = -1;
       for (int s = lane; s < cap; s += 64) {
-        const int p = (s == ws) ? newpos : pos[s];
+        const int p = (s == ws) ? newpos : pos_s[s];
         if (p == pev) cand = s;
       }
 #pragma unroll
@@ -213,7 +236,7 @@ static hipError_t run_decode(int rows, int cap, int cur_len, int k_heavy, int k_
                              const void *v_new, int32_t *slot_pos, float *acc, void *O,
                              int32_t *evict_slot, hipStream_t st) {
   const float c = kLog2e / sqrtf((float)D);
-  const size_t shm = sizeof(float) * 2 * (size_t)cap * 4;
+  const size_t shm = sizeof(float) * 2 * (size_t)cap * 4;  // probabilities and slot map per wave
   {
     TimedLaunch tl_("h2o_decode", st);
     hipLaunchKernelGGL((h2o_decode_kernel<T, D>), dim3((rows + 3) / 4), dim3(256), shm, st,
