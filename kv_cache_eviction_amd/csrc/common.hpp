@@ -126,6 +126,18 @@ template <typename Tin, typename Tout>
 __device__ __forceinline__ void store_converted16(const U128 &v, Tout *dst) {
   if constexpr (sizeof(Tin) == sizeof(Tout) && (sizeof(Tin) == 4 || __is_same(Tin, Tout))) {
     *reinterpret_cast<U128 *>(dst) = v;
+  } else if constexpr (__is_same(Tin, bf16) && __is_same(Tout, f16)) {
+    // bf16 -> fp32 is a shift; fp32 -> fp16 of a bf16 value is exact in the
+    // fp16 normal range, so the round-toward-zero pair conversion (one
+    // instruction per two elements) gives the same bits there
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    U128 o;
+    uint32_t *ow = reinterpret_cast<uint32_t *>(&o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      ow[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[e] << 16),
+                                                                      __uint_as_float(w[e] & 0xFFFF0000u)));
+    *reinterpret_cast<U128 *>(dst) = o;
   } else {
     const Tin *ve = reinterpret_cast<const Tin *>(&v);
     U128 o;
@@ -186,6 +198,21 @@ __device__ __forceinline__ float wave_sum_xor(float v, int mask) {
   return v + __shfl_xor(v, mask, 64);
 }
 
+// Cross-lane sums without LDS traffic: the gfx950 permlane swaps exchange the
+// upper 32 (16) lanes of one register with the lower 32 (16) lanes of
+// another; swapping a value with itself and adding both results gives every
+// lane v[l] + v[l ^ 32] (v[l] + v[l ^ 16]).
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// sum over the four 16-lane groups: lanes l, l^16, l^32, l^48
+__device__ __forceinline__ float group4_sum(float v) { return sum_xor16(sum_xor32(v)); }
+
 // Sum over the 16 lanes of each DPP row (lanes 16r..16r+15); every lane of the
 // row receives the total.  quad_perm [1,0,3,2] and [2,3,0,1] sum each quad,
 // row_half_mirror pairs the two quads of each half-row, row_mirror the halves.
@@ -193,6 +220,8 @@ template <int CTRL> __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
                                                                CTRL, 0xF, 0xF, false));
 }
+// v[l] + v[l ^ 8] within each 16-lane row (row_ror:8 pairs lane i with i +- 8)
+__device__ __forceinline__ float sum_xor8(float v) { return v + dpp_f32<0x128>(v); }
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f32<0xB1>(v);
   v += dpp_f32<0x4E>(v);

@@ -382,8 +382,7 @@ vnorm_kernel(const Tin *__restrict__ V, const typename ValueType<Tin>::type *__r
 #pragma unroll
         for (int j = 0; j < 4; ++j) np += acc[j] * frag_elem(vf[db >> 1], 4 * (db & 1) + j);
       }
-      np = wave_sum_xor(np, 16);
-      np = wave_sum_xor(np, 32);
+      np = group4_sum(np);
       if (grp == 0 && tok < t_end) Nh[tok] = np;
     }
   };
@@ -443,10 +442,14 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
   constexpr int VROW = D + 16 / (int)sizeof(TV);
   constexpr int ITEMS = TN * CPR;
   constexpr int PF = (ITEMS + NT - 1) / NT;
-  constexpr float kTiny = 1e-30f;
+  constexpr float kTiny = 1.17549435e-38f;  // FLT_MIN
   __shared__ __align__(16) Tin Ks[2][TN * KROW];
   __shared__ __align__(16) TV Vs[MODE == 0 ? 2 : 1][MODE == 0 ? TN * VROW : 8];
-  __shared__ __align__(16) float red[2][MAXW * TN];
+  // per-lane partial sums: row (wave, row group) of TN tokens.  Rows are 82
+  // floats apart: the reads of the per-tile sum (8 consecutive tokens x 8
+  // waves, row stride 4*82 = 8 mod 32 banks) hit 32 distinct banks per half-wave.
+  constexpr int RROW = TN + 18;
+  __shared__ __align__(16) float red[2][MAXW * 4 * RROW];
   // N of the tile's tokens for each wave's own query head
   __shared__ float Ns[MODE == 0 ? 2 : 1][MODE == 0 ? MAXW : 1][MODE == 0 ? TN : 1];
 
@@ -468,7 +471,7 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
   FQ qf[QBW][KS];
   FV yhf[MODE == 0 ? QBW : 1][KS];
   FV ylf[SPLIT_Y ? QBW : 1][KS];
-  float beta[QBW][4], wr[QBW][4];
+  float beta[QBW][4], rwr[QBW][4];
   f32x4 xinit[QBW];
   int lim[QBW][4];
   int wave_last = -1, wave_first = 0x7FFFFFFF;
@@ -482,7 +485,19 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
       // rows without keys get a = 2^-inf = 0 on every path, masked or not
       beta[qb][j] = lim[qb][j] >= 0 ? cs.x : INFINITY;
       xinit[qb][j] = -0.5f * cs.y;
-      wr[qb][j] = cs.z;
+      rwr[qb][j] = 0.f;
+      if (MODE == 0) {
+        // a * w_r = 2^(e - beta + log2 w_r): the exponent carries the row
+        // weight; rows of weight <= 0 contribute nothing (the weights are a
+        // softmax times a nonnegative lambda)
+        const float w_r = cs.z;
+        if (w_r > 0.f) {
+          beta[qb][j] -= log2f(w_r);
+          rwr[qb][j] = 1.f / w_r;
+        } else {
+          beta[qb][j] = INFINITY;
+        }
+      }
       if (lim[qb][j] >= 0) {
         wave_last = max(wave_last, lim[qb][j]);
         wave_first = min(wave_first, lim[qb][j]);
@@ -549,9 +564,9 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
     if (MODE == 0) Ns[buf][wv][lane] = pn;
   };
 
-  // One 16-token block: the sum over this wave's rows for token tok0 + col.
-  // The K and V fragments of a block are read from LDS one block ahead, so
-  // their latency hides behind the previous block's products and terms.
+  // One 16-token block: this lane's sum over its 4*QBW query rows for token
+  // tok0 + col.  The K and V fragments of a block are read from LDS one block
+  // ahead, so their latency hides behind the previous block's work.
   auto load_frags = [&](int cur, int tb, FQ (&kf)[KS], FV (&vf)[MODE == 0 ? KS : 1]) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -559,7 +574,7 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
       if (MODE == 0) vf[ks] = load8<TV>(&Vs[cur][(tb * 16 + col) * VROW + ks * 32 + 8 * grp]);
     }
   };
-  auto block = [&](auto masked, int cur, int tb, int tok0, const FQ (&kf)[KS],
+  auto block = [&](auto masked, int tok0, float nv, const FQ (&kf)[KS],
                    const FV (&vf)[MODE == 0 ? KS : 1]) -> float {
     constexpr bool MASKED = decltype(masked)::value;
     f32x4 sa[QBW], xa[QBW];
@@ -584,7 +599,6 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
       xa[qb] = x4;
     }
     const int tok = tok0 + col;
-    const float nv = (MODE == 0) ? Ns[cur][wv][tb * 16 + col] : 0.f;
     float tacc = 0.f;
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) {
@@ -592,34 +606,44 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
       for (int j = 0; j < 4; ++j) {
         float e = fmaf(sa[qb][j], c, -beta[qb][j]);
         if (MASKED && tok > lim[qb][j]) e = -INFINITY;
-        const float a = hw_exp2(e);
         if (MODE == 1) {
-          tacc += a;
+          tacc += hw_exp2(e);
         } else {
-          const float den = (1.f + eps) - a;
-          const float q2 = fmaxf(fmaf(-2.f, xa[qb][j], nv), kTiny);
-          const float u = q2 * hw_rsq(q2 * den * den);
-          tacc = fmaf(a * wr[qb][j], u, tacc);
+          // aw = a * w_r;  u = sqrt(|q2|) / (1 + eps - a) as |q2| rsqrt(|q2| den^2 + tiny)
+          const float aw = hw_exp2(e);
+          const float den = fmaf(-aw, rwr[qb][j], 1.f + eps);
+          const float q2 = fabsf(fmaf(-2.f, xa[qb][j], nv));
+          const float p = q2 * den;
+          const float u = q2 * hw_rsq(fmaf(p, den, kTiny));
+          tacc = fmaf(aw, u, tacc);
         }
       }
     }
-    tacc += __shfl_xor(tacc, 16, 64);
-    tacc += __shfl_xor(tacc, 32, 64);
     return tacc;
   };
   auto tile = [&](auto masked, int cur, int t0) {
     FQ kb[2][KS];
     FV vb[2][MODE == 0 ? KS : 1];
+    float nv[TN / 16];
+#pragma unroll
+    for (int tb = 0; tb < TN / 16; ++tb) nv[tb] = (MODE == 0) ? Ns[cur][wv][tb * 16 + col] : 0.f;
     load_frags(cur, 0, kb[0], vb[0]);
 #pragma unroll
     for (int tb = 0; tb < TN / 16; ++tb) {
       if (tb + 1 < TN / 16) load_frags(cur, tb + 1, kb[(tb + 1) & 1], vb[(tb + 1) & 1]);
       sched_fence();
-      const float tsum = block(masked, cur, tb, t0 + tb * 16, kb[tb & 1], vb[tb & 1]);
-      if (grp == 0) red[cur][wv * TN + tb * 16 + col] = tsum;
+      const float tsum = block(masked, t0 + tb * 16, nv[tb], kb[tb & 1], vb[tb & 1]);
+      red[cur][(wv * 4 + grp) * RROW + tb * 16 + col] = tsum;
+      // a wave further ahead in the tile yields issue priority to the wave
+      // sharing its SIMD, so both reach the tile barrier together
+      if (tb == 0) __builtin_amdgcn_s_setprio(2);
+      else if (tb == 1) __builtin_amdgcn_s_setprio(1);
+      else if (tb == 2) __builtin_amdgcn_s_setprio(0);
     }
+    __builtin_amdgcn_s_setprio(3);
   };
 
+  __builtin_amdgcn_s_setprio(3);
   wait_vmem_all();
   prefetch(t_begin);
   stash(0);
@@ -629,9 +653,8 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
     const int cur = it & 1;
     prefetch(t0 + TN);  // past the range this reads nothing
     if (t0 > wave_last) {
-      if (grp == 0)
 #pragma unroll
-        for (int tb = 0; tb < TN / 16; ++tb) red[cur][wv * TN + tb * 16 + col] = 0.f;
+      for (int tb = 0; tb < TN / 16; ++tb) red[cur][(wv * 4 + grp) * RROW + tb * 16 + col] = 0.f;
     } else if (t0 + TN - 1 > wave_first) {
       tile(std::true_type{}, cur, t0);
     } else {
@@ -639,11 +662,20 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
     }
     stash(cur ^ 1);
     __syncthreads();
-    if (threadIdx.x < TN) {
-      const int tok = t0 + threadIdx.x;
-      if (tok < t_end) {
-        float sum = 0.f;
-        for (int w = 0; w < MAXW; ++w) sum += red[cur][w * TN + threadIdx.x];
+    // Every wave sums the partials of TN / MAXW tokens: lane (token u, wave
+    // part p) adds the four row groups of wave p, then the MAXW parts of a
+    // token are added across lanes (u + TPW * p, p = 0..MAXW-1).
+    {
+      constexpr int TPW = TN / MAXW;
+      const int u = lane % TPW, p = lane / TPW;
+      const int tl = wv * TPW + u;
+      const float *rp = &red[cur][(p * 4) * RROW + tl];
+      float sum = (rp[0] + rp[RROW]) + (rp[2 * RROW] + rp[3 * RROW]);
+      if (TPW <= 8) sum = sum_xor8(sum);
+      if (TPW <= 16) sum = sum_xor16(sum);
+      if (TPW <= 32) sum = sum_xor32(sum);
+      const int tok = t0 + tl;
+      if (p == 0 && tok < t_end) {
         sum *= out_scale;
         Sout[tok] = accumulate ? Sout[tok] + sum : sum;
       }
