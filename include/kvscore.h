@@ -74,7 +74,7 @@ typedef enum {
  *           +chunk).  chunk >= 1.
  *  budget   B: candidates kept per KV head.  n_keep = n_sink + min(B, n-n_sink-w) + w.
  *  eps      the renormalisation guard of Eq. 5 (>= 0).
- *  lambda_l weight of the lookahead term in Eq. 7.
+ *  lambda_l weight of the lookahead term in Eq. 7 (finite, >= 0).
  *  dtype    element type of Q, K, V and W_O.
  *
  * Scores use softmax(q.k / sqrt(d)) probabilities a, attention outputs
@@ -118,7 +118,8 @@ kvs_status kvscore_probs(const kvs_lore_desc *desc, const void *Q, const void *K
  *
  *  Q, K, V                  as for kvscore_probs.
  *  W_O      [d_model][h_q*d] the attention output projection (linear-layer layout).
- *  omega    [batch][m] fp32  trajectory reliability weights (Eq. 10 output).
+ *  omega    [batch][m] fp32  trajectory reliability weights (Eq. 10 output, a
+ *           softmax, so >= 0; an entry <= 0 gives its trajectory no weight).
  *  row_max, row_sum, O      kvscore_probs outputs for the same inputs.
  *  S        [batch][h_kv][n] fp32 out: the KV head's score of every token
  *           (protected tokens are scored too; selection ignores them).

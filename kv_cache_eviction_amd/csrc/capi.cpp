@@ -64,7 +64,8 @@ kvs_status check_lore(const kvs_lore_desc *d) {
   if (d->chunk < 1) return fail(KVS_ERR_INVALID, "chunk must be >= 1");
   if (d->n > (1 << 28)) return fail(KVS_ERR_UNSUPPORTED, "n above 2^28 tokens");
   if (!(std::isfinite(d->eps) && d->eps >= 0.f)) return fail(KVS_ERR_INVALID, "eps must be finite and >= 0");
-  if (!std::isfinite(d->lambda_l)) return fail(KVS_ERR_INVALID, "lambda_l must be finite");
+  if (!(std::isfinite(d->lambda_l) && d->lambda_l >= 0.f))
+    return fail(KVS_ERR_INVALID, "lambda_l must be finite and >= 0");
   if (d->dtype != KVS_F32 && d->dtype != KVS_BF16 && d->dtype != KVS_F16)
     return fail(KVS_ERR_INVALID, "unknown dtype");
   return ok();

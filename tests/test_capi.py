@@ -55,6 +55,7 @@ def _desc(kv, **kw):
     (dict(n=20), 1),                   # n < n_sink + w
     (dict(chunk=0), 1),
     (dict(eps=float("nan")), 1),
+    (dict(lambda_l=-0.5), 1),         # the lookahead weight is nonnegative
     (dict(budget=-1), 1),
 ])
 def test_bad_descriptor_rejected_before_launch(kw, status):
