@@ -351,46 +351,71 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
 
 // LORE: merge the splits of every scoring row into row_max (natural units of
 // q.k/sqrt(d)), row_sum and the normalised O.  One block per (query head,
-// 16-wide slice of d): thread (q = tid % 64, d-lane = tid / 64); the split
-// weights are computed once per block into LDS.
+// 4-wide slice of d), thread (q = tid % 64, d = slice + tid / 64).  A thread
+// first puts its column of partial O (one value per split) in flight, then
+// the four waves share the split weights: each takes every fourth split for
+// the row maximum and the weighted row sum, combined through LDS, so no
+// thread waits on a serial chain of loads.
 template <int D>
 __global__ void __launch_bounds__(256)
 attn_combine_lore_kernel(const float *__restrict__ pm, const float *__restrict__ pl,
                          const float *__restrict__ pO, int splits, int nq,
                          float *__restrict__ row_max, float *__restrict__ row_sum,
                          float *__restrict__ O) {
-  extern __shared__ float wsh[];  // [splits][64] split weights, then [64] 1/L
+  constexpr int CH = 32;           // partial-O values held in registers per pass
+  extern __shared__ float wsh[];   // [splits][64] split weights, [4][64] max, [4][64] sums
+  float *pmax = wsh + splits * 64, *psum = pmax + 256;
   const long head = blockIdx.x;
-  const int d0 = blockIdx.y * 16;
   const int q = threadIdx.x & 63, part = threadIdx.x >> 6;
+  const int d = blockIdx.y * 4 + part;
   const float *hm = pm + head * splits * 64;
   const float *hl = pl + head * splits * 64;
-  if (part == 0) {
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, hm[s * 64 + q]);
-    const float muse = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float wgt = exp2f(hm[s * 64 + q] - muse);
-      wsh[s * 64 + q] = wgt;
-      L += hl[s * 64 + q] * wgt;
-    }
-    wsh[splits * 64 + q] = 1.f / L;
-    if (q < nq && blockIdx.y == 0) {
-      row_max[head * nq + q] = M * kLn2;
-      row_sum[head * nq + q] = L;
-    }
-  }
-  __syncthreads();
-  const float inv = wsh[splits * 64 + q];
-  const float *ho = pO + head * splits * (long)D * 64;
+  const float *ho = pO + (head * splits * (long)D + d) * 64 + q;  // split stride D * 64
+  constexpr int SPT = 32;          // splits per thread in the weight phase (splits <= 128)
+  float ov[CH], mv[SPT], lv[SPT];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int d = d0 + part * 4 + u;
-    float o = 0.f;
-    for (int s = 0; s < splits; ++s) o += ho[((long)s * D + d) * 64 + q] * wsh[s * 64 + q];
-    if (q < nq) O[(head * nq + q) * D + d] = o * inv;
+  for (int u = 0; u < CH; ++u) ov[u] = u < splits ? ho[(long)u * D * 64] : 0.f;
+#pragma unroll
+  for (int u = 0; u < SPT; ++u) {
+    const int s = part + 4 * u;
+    mv[u] = s < splits ? hm[s * 64 + q] : -INFINITY;
+    lv[u] = s < splits ? hl[s * 64 + q] : 0.f;
   }
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < SPT; ++u) mloc = fmaxf(mloc, mv[u]);
+  pmax[part * 64 + q] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(pmax[q], pmax[64 + q]), fmaxf(pmax[128 + q], pmax[192 + q]));
+  const float muse = (M == -INFINITY) ? 0.f : M;
+  float lloc = 0.f;
+#pragma unroll
+  for (int u = 0; u < SPT; ++u) {
+    const int s = part + 4 * u;
+    if (s < splits) {
+      const float wgt = exp2f(mv[u] - muse);
+      wsh[s * 64 + q] = wgt;
+      lloc += lv[u] * wgt;
+    }
+  }
+  psum[part * 64 + q] = lloc;
+  __syncthreads();
+  const float L = (psum[q] + psum[64 + q]) + (psum[128 + q] + psum[192 + q]);
+  if (part == 0 && q < nq && blockIdx.y == 0) {
+    row_max[head * nq + q] = M * kLn2;
+    row_sum[head * nq + q] = L;
+  }
+  float o = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += CH) {
+    if (s0 > 0) {
+#pragma unroll
+      for (int u = 0; u < CH; ++u) ov[u] = s0 + u < splits ? ho[(long)(s0 + u) * D * 64] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < CH; ++u)
+      if (s0 + u < splits) o += ov[u] * wsh[(s0 + u) * 64 + q];
+  }
+  if (q < nq) O[(head * nq + q) * D + d] = o * (1.f / L);
 }
 
 // H2O prefill: merge the splits into per-row constants for the column-sum
@@ -494,14 +519,14 @@ hipError_t launch_attn_partial(int etype, int d, bool with_o, const void *Q, con
 hipError_t launch_attn_combine_lore(int d, const float *part_m, const float *part_l,
                                     const float *part_O, int heads, int splits, int nq,
                                     float *row_max, float *row_sum, float *O, hipStream_t st) {
-  const size_t shm = sizeof(float) * 64 * ((size_t)splits + 1);
+  const size_t shm = sizeof(float) * 64 * ((size_t)splits + 8);
   {
     TimedLaunch tl_("attn_combine", st);
     if (d == 64)
-      hipLaunchKernelGGL(attn_combine_lore_kernel<64>, dim3(heads, 64 / 16), dim3(256), shm, st,
+      hipLaunchKernelGGL(attn_combine_lore_kernel<64>, dim3(heads, 64 / 4), dim3(256), shm, st,
                          part_m, part_l, part_O, splits, nq, row_max, row_sum, O);
     else
-      hipLaunchKernelGGL(attn_combine_lore_kernel<128>, dim3(heads, 128 / 16), dim3(256), shm, st,
+      hipLaunchKernelGGL(attn_combine_lore_kernel<128>, dim3(heads, 128 / 4), dim3(256), shm, st,
                          part_m, part_l, part_O, splits, nq, row_max, row_sum, O);
   }
   return hipGetLastError();

@@ -31,22 +31,28 @@ namespace kvs {
 
 // ---------------------------------------------------------------------------
 // G_h = W_h^T W_h, one range of d_model rows per block.  W_h is the column
-// slice h*D .. h*D+D-1 of W_O [d_model][h_q*D].  32-row slabs are staged
-// transposed in LDS so both MFMA operands are 16-byte reads; the next slab's
-// loads are in flight while the current one is multiplied.
+// slice h*D .. h*D+D-1 of W_O [d_model][h_q*D].  Stages of SR rows (128 for
+// 16-bit inputs: four MFMA k-steps) are staged transposed in LDS so both MFMA
+// operands are 16-byte reads; the next stage's loads are in flight while the
+// current one is multiplied.
+template <typename Tin> struct GramStage { static constexpr int rows = sizeof(Tin) == 2 ? 128 : 32; };
+
 template <typename Tin, int D>
 __global__ void __launch_bounds__(256)
 gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
             float *__restrict__ Gpart) {
   typedef typename FragOf<Tin>::type FW;
+  constexpr int SR = GramStage<Tin>::rows;
+  constexpr int KSTEP = SR / 32;
   constexpr int EPC = 16 / (int)sizeof(Tin);
   constexpr int CPR = D / EPC;
-  constexpr int WROW = 32 + EPC;
+  constexpr int WROW = SR + EPC;
   constexpr int DB = D / 16;
   constexpr int RPW = (DB + 3) / 4;  // row blocks per wave
   constexpr bool P16 = sizeof(Tin) == 2;
   // staging items: 16-bit -> (row pair, chunk), fp32 -> (row, chunk)
-  constexpr int ITEMS = P16 ? 16 * CPR : 32 * CPR;
+  constexpr int RI = P16 ? SR / 2 : SR;
+  constexpr int ITEMS = RI * CPR;
   constexpr int PFG = (ITEMS + 255) / 256;
   __shared__ __align__(16) Tin Wt[2][D * WROW];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -55,7 +61,7 @@ gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
   const long ld = (long)h_q * D;
   const int k_begin = s * rows_per_split;
   const int k_end = min(dm, k_begin + rows_per_split);
-  const int nslab = (k_end - k_begin + 31) / 32;
+  const int nslab = (k_end - k_begin + SR - 1) / SR;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(
       W + (long)k_begin * ld + (long)h * D,
       (uint32_t)max(k_end - k_begin, 0) * (uint32_t)(ld * sizeof(Tin)));
@@ -66,14 +72,13 @@ gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
     for (int u = 0; u < PFG; ++u) {
       const int idx = threadIdx.x + u * 256;
       if (ITEMS % 256 != 0 && idx >= ITEMS) continue;
+      const int kr = idx % RI, ch = idx / RI;
       if constexpr (P16) {
-        const int kp = idx % 16, ch = idx / 16;
-        const uint32_t r0 = (uint32_t)(slab * 32 + 2 * kp);
+        const uint32_t r0 = (uint32_t)(slab * SR + 2 * kr);
         pw[u][0] = buf_load16(rw, (uint32_t)((r0 * ld + ch * EPC) * sizeof(Tin)));
         pw[u][P16 ? 1 : 0] = buf_load16(rw, (uint32_t)(((r0 + 1) * ld + ch * EPC) * sizeof(Tin)));
       } else {
-        const int r = idx % 32, ch = idx / 32;
-        pw[u][0] = buf_load16(rw, (uint32_t)(((uint32_t)(slab * 32 + r) * ld + ch * EPC) * sizeof(Tin)));
+        pw[u][0] = buf_load16(rw, (uint32_t)(((uint32_t)(slab * SR + kr) * ld + ch * EPC) * sizeof(Tin)));
       }
     }
   };
@@ -82,19 +87,18 @@ gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
     for (int u = 0; u < PFG; ++u) {
       const int idx = threadIdx.x + u * 256;
       if (ITEMS % 256 != 0 && idx >= ITEMS) continue;
+      const int kr = idx % RI, ch = idx / RI;
       if constexpr (P16) {
-        const int kp = idx % 16, ch = idx / 16;
         const Tin *ae = reinterpret_cast<const Tin *>(&pw[u][0]);
         const Tin *be = reinterpret_cast<const Tin *>(&pw[u][P16 ? 1 : 0]);
 #pragma unroll
         for (int e = 0; e < EPC; ++e)
-          *reinterpret_cast<uint32_t *>(&Wt[buf][(ch * EPC + e) * WROW + 2 * kp]) =
+          *reinterpret_cast<uint32_t *>(&Wt[buf][(ch * EPC + e) * WROW + 2 * kr]) =
               bits16(ae[e]) | (bits16(be[e]) << 16);
       } else {
-        const int r = idx % 32, ch = idx / 32;
         const Tin *ae = reinterpret_cast<const Tin *>(&pw[u][0]);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) Wt[buf][(ch * EPC + e) * WROW + r] = ae[e];
+        for (int e = 0; e < EPC; ++e) Wt[buf][(ch * EPC + e) * WROW + kr] = ae[e];
       }
     }
   };
@@ -111,18 +115,21 @@ gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
   for (int sl = 0; sl < nslab; ++sl) {
     const int cur = sl & 1;
     prefetch(sl + 1);  // past the range this reads zeros
-    FW af[RPW];
 #pragma unroll
-    for (int ri = 0; ri < RPW; ++ri) {
-      const int rb = wv + 4 * ri;
-      af[ri] = rb < DB ? load8<Tin>(&Wt[cur][(rb * 16 + col) * WROW + 8 * grp]) : zero8<Tin>();
-    }
+    for (int ks = 0; ks < KSTEP; ++ks) {
+      FW af[RPW];
 #pragma unroll
-    for (int cb = 0; cb < DB; ++cb) {
-      const FW bfr = load8<Tin>(&Wt[cur][(cb * 16 + col) * WROW + 8 * grp]);
+      for (int ri = 0; ri < RPW; ++ri) {
+        const int rb = wv + 4 * ri;
+        af[ri] = rb < DB ? load8<Tin>(&Wt[cur][(rb * 16 + col) * WROW + ks * 32 + 8 * grp]) : zero8<Tin>();
+      }
 #pragma unroll
-      for (int ri = 0; ri < RPW; ++ri)
-        if (cb >= wv + 4 * ri) acc[ri][cb] = mma(af[ri], bfr, acc[ri][cb]);
+      for (int cb = 0; cb < DB; ++cb) {
+        const FW bfr = load8<Tin>(&Wt[cur][(cb * 16 + col) * WROW + ks * 32 + 8 * grp]);
+#pragma unroll
+        for (int ri = 0; ri < RPW; ++ri)
+          if (cb >= wv + 4 * ri) acc[ri][cb] = mma(af[ri], bfr, acc[ri][cb]);
+      }
     }
     stash(cur ^ 1);
     __syncthreads();
@@ -162,32 +169,69 @@ int gram_splits(int h_q, int d_model) {
 // to the attention output (where the three terms nearly cancel) keep their
 // relative accuracy.
 template <int D, typename TV>
-__global__ void __launch_bounds__(D)
+__global__ void __launch_bounds__(256)
 gram_reduce_kernel(const float *__restrict__ Gpart, int gsplits, int h_q, TV *__restrict__ Gv,
                    float *__restrict__ Gr) {
-  // block (row i, head h); thread j >= i sums entry (i, j) over the splits in
-  // a fixed order and writes it to (i, j) and (j, i): G~ is exactly symmetric
-  const int i = blockIdx.x, h = blockIdx.y, j = threadIdx.x;
-  if (j < i) return;
+  // block (32 x 32 tile (I, J) with I <= J, head h).  Thread (row ti, 4
+  // columns) sums the entries with j >= i over the splits in a fixed order;
+  // the tile is written in place and, through LDS, transposed to (J, I), so
+  // G~ is exactly symmetric and every global access is a 16-byte row chunk.
+  constexpr int NT = D / 32;
+  __shared__ float T[32][33];
+  int I = 0, rem = blockIdx.x;
+  while (rem >= NT - I) { rem -= NT - I; ++I; }
+  const int J = I + rem;
+  const int h = blockIdx.y;
+  const int ti = threadIdx.x >> 3, tj = (threadIdx.x & 7) * 4;
   const long total = (long)h_q * D * D;
-  const long idx = ((long)h * D + i) * D + j;
-  float g = 0.f;
-  int s = 0;
-  for (; s + 4 <= gsplits; s += 4) {
-    const float a0 = Gpart[(long)s * total + idx], a1 = Gpart[(long)(s + 1) * total + idx];
-    const float a2 = Gpart[(long)(s + 2) * total + idx], a3 = Gpart[(long)(s + 3) * total + idx];
-    g += a0;
-    g += a1;
-    g += a2;
-    g += a3;
+  const int i = 32 * I + ti, j0 = 32 * J + tj;
+  const long idx = ((long)h * D + i) * D + j0;
+  float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (j0 + 3 >= i) {  // some entry of the chunk is on or above the diagonal
+    int s = 0;
+    for (; s + 4 <= gsplits; s += 4) {
+      const float4 a0 = *reinterpret_cast<const float4 *>(Gpart + (long)s * total + idx);
+      const float4 a1 = *reinterpret_cast<const float4 *>(Gpart + (long)(s + 1) * total + idx);
+      const float4 a2 = *reinterpret_cast<const float4 *>(Gpart + (long)(s + 2) * total + idx);
+      const float4 a3 = *reinterpret_cast<const float4 *>(Gpart + (long)(s + 3) * total + idx);
+      g.x += a0.x; g.y += a0.y; g.z += a0.z; g.w += a0.w;
+      g.x += a1.x; g.y += a1.y; g.z += a1.z; g.w += a1.w;
+      g.x += a2.x; g.y += a2.y; g.z += a2.z; g.w += a2.w;
+      g.x += a3.x; g.y += a3.y; g.z += a3.z; g.w += a3.w;
+    }
+    for (; s < gsplits; ++s) {
+      const float4 a = *reinterpret_cast<const float4 *>(Gpart + (long)s * total + idx);
+      g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
+    }
   }
-  for (; s < gsplits; ++s) g += Gpart[(long)s * total + idx];
-  const TV gr = from_f32<TV>(g);
-  const long tdx = ((long)h * D + j) * D + i;
-  Gv[idx] = gr;
-  Gr[idx] = to_f32(gr);
-  Gv[tdx] = gr;
-  Gr[tdx] = to_f32(gr);
+  float gv[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    gv[e] = to_f32(from_f32<TV>(gv[e]));
+    T[ti][tj + e] = gv[e];
+  }
+  // direct write: entries with j >= i (all of them off the diagonal tile)
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (j0 + e >= i) {
+      Gv[idx + e] = from_f32<TV>(gv[e]);
+      Gr[idx + e] = gv[e];
+    }
+  __syncthreads();
+  // transposed write: entry (32J + ti, 32I + tj + e) = tile (tj + e, ti),
+  // taken where that tile entry is above the diagonal (the rest is written
+  // directly on a diagonal tile)
+  const int r = 32 * J + ti;
+  const long tdx = ((long)h * D + r) * D + 32 * I + tj;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int c = 32 * I + tj + e;
+    if (r > c) {
+      const float v = T[tj + e][ti];
+      Gv[tdx + e] = from_f32<TV>(v);
+      Gr[tdx + e] = v;
+    }
+  }
 }
 
 // Per (query head, sequence, 16-row group): y_q = G~ o_q (stored as a hi + lo
@@ -239,6 +283,114 @@ prep_kernel(const float *__restrict__ Gr, const float *__restrict__ O,
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) pi += __shfl_xor(pi, o, 64);
   if (sub == 0) {
+    float beta2 = 0.f, wr = 0.f;
+    int last = -1;
+    if (r < nq) {
+      beta2 = row_max[hb * nq + r] * kLog2e + log2f(row_sum[hb * nq + r]);
+      if (r < w) {
+        wr = 1.f / (float)w;
+        last = n - w + r;
+      } else {
+        wr = lambda_l * omega[(long)b * m + (r - w) / t] / (float)t;
+        last = n - 1;
+      }
+    }
+    consts[hb * 64 + r] = make_float4(beta2, pi, wr, __int_as_float(last));
+  }
+}
+
+// The same outputs for 16-bit value types, on the matrix cores.  One block
+// per (query head, sequence); wave w takes rows 16w..16w+15.  G~ is exact in
+// fp16, so y = G~ o is formed as G~ o_hi + G~ o_lo with o scaled per row by a
+// power of two (largest |o| in [2^14, 2^15)) and split into fp16 hi + lo
+// parts: the products are exact and the sum is an fp32 accumulation, as in
+// a plain fp32 dot product.  G~ is symmetric, so its rows serve as the
+// columns of the B operand.
+template <int D>
+__global__ void __launch_bounds__(256)
+prep_mfma_kernel(const f16 *__restrict__ Gv, const float *__restrict__ O,
+                 const float *__restrict__ row_max, const float *__restrict__ row_sum,
+                 const float *__restrict__ omega, int h_q, int n, int nq, int w, int m, int t,
+                 float lambda_l, f16 *__restrict__ Yhi, f16 *__restrict__ Ylo,
+                 float4 *__restrict__ consts) {
+  constexpr int KS = D / 32, NB = D / 16;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const long hb = (long)b * h_q + h;
+  const f16 *G = Gv + (long)h * D * D;
+  // A operand: lane (col, grp) holds o[16w + col][32 ks + 8 grp + e]
+  const int ra = wv * 16 + col;
+  float oa[KS][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const float4 *src = reinterpret_cast<const float4 *>(O + (hb * nq + ra) * D + ks * 32 + 8 * grp);
+    const float4 v0 = ra < nq ? src[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 v1 = ra < nq ? src[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+    oa[ks][0] = v0.x; oa[ks][1] = v0.y; oa[ks][2] = v0.z; oa[ks][3] = v0.w;
+    oa[ks][4] = v1.x; oa[ks][5] = v1.y; oa[ks][6] = v1.z; oa[ks][7] = v1.w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(oa[ks][e]));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+  // power-of-two row scale: exponent of amax -> 14
+  const int ex = amax > 0.f ? max(((__float_as_int(amax) >> 23) & 0xFF) - 127, -100) : 14;
+  const float sc = ldexpf(1.f, 14 - ex), unsc = ldexpf(1.f, ex - 14);
+  f16x8 ahi[KS], alo[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = oa[ks][e] * sc;
+      const f16 hi = (f16)v;
+      ahi[ks][e] = hi;
+      alo[ks][e] = (f16)(v - (float)hi);
+    }
+  // output rows 16w + 4 grp + j: their unscale factors live in lanes 4 grp + j
+  float unr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) unr[j] = __shfl(unsc, 4 * grp + j, 64);
+  // every G~ fragment and every o element the pi sums need are requested up
+  // front, so the block waits for one round of loads rather than one per
+  // column block
+  f16x8 bfa[NB][KS];
+  float oc[NB][4];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bfa[nb][ks] = load8<f16>(G + (nb * 16 + col) * D + ks * 32 + 8 * grp);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wv * 16 + 4 * grp + j;
+      oc[nb][j] = r < nq ? O[(hb * nq + r) * D + nb * 16 + col] : 0.f;
+    }
+  }
+  float pij[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const f16x8 (&bf)[KS] = bfa[nb];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) acc = mma(ahi[ks], bf[ks], acc);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) acc = mma(alo[ks], bf[ks], acc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wv * 16 + 4 * grp + j, c = nb * 16 + col;
+      const float y = r < nq ? acc[j] * unr[j] : 0.f;
+      const f16 hi = (f16)y;
+      Yhi[(hb * 64 + r) * D + c] = hi;
+      Ylo[(hb * 64 + r) * D + c] = (f16)(y - (float)hi);
+      pij[j] = fmaf(oc[nb][j], y, pij[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pij[j] = row16_sum(pij[j]);
+  if (col < 4) {
+    const int r = wv * 16 + 4 * grp + col;
+    const float pi = col == 0 ? pij[0] : col == 1 ? pij[1] : col == 2 ? pij[2] : pij[3];
     float beta2 = 0.f, wr = 0.f;
     int last = -1;
     if (r < nq) {
@@ -687,8 +839,9 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
 template <typename Tin, int D>
 static hipError_t run_gram(const void *W, int dm, int h_q, int splits, float *Gpart,
                            hipStream_t st) {
-  const int slabs = (dm + 31) / 32;
-  const int rps = (slabs + splits - 1) / splits * 32;
+  constexpr int SR = GramStage<Tin>::rows;
+  const int slabs = (dm + SR - 1) / SR;
+  const int rps = (slabs + splits - 1) / splits * SR;
   {
     TimedLaunch tl_("gram", st);
     hipLaunchKernelGGL((gram_kernel<Tin, D>), dim3(splits, h_q), dim3(256), 0, st, (const Tin *)W,
@@ -714,16 +867,22 @@ static hipError_t run_prep(const float *Gpart, int gsplits, const float *O, cons
                            void *Yhi, void *Ylo, float4 *consts, hipStream_t st) {
   {
     TimedLaunch tl_("gram_reduce", st);
-    hipLaunchKernelGGL((gram_reduce_kernel<D, TV>), dim3(D, h_q), dim3(D), 0, st, Gpart, gsplits,
-                       h_q, (TV *)Gv, Gr);
+    constexpr int NT = D / 32;
+    hipLaunchKernelGGL((gram_reduce_kernel<D, TV>), dim3(NT * (NT + 1) / 2, h_q), dim3(256), 0, st,
+                       Gpart, gsplits, h_q, (TV *)Gv, Gr);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     TimedLaunch tl_("deletion_prep", st);
-    hipLaunchKernelGGL((prep_kernel<D, TV>), dim3(h_q, batch, 4), dim3(256), 0, st, Gr, O,
-                       row_max, row_sum, omega, h_q, n, nq, w, m, t, lambda_l, (TV *)Yhi,
-                       (TV *)Ylo, consts);
+    if constexpr (sizeof(TV) == 2)
+      hipLaunchKernelGGL((prep_mfma_kernel<D>), dim3(h_q, batch), dim3(256), 0, st,
+                         (const f16 *)Gv, O, row_max, row_sum, omega, h_q, n, nq, w, m, t,
+                         lambda_l, (f16 *)Yhi, (f16 *)Ylo, consts);
+    else
+      hipLaunchKernelGGL((prep_kernel<D, TV>), dim3(h_q, batch, 4), dim3(256), 0, st, Gr, O,
+                         row_max, row_sum, omega, h_q, n, nq, w, m, t, lambda_l, (TV *)Yhi,
+                         (TV *)Ylo, consts);
   }
   return hipGetLastError();
 }
