@@ -21,6 +21,8 @@
 // of a B fragment, so P^T enters the P.V product straight from registers.
 // V is staged transposed (and converted to fp16 for 16-bit inputs) so the A
 // fragment of O^T = V^T P^T is one 16-byte LDS read.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "timing.hpp"
@@ -196,8 +198,12 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
           const Tin *be = reinterpret_cast<const Tin *>(&pv[u][V16 ? 1 : 0]);
 #pragma unroll
           for (int e = 0; e < EPC; ++e) {
-            const uint32_t packed = bits16(from_f32<TV>(to_f32(ae[e]))) |
-                                    (bits16(from_f32<TV>(to_f32(be[e]))) << 16);
+            uint32_t packed;
+            if constexpr (__is_same(Tin, bf16) && __is_same(TV, f16))
+              // exact in the fp16 normal range: round-toward-zero changes nothing there
+              packed = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(to_f32(ae[e]), to_f32(be[e])));
+            else
+              packed = bits16(from_f32<TV>(to_f32(ae[e]))) | (bits16(from_f32<TV>(to_f32(be[e]))) << 16);
             *reinterpret_cast<uint32_t *>(&Vt[buf][(ch * EPC + e) * VROW + 2 * kp]) = packed;
           }
         } else {
@@ -218,7 +224,9 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
     const int t0 = t_begin + it * TN;
     const int cur = it & 1;
     prefetch(t0 + TN);  // past the split end this reads nothing
-    if (t0 <= wave_last) {
+    // a tile's causal masking is compiled only into the tiles that need it
+    auto tile = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
       // S^T for the tile: block tb holds tokens (tb/2)*32 + 8*(row/4) + 4*(tb%2) + row%4.
       // LDS fragments are read one step ahead of the products that use them.
       auto load_k = [&](int tb, FQ (&kf)[KS]) {
@@ -250,7 +258,7 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
         }
       }
       // Lane (col, grp) holds tokens t0 + (tb/2)*32 + 8*grp + 4*(tb%2) + j.
-      if (t0 + TN - 1 > wave_first) {
+      if constexpr (MASKED) {
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
@@ -277,8 +285,7 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
         for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
           for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sacc[tb][qb][j]);
-        mx = wave_max_xor(mx, 16);
-        mx = wave_max_xor(mx, 32);
+        mx = group4_max(mx);
         const float mxs = mx * c;
         mtop[qb] = fmaxf(mtop[qb], mxs);
         if (__any(mxs > mref[qb] + kSlack)) {
@@ -318,6 +325,10 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
             oacc[db % (WITH_O ? DB : 1)][qb] = mma(vf, pf[h][qb], oacc[db % (WITH_O ? DB : 1)][qb]);
         }
       }
+    };
+    if (t0 <= wave_last) {
+      if (t0 + TN - 1 > wave_first) tile(std::true_type{});
+      else tile(std::false_type{});
     }
     stash(cur ^ 1);
     __syncthreads();
@@ -331,8 +342,7 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
     // bring (l, O) from the reference max to the exact max
     const float fix = (mtop[qb] == -INFINITY) ? 1.f : hw_exp2(mref[qb] - mtop[qb]);
     float l = lsum[qb] * fix;
-    l = wave_sum_xor(l, 16);
-    l = wave_sum_xor(l, 32);
+    l = group4_sum(l);
     const int r = (qb0 + qb) * 16 + col;
     if (grp == 0) {
       pm[pbase + r] = mtop[qb];

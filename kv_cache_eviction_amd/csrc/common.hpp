@@ -212,6 +212,12 @@ __device__ __forceinline__ float sum_xor16(float v) {
 }
 // sum over the four 16-lane groups: lanes l, l^16, l^32, l^48
 __device__ __forceinline__ float group4_sum(float v) { return sum_xor16(sum_xor32(v)); }
+__device__ __forceinline__ float group4_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
 
 // Sum over the 16 lanes of each DPP row (lanes 16r..16r+15); every lane of the
 // row receives the total.  quad_perm [1,0,3,2] and [2,3,0,1] sum each quad,

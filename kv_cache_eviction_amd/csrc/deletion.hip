@@ -773,7 +773,26 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
     }
     return tacc;
   };
-  auto tile = [&](auto masked, int cur, int t0) {
+  // Every wave sums the partials of TN / MAXW tokens of a finished tile: lane
+  // (token u, wave part p) adds the four row groups of wave p, then the MAXW
+  // parts of a token are added across lanes (u + TPW * p, p = 0..MAXW-1).
+  constexpr int TPW = TN / MAXW;
+  auto reduce_load = [&](int buf) -> float {
+    const int u = lane % TPW, p = lane / TPW;
+    const float *rp = &red[buf][(p * 4) * RROW + wv * TPW + u];
+    return (rp[0] + rp[RROW]) + (rp[2 * RROW] + rp[3 * RROW]);
+  };
+  auto reduce_store = [&](float sum, int t0p) {
+    if (TPW <= 8) sum = sum_xor8(sum);
+    if (TPW <= 16) sum = sum_xor16(sum);
+    if (TPW <= 32) sum = sum_xor32(sum);
+    const int tok = t0p + wv * TPW + lane % TPW;
+    if (lane < TPW && tok < t_end) {
+      sum *= out_scale;
+      Sout[tok] = accumulate ? Sout[tok] + sum : sum;
+    }
+  };
+  auto tile = [&](auto masked, int cur, int t0, bool pending, float part) {
     FQ kb[2][KS];
     FV vb[2][MODE == 0 ? KS : 1];
     float nv[TN / 16];
@@ -786,6 +805,7 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
       sched_fence();
       const float tsum = block(masked, t0 + tb * 16, nv[tb], kb[tb & 1], vb[tb & 1]);
       red[cur][(wv * 4 + grp) * RROW + tb * 16 + col] = tsum;
+      if (tb == 0 && pending) reduce_store(part, t0 - TN);
       // a wave further ahead in the tile yields issue priority to the wave
       // sharing its SIMD, so both reach the tile barrier together
       if (tb == 0) __builtin_amdgcn_s_setprio(2);
@@ -804,35 +824,22 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
     const int t0 = t_begin + it * TN;
     const int cur = it & 1;
     prefetch(t0 + TN);  // past the range this reads nothing
+    // the previous tile's sums are read now and finished after this tile's
+    // first block, so their LDS latency hides behind the products
+    const float part = it > 0 ? reduce_load(cur ^ 1) : 0.f;
     if (t0 > wave_last) {
 #pragma unroll
       for (int tb = 0; tb < TN / 16; ++tb) red[cur][(wv * 4 + grp) * RROW + tb * 16 + col] = 0.f;
+      if (it > 0) reduce_store(part, t0 - TN);
     } else if (t0 + TN - 1 > wave_first) {
-      tile(std::true_type{}, cur, t0);
+      tile(std::true_type{}, cur, t0, it > 0, part);
     } else {
-      tile(std::false_type{}, cur, t0);
+      tile(std::false_type{}, cur, t0, it > 0, part);
     }
     stash(cur ^ 1);
     __syncthreads();
-    // Every wave sums the partials of TN / MAXW tokens: lane (token u, wave
-    // part p) adds the four row groups of wave p, then the MAXW parts of a
-    // token are added across lanes (u + TPW * p, p = 0..MAXW-1).
-    {
-      constexpr int TPW = TN / MAXW;
-      const int u = lane % TPW, p = lane / TPW;
-      const int tl = wv * TPW + u;
-      const float *rp = &red[cur][(p * 4) * RROW + tl];
-      float sum = (rp[0] + rp[RROW]) + (rp[2 * RROW] + rp[3 * RROW]);
-      if (TPW <= 8) sum = sum_xor8(sum);
-      if (TPW <= 16) sum = sum_xor16(sum);
-      if (TPW <= 32) sum = sum_xor32(sum);
-      const int tok = t0 + tl;
-      if (p == 0 && tok < t_end) {
-        sum *= out_scale;
-        Sout[tok] = accumulate ? Sout[tok] + sum : sum;
-      }
-    }
   }
+  if (nt > 0) reduce_store(reduce_load((nt - 1) & 1), t_begin + (nt - 1) * TN);
 }
 
 // ---------------------------------------------------------------------------
