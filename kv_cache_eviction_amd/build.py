@@ -30,6 +30,9 @@ def _hipcc():
 def _flags():
     return ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "--offload-arch=" + ARCH,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results in VGPRs: the epilogues read them with ordinary VALU
+            # operands instead of one accvgpr read per element
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wno-unused-command-line-argument"]
 
 
