@@ -226,6 +226,25 @@ template <int CTRL> __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
                                                                CTRL, 0xF, 0xF, false));
 }
+// Inclusive prefix sum over the 64 lanes on the DPP network (every lane
+// active): row_shr 1, 2, 4, 8 scan each 16-lane row, row_bcast 15 and 31
+// carry the row totals into the rows above.
+template <int CTRL> __device__ __forceinline__ int dpp_shr_i32(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL, int ROWS> __device__ __forceinline__ int dpp_bcast_i32(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_shr_i32<0x111>(x);
+  x += dpp_shr_i32<0x112>(x);
+  x += dpp_shr_i32<0x114>(x);
+  x += dpp_shr_i32<0x118>(x);
+  x += dpp_bcast_i32<0x142, 0xA>(x);
+  x += dpp_bcast_i32<0x143, 0xC>(x);
+  return x;
+}
+
 // v[l] + v[l ^ 8] within each 16-lane row (row_ror:8 pairs lane i with i +- 8)
 __device__ __forceinline__ float sum_xor8(float v) { return v + dpp_f32<0x128>(v); }
 __device__ __forceinline__ float row16_sum(float v) {

@@ -10,7 +10,7 @@
 // ranking chunks weighted by their candidate count.  Each chunk's mean becomes
 // an order-preserving 32-bit key.  Selection runs in two levels so a row is
 // spread over many workgroups: every segment of kSeg chunks keeps the chunks
-// whose key reaches its own top-B threshold (a superset of the row's
+// whose key reaches the 16-bit bin of its own top-B threshold (a superset of the row's
 // selection within that segment), then one workgroup per row runs a 4-pass
 // 8-bit radix select with token-count weights over the surviving candidates
 // to find the threshold key tau and how many tokens of the tau-chunks are
@@ -33,12 +33,7 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 __device__ int block_exclusive_scan(int v, int *sh, int *total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) sh[wid] = x;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -92,13 +87,16 @@ topb_pool_kernel(const float *__restrict__ S, int n, int n_sink, int w, int chun
 // The caller guarantees the list holds at least rem tokens.  hist holds
 // nw * 256 ints (one histogram per wave: the high digits of nearby scores
 // collide, and one shared histogram would serialise every atomic on one bin).
+// With last_shift > 0 the select stops after the digit at last_shift: the
+// result is the threshold's high bits, and keys >= it form a superset.
 template <class KeyF, class CntF>
 __device__ uint32_t radix_threshold(int n_items, KeyF key, CntF cnt, int rem, int *hist,
-                                    uint32_t *s_prefix, int *s_rem, int *rem_out) {
+                                    uint32_t *s_prefix, int *s_rem, int *rem_out,
+                                    int last_shift = 0) {
   const int tid = threadIdx.x, bs = blockDim.x;
   const int wv = tid >> 6, nw = bs >> 6;
   uint32_t prefix = 0, mask = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int shift = 24; shift >= last_shift; shift -= 8) {
     for (int i = tid; i < nw * 256; i += bs) hist[i] = 0;
     __syncthreads();
     for (int i = tid; i < n_items; i += bs) {
@@ -121,12 +119,7 @@ __device__ uint32_t radix_threshold(int n_items, KeyF key, CntF cnt, int rem, in
         hb[j] = hist[255 - 4 * tid - j];
         ltot += hb[j];
       }
-      int incl = ltot;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (tid >= o) incl += y;
-      }
+      const int incl = wave_incl_scan(ltot);
       const int before = incl - ltot;  // tokens in bins above this lane's
       if (before < rem && incl >= rem) {
         int cum = before, sel = 0;
@@ -158,8 +151,8 @@ __device__ __forceinline__ int chunk_tokens(int cj, int chunk, int lo, int hi) {
 
 // Level 1: one workgroup of 256 threads per (segment of kSeg chunks, row);
 // thread t owns chunks 4t..4t+3 of the segment.  Keeps, in index order, the
-// chunks whose key is at least the segment's own top-B threshold (all of
-// them when the segment holds at most B tokens).
+// chunks whose key reaches the 16-bit bin of the segment's own top-B
+// threshold (all of them when the segment holds at most B tokens).
 constexpr int kSeg = 1024;
 
 __global__ void __launch_bounds__(256)
@@ -189,10 +182,12 @@ topb_local_kernel(const uint32_t *__restrict__ keys_ws, int n, int n_sink, int w
   uint32_t tau = 0;
   if (total > B) {
     int rem_unused;
+    // two 8-bit digits suffice here: every chunk at or above the 16-bit
+    // threshold bin is kept, a superset the final select narrows exactly
     tau = radix_threshold(
         items, [&](int i) { return seg_keys[i]; },
         [&](int i) { return chunk_tokens(c0 + i, chunk, lo, hi); }, B, hist, &s_prefix, &s_rem,
-        &rem_unused);
+        &rem_unused, 16);
   }
   int keep[4], nk = 0;
 #pragma unroll
@@ -223,6 +218,7 @@ topb_final_kernel(int n, int n_sink, int w, int chunk, int budget, int n_keep, i
   __shared__ int32_t c_idx[kCandLds];
   __shared__ int hist[16 * 256];
   __shared__ int scan_sh[17];
+  __shared__ int seg_at[1024], seg_cn[1024];
   __shared__ uint32_t s_prefix;
   __shared__ int s_rem;
   const int tid = threadIdx.x, bs = blockDim.x;
@@ -238,22 +234,32 @@ topb_final_kernel(int n, int n_sink, int w, int chunk, int budget, int n_keep, i
 
   const uint32_t *rk = keys_ws + row * nchunks;
   const int32_t *rc = cand + row * (long)nchunks;
-  // gather the segments' candidate lists in order
+  // gather the segments' candidate lists in order: a scan over the list
+  // lengths gives each segment's offset, then 32 threads per segment copy
+  // its list, so every load is one of a few independent rounds
   int total = 0;
   for (int base = 0; base < nseg; base += bs) {
     const int sg = base + tid;
     const int cn = sg < nseg ? cand_n[row * nseg + sg] : 0;
     int part;
     const int at = total + block_exclusive_scan(cn, scan_sh, &part);
-    if (sg < nseg && at + cn <= kCandLds)
-      for (int j = 0; j < cn; ++j) {
-        const int ci = rc[sg * kSeg + j];
-        c_idx[at + j] = ci;
-        c_key[at + j] = rk[ci];
+    seg_at[tid] = at;
+    seg_cn[tid] = cn;
+    __syncthreads();
+    const int nsg = min(bs, nseg - base);
+    for (int k = tid >> 5; k < nsg; k += bs >> 5) {
+      const int a0 = seg_at[k], c = seg_cn[k];
+      if (a0 + c > kCandLds) continue;
+      const int32_t *src = rc + (long)(base + k) * kSeg;
+      for (int j = tid & 31; j < c; j += 32) {
+        const int ci = src[j];
+        c_idx[a0 + j] = ci;
+        c_key[a0 + j] = rk[ci];
       }
+    }
+    __syncthreads();
     total += part;
   }
-  __syncthreads();
   const bool in_lds = total <= kCandLds;
   const int n_items = in_lds ? total : nchunks;
   auto idx_of = [&](int i) { return in_lds ? (int)c_idx[i] : i; };
@@ -270,14 +276,8 @@ topb_final_kernel(int n, int n_sink, int w, int chunk, int budget, int n_keep, i
   const int lane = tid & 63, wv = tid >> 6, nw = bs >> 6;
   const int per = ((n_items + nw - 1) / nw + 63) / 64 * 64;
   const int c_lo = min(n_items, wv * per), c_hi = min(n_items, c_lo + per);
-  auto wave_incl = [&](int x) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
-    return x;
-  };
+  auto wave_incl = [&](int x) { return wave_incl_scan(x); };
+  auto last_lane = [&](int x) { return __builtin_amdgcn_readlane(x, 63); };
   // pass 1: tau-tokens per wave
   int ties = 0;
   for (int base = c_lo; base < c_hi; base += 64) {
@@ -287,10 +287,10 @@ topb_final_kernel(int n, int n_sink, int w, int chunk, int budget, int n_keep, i
       if (cnt > 0 && key_of(it) == tau) ties += cnt;
     }
   }
-  ties = __shfl(wave_incl(ties), 63, 64);
+  ties = last_lane(wave_incl(ties));
   int tot;
   const int tie_before_wave = block_exclusive_scan(lane == 0 ? ties : 0, scan_sh, &tot);
-  const int tie_wave0 = __shfl(tie_before_wave, 0, 64);
+  const int tie_wave0 = __builtin_amdgcn_readlane(tie_before_wave, 0);
   // pass 2: selected tokens per wave
   int sel = 0, tie_run = tie_wave0;
   for (int base = c_lo; base < c_hi; base += 64) {
@@ -308,11 +308,11 @@ topb_final_kernel(int n, int n_sink, int w, int chunk, int budget, int n_keep, i
       if (key > tau) sel += cnt;
       else if (key == tau) sel += min(max(rem - tb, 0), cnt);
     }
-    tie_run += __shfl(tincl, 63, 64);
+    tie_run += last_lane(tincl);
   }
-  sel = __shfl(wave_incl(sel), 63, 64);
+  sel = last_lane(wave_incl(sel));
   const int out_before_wave = block_exclusive_scan(lane == 0 ? sel : 0, scan_sh, &tot);
-  int out_run = n_sink + __shfl(out_before_wave, 0, 64);
+  int out_run = n_sink + __builtin_amdgcn_readlane(out_before_wave, 0);
   // pass 3: write
   tie_run = tie_wave0;
   for (int base = c_lo; base < c_hi; base += 64) {
@@ -337,8 +337,8 @@ topb_final_kernel(int n, int n_sink, int w, int chunk, int budget, int n_keep, i
     int out = out_run + oincl - take;
     for (int i = a; i < a + take; ++i, ++out)
       if (out < n_sink + B) kr[out] = i;
-    out_run += __shfl(oincl, 63, 64);
-    tie_run += __shfl(tincl, 63, 64);
+    out_run += last_lane(oincl);
+    tie_run += last_lane(tincl);
   }
 }
 
