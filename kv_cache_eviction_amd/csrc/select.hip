@@ -52,34 +52,6 @@ __device__ int block_exclusive_scan(int v, int *sh, int *total) {
   return excl;
 }
 
-// Pooling: one thread per chunk.  keys[row][c] = order_key(mean of the
-// candidates in chunk c), 0 for chunks with no candidate; pooled (optional)
-// gets each candidate's pooled score and NaN for protected tokens.
-__global__ void __launch_bounds__(256)
-topb_pool_kernel(const float *__restrict__ S, int n, int n_sink, int w, int chunk, int nchunks,
-                 uint32_t *__restrict__ keys_ws, float *__restrict__ pooled) {
-  const long row = blockIdx.y;
-  const int cj = blockIdx.x * blockDim.x + threadIdx.x;
-  if (cj >= nchunks) return;
-  const int lo = n_sink, hi = n - w;
-  const float *Sr = S + row * n;
-  const int c0 = cj * chunk, c1 = min(c0 + chunk, n);
-  const int a = max(c0, lo), e = min(c1, hi);
-  uint32_t key = 0;
-  float P = 0.f;
-  if (e > a) {
-    float s = 0.f;
-    for (int i = a; i < e; ++i) s += Sr[i];
-    P = s / (float)(e - a);
-    key = order_key(P);
-  }
-  keys_ws[row * nchunks + cj] = key;
-  if (pooled) {
-    float *pr = pooled + row * n;
-    for (int i = c0; i < c1; ++i) pr[i] = (i >= lo && i < hi) ? P : __int_as_float(0x7FC00000);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Weighted radix select over a list of items (item i: key(i), tokens cnt(i)):
 // the largest key tau such that the items with key >= tau hold at least rem
@@ -150,15 +122,17 @@ __device__ __forceinline__ int chunk_tokens(int cj, int chunk, int lo, int hi) {
 }
 
 // Level 1: one workgroup of 256 threads per (segment of kSeg chunks, row);
-// thread t owns chunks 4t..4t+3 of the segment.  Keeps, in index order, the
-// chunks whose key reaches the 16-bit bin of the segment's own top-B
-// threshold (all of them when the segment holds at most B tokens).
+// thread t owns chunks 4t..4t+3 of the segment.  The workgroup pools its
+// chunks from S (keys for the final pass, pooled scores when asked for), then
+// keeps, in index order, the chunks whose key reaches the 16-bit bin of the
+// segment's own top-B threshold (all of them when the segment holds at most
+// B tokens).
 constexpr int kSeg = 1024;
 
 __global__ void __launch_bounds__(256)
-topb_local_kernel(const uint32_t *__restrict__ keys_ws, int n, int n_sink, int w, int chunk,
-                  int nchunks, int B, int nseg, int32_t *__restrict__ cand,
-                  int32_t *__restrict__ cand_n) {
+topb_local_kernel(const float *__restrict__ S, int n, int n_sink, int w, int chunk, int nchunks,
+                  int B, int nseg, uint32_t *__restrict__ keys_ws, float *__restrict__ pooled,
+                  int32_t *__restrict__ cand, int32_t *__restrict__ cand_n) {
   __shared__ int hist[4 * 256];
   __shared__ int scan_sh[5];
   __shared__ uint32_t s_prefix;
@@ -169,14 +143,35 @@ topb_local_kernel(const uint32_t *__restrict__ keys_ws, int n, int n_sink, int w
   const int lo = n_sink, hi = n - w;
   const int c0 = seg * kSeg;
   const int items = min(kSeg, nchunks - c0);
-  const uint32_t *gk = keys_ws + row * nchunks + c0;
-  for (int i = threadIdx.x; i < kSeg; i += blockDim.x) seg_keys[i] = i < items ? gk[i] : 0u;
+  const float *Sr = S + row * n;
+  // pooling: chunk c holds tokens [c*chunk, c*chunk + chunk); its key is the
+  // order key of the mean over its candidates (0 when it has none)
   int toks = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int i = 4 * threadIdx.x + k;
-    if (i < items) toks += max(chunk_tokens(c0 + i, chunk, lo, hi), 0);
+    uint32_t key = 0;
+    if (i < items) {
+      const int cj = c0 + i;
+      const int t0 = cj * chunk, t1 = min(t0 + chunk, n);
+      const int a = max(t0, lo), e = min(t1, hi);
+      float P = 0.f;
+      if (e > a) {
+        float sum = 0.f;
+        for (int t = a; t < e; ++t) sum += Sr[t];
+        P = sum / (float)(e - a);
+        key = order_key(P);
+        toks += e - a;
+      }
+      keys_ws[row * nchunks + cj] = key;
+      if (pooled) {
+        float *pr = pooled + row * n;
+        for (int t = t0; t < t1; ++t) pr[t] = (t >= lo && t < hi) ? P : __int_as_float(0x7FC00000);
+      }
+    }
+    seg_keys[i] = key;
   }
+  if (B <= 0) return;  // nothing to select: the pooled output was the only work
   int total;
   block_exclusive_scan(toks, scan_sh, &total);  // (also orders the seg_keys writes)
   uint32_t tau = 0;
@@ -360,18 +355,11 @@ hipError_t launch_topb(const float *S, int rows, int n, int n_sink, int w, int c
   const int n_cand = n - n_sink - w;
   const int B = budget < n_cand ? budget : n_cand;
   {
-    TimedLaunch tl_("topb_pool", st);
-    hipLaunchKernelGGL(topb_pool_kernel, dim3((nchunks + 255) / 256, rows), dim3(256), 0, st, S,
-                       n, n_sink, w, chunk, nchunks, keys_ws, pooled);
+    TimedLaunch tl_("topb_local", st);
+    hipLaunchKernelGGL(topb_local_kernel, dim3(nseg, rows), dim3(256), 0, st, S, n, n_sink, w,
+                       chunk, nchunks, B, nseg, keys_ws, pooled, cand, cand_n);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (B > 0) {
-    TimedLaunch tl_("topb_local", st);
-    hipLaunchKernelGGL(topb_local_kernel, dim3(nseg, rows), dim3(256), 0, st, keys_ws, n, n_sink,
-                       w, chunk, nchunks, B, nseg, cand, cand_n);
-  }
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     TimedLaunch tl_("topb_select", st);
