@@ -175,6 +175,14 @@ __device__ __forceinline__ U128 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t by
 __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0));
 }
+// A byte offset past every range: a load there reads zeros without a memory
+// access, a store there is dropped.
+constexpr uint32_t kNoLoad = 0xFFFFFFF0u;
+// A store past the resource's range is dropped by the same check, so lanes
+// that must not write pass kNoLoad instead of taking a branch.
+__device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)byte_off, 0, 0);
+}
 // A kernel's token range [t_begin, t_end) is covered by one resource built
 // once; tile t0 is addressed with the lane offset plus (t0 - t_begin) * row
 // bytes, and tiles past t_end read zeros without touching memory.  The range

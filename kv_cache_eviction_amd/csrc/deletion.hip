@@ -485,6 +485,7 @@ vnorm_kernel(const Tin *__restrict__ V, const typename ValueType<Tin>::type *__r
   // V has n rows; tokens n..n_pad-1 read as zeros (N = 0 there)
   const __amdgpu_buffer_rsrc_t rv =
       make_rsrc(Vg + (long)t_begin * D, range_bytes(t_begin, min(t_end, n), RB));
+  const __amdgpu_buffer_rsrc_t rn = make_rsrc(Nh + t_begin, range_bytes(t_begin, t_end, 4));
   auto prefetch = [&](int t0) {
     const uint32_t toff = (uint32_t)(t0 - t_begin) * RB;
 #pragma unroll
@@ -525,17 +526,20 @@ vnorm_kernel(const Tin *__restrict__ V, const typename ValueType<Tin>::type *__r
       sched_fence();
       const FV (&vf)[KS] = vb[k & 1];
       const int tok = t0 + tb * 16 + col;
-      float np = 0.f;
+      // four partial sums, one per accumulator row, keep the chains short
+      float npj[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = db >> 1; ks < KS; ++ks) acc = mma(gf[db][ks], vf[ks], acc);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) np += acc[j] * frag_elem(vf[db >> 1], 4 * (db & 1) + j);
+        for (int j = 0; j < 4; ++j) npj[j] += acc[j] * frag_elem(vf[db >> 1], 4 * (db & 1) + j);
       }
-      np = group4_sum(np);
-      if (grp == 0 && tok < t_end) Nh[tok] = np;
+      const float np = group4_sum((npj[0] + npj[1]) + (npj[2] + npj[3]));
+      // tiles end at or before t_end (a multiple of 64): the lanes of group 0
+      // store, the others are dropped by the range check
+      buf_store_f32(rn, grp == 0 ? (uint32_t)(tok - t_begin) * 4u : kNoLoad, np);
     }
   };
 

@@ -45,7 +45,6 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
   constexpr int LPR = D / EPC;  // lanes per slot row
   constexpr int RPI = 64 / LPR; // slot rows per wave step
   constexpr int U = 8;          // wave steps whose loads are in flight together
-  constexpr uint32_t kNoLoad = 0xFFFFFFF0u;  // offset past every range: reads 0, no access
   extern __shared__ float dsh[];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const long row = (long)blockIdx.x * 4 + wv;
