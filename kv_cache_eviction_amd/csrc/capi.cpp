@@ -86,7 +86,7 @@ LorePlan plan_lore(const kvs_lore_desc *d) {
   p.off_po = align_up(p.off_pl + heads * S * 64 * 4);
   p.probs_bytes = align_up(p.off_po + heads * S * D * 64 * 4);
 
-  p.gsplits = kvs::gram_splits(d->h_q, d->d_model);
+  p.gsplits = kvs::gram_splits(d->h_q, d->d_model, d->dtype == KVS_F32 ? 4 : 2);
   p.off_gpart = 0;
   p.off_gv = align_up(p.off_gpart + (size_t)p.gsplits * d->h_q * D * D * 4);
   p.off_gr = align_up(p.off_gv + (size_t)d->h_q * D * D * vbytes);

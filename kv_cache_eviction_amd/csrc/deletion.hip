@@ -33,9 +33,10 @@ namespace kvs {
 // G_h = W_h^T W_h, one range of d_model rows per block.  W_h is the column
 // slice h*D .. h*D+D-1 of W_O [d_model][h_q*D].  Stages of SR rows (128 for
 // 16-bit inputs: four MFMA k-steps) are staged transposed in LDS so both MFMA
-// operands are 16-byte reads; the next stage's loads are in flight while the
-// current one is multiplied.
+// operands are 16-byte reads.  A split holds at most kGramStages stages,
+// whose loads are all issued before the first is multiplied.
 template <typename Tin> struct GramStage { static constexpr int rows = sizeof(Tin) == 2 ? 128 : 32; };
+constexpr int kGramStages = 4;  // stages per split, all in flight at once
 
 template <typename Tin, int D>
 __global__ void __launch_bounds__(256)
@@ -55,7 +56,9 @@ gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
   constexpr int ITEMS = RI * CPR;
   constexpr int PFG = (ITEMS + 255) / 256;
   __shared__ __align__(16) Tin Wt[2][D * WROW];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // wave-uniform in a scalar register, so the per-wave block-triangle tests
+  // below are scalar branches, not exec masks
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int s = blockIdx.x, h = blockIdx.y;
   const long ld = (long)h_q * D;
@@ -66,8 +69,9 @@ gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
       W + (long)k_begin * ld + (long)h * D,
       (uint32_t)max(k_end - k_begin, 0) * (uint32_t)(ld * sizeof(Tin)));
 
-  U128 pw[PFG][P16 ? 2 : 1];
-  auto prefetch = [&](int slab) {
+  constexpr int NR = kGramStages;
+  U128 pw[NR][PFG][P16 ? 2 : 1];
+  auto prefetch = [&](int slab, U128 (&pw)[PFG][P16 ? 2 : 1]) {
 #pragma unroll
     for (int u = 0; u < PFG; ++u) {
       const int idx = threadIdx.x + u * 256;
@@ -82,7 +86,7 @@ gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
       }
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, const U128 (&pw)[PFG][P16 ? 2 : 1]) {
 #pragma unroll
     for (int u = 0; u < PFG; ++u) {
       const int idx = threadIdx.x + u * 256;
@@ -109,30 +113,53 @@ gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
 #pragma unroll
     for (int cb = 0; cb < DB; ++cb) acc[ri][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  prefetch(0);
-  stash(0);
-  __syncthreads();
-  for (int sl = 0; sl < nslab; ++sl) {
-    const int cur = sl & 1;
-    prefetch(sl + 1);  // past the range this reads zeros
+  // the blocks a wave forms depend on its index; each wave runs a copy of the
+  // loop specialised for it, so the block-triangle tests are resolved at
+  // compile time
+  auto compute_w = [&](auto wvc, int cur) {
+    constexpr int WV = decltype(wvc)::value;
 #pragma unroll
     for (int ks = 0; ks < KSTEP; ++ks) {
       FW af[RPW];
 #pragma unroll
       for (int ri = 0; ri < RPW; ++ri) {
-        const int rb = wv + 4 * ri;
+        const int rb = WV + 4 * ri;
         af[ri] = rb < DB ? load8<Tin>(&Wt[cur][(rb * 16 + col) * WROW + ks * 32 + 8 * grp]) : zero8<Tin>();
       }
 #pragma unroll
-      for (int cb = 0; cb < DB; ++cb) {
+      for (int cb = WV; cb < DB; ++cb) {
         const FW bfr = load8<Tin>(&Wt[cur][(cb * 16 + col) * WROW + ks * 32 + 8 * grp]);
 #pragma unroll
         for (int ri = 0; ri < RPW; ++ri)
-          if (cb >= wv + 4 * ri) acc[ri][cb] = mma(af[ri], bfr, acc[ri][cb]);
+          if (cb >= WV + 4 * ri) acc[ri][cb] = mma(af[ri], bfr, acc[ri][cb]);
       }
     }
-    stash(cur ^ 1);
+  };
+  auto compute = [&](int cur) {
+    switch (wv) {
+      case 0: compute_w(std::integral_constant<int, 0>{}, cur); break;
+      case 1: compute_w(std::integral_constant<int, 1>{}, cur); break;
+      case 2: compute_w(std::integral_constant<int, 2>{}, cur); break;
+      default: compute_w(std::integral_constant<int, 3>{}, cur); break;
+    }
+  };
+
+  // a split holds at most NR stages (gram_splits), all requested up front
+  // stages past the split read zeros; the fences keep the loads in stage
+  // order, so each stage waits only for its own
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    prefetch(r, pw[r]);
+    sched_fence();
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    if (r >= nslab) break;
+    // LDS buffer r % 2 was last read by stage r - 2, which every wave
+    // finished before the previous barrier
+    stash(r & 1, pw[r]);
     __syncthreads();
+    compute(r & 1);
   }
   // G is symmetric: only the 16x16 blocks on and above the diagonal are
   // formed and written (the reduction mirrors them).
@@ -150,10 +177,13 @@ gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
   }
 }
 
-int gram_splits(int h_q, int d_model) {
+int gram_splits(int h_q, int d_model, int elem_bytes) {
+  const int sr = elem_bytes == 2 ? GramStage<bf16>::rows : GramStage<float>::rows;
+  const int stages = (d_model + sr - 1) / sr;
   int splits = (256 + h_q - 1) / h_q;
-  const int slabs = (d_model + 31) / 32;
-  if (splits > slabs) splits = slabs;
+  const int need = (stages + kGramStages - 1) / kGramStages;  // at most kGramStages per split
+  if (splits < need) splits = need;
+  if (splits > stages) splits = stages;
   if (splits < 1) splits = 1;
   return splits;
 }
@@ -853,6 +883,7 @@ static hipError_t run_gram(const void *W, int dm, int h_q, int splits, float *Gp
   constexpr int SR = GramStage<Tin>::rows;
   const int slabs = (dm + SR - 1) / SR;
   const int rps = (slabs + splits - 1) / splits * SR;
+  if (rps > kGramStages * SR) return hipErrorInvalidValue;  // splits from gram_splits()
   {
     TimedLaunch tl_("gram", st);
     hipLaunchKernelGGL((gram_kernel<Tin, D>), dim3(splits, h_q), dim3(256), 0, st, (const Tin *)W,

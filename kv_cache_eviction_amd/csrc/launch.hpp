@@ -48,7 +48,7 @@ hipError_t launch_attn_combine_rows(const float *part_m, const float *part_l, in
                                     int splits, int group, int P, float4 *consts, hipStream_t st);
 
 // Deletion score pieces.
-int gram_splits(int h_q, int d_model);
+int gram_splits(int h_q, int d_model, int elem_bytes);
 hipError_t launch_gram(int etype, int d, const void *W_O, int d_model, int h_q, int splits,
                        float *Gpart, hipStream_t st);
 hipError_t launch_deletion_prep(int etype, int d, const float *Gpart, int gsplits, const float *O,
