@@ -76,7 +76,9 @@ gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
     for (int u = 0; u < PFG; ++u) {
       const int idx = threadIdx.x + u * 256;
       if (ITEMS % 256 != 0 && idx >= ITEMS) continue;
-      const int kr = idx % RI, ch = idx / RI;
+      // 16-bit: chunks of a row pair are adjacent lanes, so a wave reads whole
+      // 256-byte row slices; fp32: rows are adjacent lanes
+      const int kr = P16 ? idx / CPR : idx % RI, ch = P16 ? idx % CPR : idx / RI;
       if constexpr (P16) {
         const uint32_t r0 = (uint32_t)(slab * SR + 2 * kr);
         pw[u][0] = buf_load16(rw, (uint32_t)((r0 * ld + ch * EPC) * sizeof(Tin)));
@@ -91,13 +93,16 @@ gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
     for (int u = 0; u < PFG; ++u) {
       const int idx = threadIdx.x + u * 256;
       if (ITEMS % 256 != 0 && idx >= ITEMS) continue;
-      const int kr = idx % RI, ch = idx / RI;
+      const int kr = P16 ? idx / CPR : idx % RI, ch = P16 ? idx % CPR : idx / RI;
       if constexpr (P16) {
         const Tin *ae = reinterpret_cast<const Tin *>(&pw[u][0]);
         const Tin *be = reinterpret_cast<const Tin *>(&pw[u][P16 ? 1 : 0]);
+        // row pair kr lands at dword kr ^ 4*((row >> 3) & 7) of LDS row
+        // ch*8 + e: the 16 lanes of a row pair then hit distinct banks
+        const int kd = kr ^ (4 * (ch & 7));
 #pragma unroll
         for (int e = 0; e < EPC; ++e)
-          *reinterpret_cast<uint32_t *>(&Wt[buf][(ch * EPC + e) * WROW + 2 * kr]) =
+          *reinterpret_cast<uint32_t *>(&Wt[buf][(ch * EPC + e) * WROW + 2 * kd]) =
               bits16(ae[e]) | (bits16(be[e]) << 16);
       } else {
         const Tin *ae = reinterpret_cast<const Tin *>(&pw[u][0]);
@@ -120,15 +125,19 @@ gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
     constexpr int WV = decltype(wvc)::value;
 #pragma unroll
     for (int ks = 0; ks < KSTEP; ++ks) {
+      // k offset of the 8-element group, undoing the staging swizzle of row r
+      auto koff = [&](int r) { return P16 ? (ks * 32 + 8 * grp) ^ (8 * ((r >> 3) & 7)) : ks * 32 + 8 * grp; };
       FW af[RPW];
 #pragma unroll
       for (int ri = 0; ri < RPW; ++ri) {
         const int rb = WV + 4 * ri;
-        af[ri] = rb < DB ? load8<Tin>(&Wt[cur][(rb * 16 + col) * WROW + ks * 32 + 8 * grp]) : zero8<Tin>();
+        const int r = rb * 16 + col;
+        af[ri] = rb < DB ? load8<Tin>(&Wt[cur][r * WROW + koff(r)]) : zero8<Tin>();
       }
 #pragma unroll
       for (int cb = WV; cb < DB; ++cb) {
-        const FW bfr = load8<Tin>(&Wt[cur][(cb * 16 + col) * WROW + ks * 32 + 8 * grp]);
+        const int r = cb * 16 + col;
+        const FW bfr = load8<Tin>(&Wt[cur][r * WROW + koff(r)]);
 #pragma unroll
         for (int ri = 0; ri < RPW; ++ri)
           if (cb >= WV + 4 * ri) acc[ri][cb] = mma(af[ri], bfr, acc[ri][cb]);
