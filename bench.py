@@ -159,6 +159,10 @@ def bench_h2o(kv, torch, dev):
     kv.kvs_timing_enable(False)
     kv.kvs_timing_reset()
     dec = [ms for nm, ms in recs if nm == "h2o_decode"]
+    # the prefill's reduction ends with one compact of the kept prompt rows
+    pc = [ms for nm, ms in recs if nm == "compact"]
+    k_h, k_r = cache.budget(cfg.prompt)
+    pc_bytes = 2 * 2 * cfg.batch * cfg.heads * (k_h + k_r) * cfg.d * 2
     rows = cfg.batch * cfg.heads
     # bytes per step: K and V of the retained slots, acc read+write, slot map, q/k/v/O
     avg_slots = slots / cfg.steps
@@ -171,7 +175,51 @@ def bench_h2o(kv, torch, dev):
             "slots_attended_per_s": round(rows * slots / (e1.elapsed_time(e2) * 1e-3), 1),
             "roofline": {"kernel": "h2o_decode", "bound": "hbm", "achieved": round(hbm, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(hbm / PEAK_HBM_GBS, 4),
-                         "traffic": measured_traffic("h2o_decode")}}
+                         "traffic": measured_traffic("h2o_decode")},
+            "prefill_compact": {"kernel_ms": round(pc[0], 4), "bytes": pc_bytes,
+                                "achieved_gbs": round(pc_bytes / (pc[0] * 1e-3) / 1e9, 1),
+                                "frac": round(pc_bytes / (pc[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            if pc else None}
+
+
+def bench_compact_qwen(kv, torch, dev, reps=20):
+    """kv_compact on the Qwen2.5-14B batch shape (8 sequences x 8 KV heads of
+    32K tokens, bf16, keep 1 + 512 + 32 per head): the HBM-bound gather at a
+    size where it is not launch-bound.  K/V (1.07 GB) exceed the 256 MB MALL."""
+    from kvsynth import QWEN_14B_BATCH as cfg
+    b, hk, n, d = cfg.batch, cfg.h_kv, cfg.n, cfg.d
+    n_keep = 1 + cfg.budget + cfg.w
+    g = torch.Generator(device=dev)
+    g.manual_seed(4040)
+    K = torch.randn(b, hk, n, d, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    V = torch.randn(b, hk, n, d, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    rows = b * hk
+    mid = torch.rand(rows, n - 1 - cfg.w, generator=g, device=dev).argsort(dim=1)[:, :cfg.budget] + 1
+    tail = torch.arange(n - cfg.w, n, device=dev).expand(rows, cfg.w)
+    kept = torch.cat([torch.zeros(rows, 1, dtype=torch.long, device=dev), mid, tail], dim=1)
+    kept = kept.sort(dim=1).values.to(torch.int32).reshape(b, hk, n_keep).contiguous()
+    Ko = torch.empty(b, hk, n_keep, d, dtype=torch.bfloat16, device=dev)
+    Vo = torch.empty_like(Ko)
+    for _ in range(3):
+        kv.kv_compact(K, V, kept, Ko, Vo)
+    torch.cuda.synchronize()
+    kv.kvs_timing_reset()
+    kv.kvs_timing_enable(True)
+    for _ in range(reps):
+        kv.kv_compact(K, V, kept, Ko, Vo)
+    torch.cuda.synchronize()
+    recs = [ms for nm, ms in kv.kvs_timing_records() if nm == "compact"]
+    kv.kvs_timing_enable(False)
+    kv.kvs_timing_reset()
+    ms = sum(recs) / len(recs)
+    nbytes = 2 * 2 * rows * n_keep * d * 2  # read + write of the kept K and V rows
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del K, V
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name + "-compact", "kernel_ms": round(ms, 4), "bytes": nbytes,
+            "roofline": {"kernel": "compact", "bound": "hbm", "achieved": round(gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": None}}
 
 
 def main():
@@ -309,6 +357,8 @@ def main():
         del data
         torch.cuda.empty_cache()
         out["h2o"] = bench_h2o(kv, torch, dev)
+        print("[bench] compact on the Qwen batch shape", file=sys.stderr, flush=True)
+        out["compact_qwen"] = bench_compact_qwen(kv, torch, dev)
     print(json.dumps(out), flush=True)
 
 
