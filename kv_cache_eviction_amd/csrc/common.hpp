@@ -262,6 +262,16 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f32<0x140>(v);
   return v;
 }
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return v;
+}
+// sum / max over all 64 lanes, every lane receiving the result (all lanes active)
+__device__ __forceinline__ float wave_sum_dpp(float v) { return group4_sum(row16_sum(v)); }
+__device__ __forceinline__ float wave_max_dpp(float v) { return group4_max(row16_max(v)); }
 
 // Fast hardware transcendentals (about 1 ulp).
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

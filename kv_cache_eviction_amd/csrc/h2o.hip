@@ -29,6 +29,25 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Sum over each group of LPR consecutive lanes (LPR a power of two <= 64),
+// and over the lanes l, l + LPR, l + 2 LPR, ... : DPP within 16-lane rows,
+// permlane swaps across them, no LDS traffic.
+template <int LPR> __device__ __forceinline__ float lane_group_sum(float v) {
+  if (LPR >= 2) v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  if (LPR >= 4) v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  if (LPR >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror
+  if (LPR >= 16) v += dpp_f32<0x140>(v); // row_mirror
+  if (LPR >= 32) v = sum_xor16(v);
+  if (LPR >= 64) v = sum_xor32(v);
+  return v;
+}
+template <int LPR> __device__ __forceinline__ float across_groups_sum(float v) {
+  if (LPR <= 8) v = sum_xor8(v);
+  if (LPR <= 16) v = sum_xor16(v);
+  if (LPR <= 32) v = sum_xor32(v);
+  return v;
+}
+
 __device__ __forceinline__ uint32_t order_key_pos(float x) {
   const uint32_t u = __float_as_uint(x + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -118,8 +137,7 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
 #pragma unroll
         for (int e = 0; e < EPC; ++e) part += qv[e] * to_f32(ke[e]);
       }
-#pragma unroll
-      for (int o = 1; o < LPR; o <<= 1) part += __shfl_xor(part, o, 64);
+      part = lane_group_sum<LPR>(part);
       if (sub == 0 && inb) prob[s] = valid ? part * c : -INFINITY;
     }
   }
@@ -127,12 +145,10 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
 
   float mx = -INFINITY;
   for (int s = lane; s < cap; s += 64) mx = fmaxf(mx, prob[s]);
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  mx = wave_max_dpp(mx);
   float l = 0.f;
   for (int s = lane; s < cap; s += 64) l += hw_exp2(prob[s] - mx);
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o, 64);
+  l = wave_sum_dpp(l);
   const float inv = 1.f / l;
   for (int s = lane; s < cap; s += 64) {
     const bool valid = (s == ws) || pos_s[s] >= 0;
@@ -173,9 +189,7 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
       }
     }
 #pragma unroll
-    for (int e = 0; e < EPC; ++e)
-#pragma unroll
-      for (int o = LPR; o < 64; o <<= 1) ov[e] += __shfl_xor(ov[e], o, 64);
+    for (int e = 0; e < EPC; ++e) ov[e] = across_groups_sum<LPR>(ov[e]);
     if (rr == 0) {
       U128 out;
       T *oe = reinterpret_cast<T *>(&out);

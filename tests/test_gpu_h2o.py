@@ -111,7 +111,7 @@ def run_lockstep(cfg, dev, rows, steps, gen_device="cpu"):
     return ties
 
 
-@pytest.mark.parametrize("dtype,d", [("f16", 128), ("f32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,d", [("f16", 128), ("f32", 64), ("bf16", 128), ("f16", 64), ("f32", 128)])
 def test_small_lockstep(dev, dtype, d):
     cfg = OPT30B_H2O.with_(name="small", batch=2, heads=3, d=d, prompt=200, steps=60,
                            dtype=dtype, seed=31)
