@@ -349,6 +349,30 @@ def main():
         "kernels": kernels,
         "kernel_rooflines": others,
     }
+    # the prompt-side baseline scorer on the same layer: the window rows'
+    # attention summed per token (K read once; HBM-bound: 34 GFLOP of credited
+    # QK^T against 268 MB)
+    print("[bench] prompt-side window score", file=sys.stderr, flush=True)
+    x = data[0]
+    ev.baseline(kv.KVS_BASELINE_WINDOW, x["Q"], x["K"], x["V"])
+    torch.cuda.synchronize()
+    kv.kvs_timing_reset()
+    kv.kvs_timing_enable(True)
+    for _ in range(5):
+        kv.kvscore_baseline_scores(desc, kv.KVS_BASELINE_WINDOW, x["Q"], x["K"], ev.row_max,
+                                   ev.row_sum, ev.S, ev.ws)
+    torch.cuda.synchronize()
+    brec = kv.kvs_timing_records()
+    kv.kvs_timing_enable(False)
+    kv.kvs_timing_reset()
+    bms = sum(ms for _, ms in brec) / 5
+    kbytes = cfg.batch * cfg.h_kv * cfg.n * cfg.d * 2 + 4 * cfg.batch * cfg.h_kv * cfg.n
+    out["baseline_window"] = {
+        "kernels_ms": round(bms, 4), "launches_per_call": len(brec) // 5,
+        "roofline": {"kernel": "score_h2o_colsum", "bound": "hbm",
+                     "achieved": round(kbytes / (bms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(kbytes / (bms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": None}}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, data[0])

@@ -132,6 +132,31 @@ kvs_status kvscore_deletion(const kvs_lore_desc *desc, const void *Q, const void
                             const float *row_max, const float *row_sum, const float *O,
                             float *S, void *ws, size_t ws_bytes, void *stream);
 
+/* Which prompt-side baseline kvscore_baseline_scores computes. */
+typedef enum { KVS_BASELINE_WINDOW = 0, KVS_BASELINE_TOVA = 1 } kvs_baseline;
+
+/*
+ * Prompt-side attention scores of every cached token, per KV head, for the
+ * same selector: the baselines the LORE-KV page sets its score against
+ * ("The query-reference mismatch", "Prompt-side eviction": tokens ranked by
+ * how the last w prompt tokens attend to them), and the single-query form of
+ * the counter-causal review's background paragraph on TOVA ("Prerequisites":
+ * the most recent token's attention over the cache).  Lookahead rows are not
+ * read.
+ *
+ *  kind     KVS_BASELINE_WINDOW: S_i = mean over the KV head's query heads of
+ *           sum_{r<w} a_{r,i}.  KVS_BASELINE_TOVA: the same with the last
+ *           window row only (r = w - 1, the last prompt token).
+ *  Q, K     as for kvscore_probs (V is not read).
+ *  row_max, row_sum  kvscore_probs outputs for the same inputs.
+ *  S        [batch][h_kv][n] fp32 out.
+ *  ws, ws_bytes  the LORE workspace (>= kvs_lore_workspace_bytes).
+ * Errors: KVS_ERR_INVALID for an unknown kind, w < 1 or a NULL pointer.
+ */
+kvs_status kvscore_baseline_scores(const kvs_lore_desc *desc, int kind, const void *Q,
+                                   const void *K, const float *row_max, const float *row_sum,
+                                   float *S, void *ws, size_t ws_bytes, void *stream);
+
 /* Bytes of workspace kvscore_topb_select needs (0 if the selection fields of
  * the descriptor are invalid).  No larger than kvs_lore_workspace_bytes(). */
 size_t kvs_topb_workspace_bytes(const kvs_lore_desc *desc);

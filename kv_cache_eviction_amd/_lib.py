@@ -17,11 +17,12 @@ LIB_PATH = os.path.join(_PKG, "libkvscore.so")
 
 KVS_F32, KVS_BF16, KVS_F16 = 0, 1, 2
 KVS_H2O_PREFILL, KVS_H2O_DECODE = 0, 1
+KVS_BASELINE_WINDOW, KVS_BASELINE_TOVA = 0, 1
 DTYPE_CODE = {torch.float32: KVS_F32, torch.bfloat16: KVS_BF16, torch.float16: KVS_F16}
 CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
 
 EXPORTS = ("kvs_lore_workspace_bytes", "kvs_topb_workspace_bytes", "kvscore_probs", "kvscore_deletion",
-           "kvscore_topb_select", "kv_compact", "kvs_h2o_workspace_bytes",
+           "kvscore_baseline_scores", "kvscore_topb_select", "kv_compact", "kvs_h2o_workspace_bytes",
            "kvscore_h2o_accumulate", "kvs_timing_enable", "kvs_timing_count", "kvs_timing_read",
            "kvs_timing_reset", "kvs_last_error")
 
@@ -73,6 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvscore_probs.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kvscore_deletion.restype = i32
     lib.kvscore_deletion.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kvscore_baseline_scores.restype = i32
+    lib.kvscore_baseline_scores.argtypes = [LP, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kvs_topb_workspace_bytes.restype = sz
     lib.kvs_topb_workspace_bytes.argtypes = [LP]
     lib.kvscore_topb_select.restype = i32
@@ -186,6 +189,24 @@ def kvscore_deletion(desc, Q, K, V, W_O, omega, row_max, row_sum, O, S, ws, stre
                                    _ptr(omega), _ptr(row_max), _ptr(row_sum), _ptr(O), _ptr(S),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "kvscore_deletion")
+
+
+def kvscore_baseline_scores(desc, kind, Q, K, row_max, row_sum, S, ws, stream=None):
+    """kind: KVS_BASELINE_WINDOW or KVS_BASELINE_TOVA; row_max, row_sum from
+    kvscore_probs on the same Q, K."""
+    dt = CODE_DTYPE[desc.dtype]
+    b, hq, hk, n, d, nq = desc.batch, desc.h_q, desc.h_kv, desc.n, desc.d, desc.n_q
+    _need(Q, "Q", (b, hq, nq, d), dt)
+    _need(K, "K", (b, hk, n, d), dt)
+    _need(row_max, "row_max", (b, hq, nq), torch.float32)
+    _need(row_sum, "row_sum", (b, hq, nq), torch.float32)
+    _need(S, "S", (b, hk, n), torch.float32)
+    need = kvs_lore_workspace_bytes(desc)
+    _ws_check(ws, need)
+    _check(load().kvscore_baseline_scores(ctypes.byref(desc), int(kind), _ptr(Q), _ptr(K),
+                                          _ptr(row_max), _ptr(row_sum), _ptr(S), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream)),
+           "kvscore_baseline_scores")
 
 
 def kvs_topb_workspace_bytes(desc: LoreDesc) -> int:

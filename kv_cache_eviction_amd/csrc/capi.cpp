@@ -206,6 +206,32 @@ KVS_API kvs_status kvscore_deletion(const kvs_lore_desc *desc, const void *Q, co
   return hip_status(e, "deletion score");
 }
 
+KVS_API kvs_status kvscore_baseline_scores(const kvs_lore_desc *desc, int kind, const void *Q,
+                                           const void *K, const float *row_max,
+                                           const float *row_sum, float *S, void *ws,
+                                           size_t ws_bytes, void *stream) {
+  kvs_status st = check_lore(desc);
+  if (st != KVS_OK) return st;
+  if (kind != KVS_BASELINE_WINDOW && kind != KVS_BASELINE_TOVA)
+    return fail(KVS_ERR_INVALID, "kvscore_baseline_scores: unknown kind");
+  if (desc->w < 1) return fail(KVS_ERR_INVALID, "kvscore_baseline_scores: needs w >= 1 window rows");
+  if (!Q || !K || !row_max || !row_sum || !S)
+    return fail(KVS_ERR_INVALID, "kvscore_baseline_scores: a required pointer is NULL");
+  const LorePlan p = plan_lore(desc);
+  st = check_ws(ws, ws_bytes, p.deletion_bytes);
+  if (st != KVS_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const kvs::RowGeom geo = lore_geom(desc);
+  float4 *consts = at<float4>(ws, p.off_consts);
+  hipError_t e = kvs::launch_baseline_prep(row_max, row_sum, desc->batch, desc->h_q, desc->n,
+                                           geo.nq, desc->w, kind == KVS_BASELINE_TOVA, consts, s);
+  if (e != hipSuccess) return hip_status(e, "baseline prep");
+  e = kvs::launch_score(desc->dtype, desc->d, 1, Q, K, nullptr, nullptr, nullptr, consts, nullptr,
+                        n_pad_of(desc->n), geo, desc->batch, desc->h_kv, desc->eps,
+                        1.f / (float)geo.group, S, s);
+  return hip_status(e, "baseline score");
+}
+
 KVS_API size_t kvs_topb_workspace_bytes(const kvs_lore_desc *desc) {
   if (check_select(desc) != KVS_OK) return 0;
   return topb_bytes_of(desc);

@@ -911,6 +911,38 @@ hipError_t launch_gram(int etype, int d, const void *W_O, int d_model, int h_q, 
 #undef KVS_G
 }
 
+// Row constants of the prompt-side baselines, read by score_kernel<1> (a
+// plain sum of probabilities): window row r keeps beta2 = row_max*log2(e) +
+// log2(row_sum) and its last visible key n - w + r; rows outside the chosen
+// set (lookahead rows, padding, and for the single-query form every window
+// row but the last) get last = -1, which the score pass treats as a row
+// without keys (a = 0).
+__global__ void __launch_bounds__(64)
+baseline_prep_kernel(const float *__restrict__ row_max, const float *__restrict__ row_sum,
+                     int n, int nq, int w, int last_only, float4 *__restrict__ consts) {
+  const long hb = blockIdx.x;
+  const int r = threadIdx.x;
+  const bool used = r < nq && r < w && (!last_only || r == w - 1);
+  float beta2 = 0.f;
+  int last = -1;
+  if (used) {
+    beta2 = row_max[hb * nq + r] * kLog2e + log2f(row_sum[hb * nq + r]);
+    last = n - w + r;
+  }
+  consts[hb * 64 + r] = make_float4(beta2, 0.f, 1.f, __int_as_float(last));
+}
+
+hipError_t launch_baseline_prep(const float *row_max, const float *row_sum, int batch, int h_q,
+                                int n, int nq, int w, bool last_only, float4 *consts,
+                                hipStream_t st) {
+  {
+    TimedLaunch tl_("baseline_prep", st);
+    hipLaunchKernelGGL(baseline_prep_kernel, dim3(batch * h_q), dim3(64), 0, st, row_max, row_sum,
+                       n, nq, w, last_only ? 1 : 0, consts);
+  }
+  return hipGetLastError();
+}
+
 template <int D, typename TV>
 static hipError_t run_prep(const float *Gpart, int gsplits, const float *O, const float *row_max,
                            const float *row_sum, const float *omega, int batch, int h_q, int n,

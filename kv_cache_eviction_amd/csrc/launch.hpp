@@ -49,6 +49,10 @@ hipError_t launch_attn_combine_rows(const float *part_m, const float *part_l, in
 
 // Deletion score pieces.
 int gram_splits(int h_q, int d_model, int elem_bytes);
+// Row constants for the prompt-side baselines (window rows, or the last one).
+hipError_t launch_baseline_prep(const float *row_max, const float *row_sum, int batch, int h_q,
+                                int n, int nq, int w, bool last_only, float4 *consts,
+                                hipStream_t st);
 hipError_t launch_gram(int etype, int d, const void *W_O, int d_model, int h_q, int splits,
                        float *Gpart, hipStream_t st);
 hipError_t launch_deletion_prep(int etype, int d, const float *Gpart, int gsplits, const float *O,

@@ -34,6 +34,14 @@ class LoreEviction:
                            self.S, self.ws, stream)
         return self.S
 
+    def baseline(self, kind, Q, K, V, stream=None):
+        """Prompt-side baseline scores (L.KVS_BASELINE_WINDOW or L.KVS_BASELINE_TOVA)
+        into S, for the same selector; runs pass 1 for the row statistics."""
+        L.kvscore_probs(self.desc, Q, K, V, self.row_max, self.row_sum, self.O, self.ws, stream)
+        L.kvscore_baseline_scores(self.desc, kind, Q, K, self.row_max, self.row_sum, self.S,
+                                  self.ws, stream)
+        return self.S
+
     def select(self, pooled=None, stream=None):
         L.kvscore_topb_select(self.desc, self.S, self.kept, pooled, self.ws, stream)
         return self.kept

@@ -11,6 +11,9 @@ Sources followed (cited per function):
   * H2O summary page, "H2O: Heavy-Hitter Oracle": 3.4 formal problem
     formulation (Defs. 2.1-2.2), the H2O eviction algorithm (accumulated
     scores, greedy eviction, budget split), System Implementation Details.
+  * LORE-KV page, "The query-reference mismatch" ("Prompt-side eviction") and
+    the counter-causal review "Back from the Future", "Prerequisites"
+    (TOVA): the prompt-side baseline scores.
 
 Readings taken where the pages leave a step open (each also listed in the
 design notes): softmax logits carry 1/sqrt(d); window rows are causal at their
@@ -18,7 +21,9 @@ own positions; psi is the arithmetic mean; the GQA group score is the mean of
 its query heads' scores; chunk pooling is the mean over a chunk's candidate
 members; ties rank by lower index; H2O's budget is floor(frac * current
 length) per part, the recent part is protected, and the prompt is reduced to
-the budget by accumulated column sums before decoding.
+the budget by accumulated column sums before decoding; the prompt-side
+baseline scores sum the window rows' attention (TOVA: the last window row
+only) and take the GQA group mean.
 """
 
 import ctypes
@@ -147,6 +152,37 @@ def lore_scores(Q, K, V, W_O, omega, *, w, m, t, eps, lambda_l, nthreads=0, R=No
         raise ValueError("ora_lore_scores: invalid shape (%d)" % rc)
     S = S_head.reshape(b, h_kv, h_q // h_kv, n).mean(axis=2)
     return {"S": S, "S_head": S_head, "row_max": row_max, "row_sum": row_sum, "O": O}
+
+
+def baseline_scores(Q, K, *, w, kind):
+    """Prompt-side attention scores of every cached token per KV head.
+
+    kind "window": the LORE-KV page's prompt-side baseline ("The
+    query-reference mismatch", "Prompt-side eviction"): a token ranks by how
+    the last w prompt queries attend to it, S_i = sum_{r<w} a_{r,i}.
+    kind "tova": the counter-causal review's TOVA ("Prerequisites",
+    attention-based eviction): the last prompt token's attention only,
+    S_i = a_{w-1,i}.  Window row r is causal at position n-w+r, as in
+    lore_attention; the KV head's score is the mean over its query heads.
+    Returns S [b][h_kv][n].
+    """
+    if kind not in ("window", "tova"):
+        raise ValueError("kind must be 'window' or 'tova'")
+    Q, K = _f64(Q), _f64(K)
+    b, h_q, n_q, d = Q.shape
+    _, h_kv, n, _ = K.shape
+    G = h_q // h_kv
+    rows = range(w) if kind == "window" else [w - 1]
+    S = np.zeros((b, h_kv, n))
+    for bb in range(b):
+        for h in range(h_q):
+            g = h // G
+            for r in rows:
+                s = K[bb, g] @ Q[bb, h, r] / math.sqrt(d)
+                s[n - w + r + 1:] = -np.inf  # causal at its own position
+                s = np.exp(s - s.max())
+                S[bb, g] += s / s.sum() / G
+    return S
 
 
 def pooled_scores(S, n_sink, w, chunk):
