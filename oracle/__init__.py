@@ -11,6 +11,8 @@ Sources followed (cited per function):
   * H2O summary page, "H2O: Heavy-Hitter Oracle": 3.4 formal problem
     formulation (Defs. 2.1-2.2), the H2O eviction algorithm (accumulated
     scores, greedy eviction, budget split), System Implementation Details.
+  * LORE-KV page, Method, "Reliability weights" (Eqs. 2-4, 10): the
+    trajectory weights omega.
   * LORE-KV page, "The query-reference mismatch" ("Prompt-side eviction") and
     the counter-causal review "Back from the Future", "Prerequisites"
     (TOVA): the prompt-side baseline scores.
@@ -23,7 +25,9 @@ members; ties rank by lower index; H2O's budget is floor(frac * current
 length) per part, the recent part is protected, and the prompt is reduced to
 the budget by accumulated column sums before decoding; the prompt-side
 baseline scores sum the window rows' attention (TOVA: the last window row
-only) and take the GQA group mean.
+only) and take the GQA group mean; the trajectory disagreement D_m is the mean
+(1 - cosine) between its lookahead queries and every other trajectory's, per
+query head, standardized over the trajectories (zero below a spread of 1e-6).
 """
 
 import ctypes
@@ -183,6 +187,69 @@ def baseline_scores(Q, K, *, w, kind):
                 s = np.exp(s - s.max())
                 S[bb, g] += s / s.sum() / G
     return S
+
+
+STD_FLOOR = 1e-6  # below this spread the disagreements are taken as equal
+
+
+def centered_score(probs, y):
+    """Centered score of one sampled token (LORE-KV "Reliability weights",
+    Eqs. 2-4): c = log q(y | h) + H(q(. | h)), from the full next-token
+    distribution `probs` and the sampled index `y`.  Returns (c, H)."""
+    p = np.asarray(probs, dtype=np.float64)
+    nz = p > 0
+    H = float(-(p[nz] * np.log(p[nz])).sum())
+    return float(math.log(p[y])) + H, H
+
+
+def reliability_weights(Q, logp, entropy, *, w, m, t, beta, gamma, lambda_d):
+    """Trajectory weights omega of Eq. 10 (LORE-KV "Reliability weights"):
+    R_m = beta * cbar_m - gamma * Hbar_m - lambda_d * Dhat_m, omega = softmax(R).
+
+    Q [b][h_q][w + m*t][d]: the scoring queries; rows w + j*t .. w + j*t + t-1
+    are trajectory j's lookahead queries.  logp, entropy [b][m][t]: log q(y_u)
+    of each sampled token and the entropy of the distribution it was drawn
+    from, so c_u = logp_u + entropy_u (Eqs. 2-4); cbar_m and Hbar_m are the
+    means over the trajectory's t tokens.
+
+    Dhat_m, "the standardized cosine disagreement of trajectory m's queries
+    with the others", is read as: D_m = mean of (1 - cos(q, q')) over every
+    query head, every query q of trajectory m and every query q' of every other
+    trajectory at the same head (a query of zero norm has cosine 0 with all);
+    Dhat = (D - mean D) / std D over the m trajectories (population std), and
+    Dhat = 0 when that std is below STD_FLOOR (all trajectories equally
+    typical, e.g. m = 2, where D_1 = D_2 by symmetry).
+    Returns dict(omega [b][m], dhat [b][m], D [b][m], R [b][m]).
+    """
+    Q, logp, entropy = _f64(Q), _f64(logp), _f64(entropy)
+    b, h_q, n_q, d = Q.shape
+    if n_q != w + m * t or logp.shape != (b, m, t) or entropy.shape != (b, m, t):
+        raise ValueError("shape mismatch")
+    D = np.zeros((b, m))
+    for bb in range(b):
+        for j in range(m):
+            total, count = 0.0, 0
+            for h in range(h_q):
+                mine = Q[bb, h, w + j * t: w + (j + 1) * t]
+                for jj in range(m):
+                    if jj == j:
+                        continue
+                    other = Q[bb, h, w + jj * t: w + (jj + 1) * t]
+                    for q in mine:
+                        for q2 in other:
+                            nq, nq2 = np.linalg.norm(q), np.linalg.norm(q2)
+                            cos = 0.0 if nq == 0.0 or nq2 == 0.0 else float(q @ q2) / (nq * nq2)
+                            total += 1.0 - cos
+                            count += 1
+            D[bb, j] = total / count if count else 0.0
+    mu = D.mean(axis=1, keepdims=True)
+    sd = np.sqrt(((D - mu) ** 2).mean(axis=1, keepdims=True))
+    dhat = np.where(sd < STD_FLOOR, 0.0, (D - mu) / np.where(sd < STD_FLOOR, 1.0, sd))
+    cbar = (logp + entropy).mean(axis=2)
+    hbar = entropy.mean(axis=2)
+    R = beta * cbar - gamma * hbar - lambda_d * dhat
+    e = np.exp(R - R.max(axis=1, keepdims=True))
+    return {"omega": e / e.sum(axis=1, keepdims=True), "dhat": dhat, "D": D, "R": R}
 
 
 def pooled_scores(S, n_sink, w, chunk):
