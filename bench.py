@@ -243,7 +243,7 @@ def main():
 
     import torch
     import kv_cache_eviction_amd as kv
-    from kvsynth import LORE_CONFIGS, lore_inputs, TORCH_DTYPES
+    from kvsynth import LORE_CONFIGS, lore_inputs, trajectory_token_stats, TORCH_DTYPES
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -376,6 +376,31 @@ def main():
                      "achieved": round(kbytes / (sms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(kbytes / (sms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic("score_baseline")}}
+    # the trajectory reliability weights that feed the lookahead term (Eq. 10):
+    # a few microseconds of fp64 cosines over the M*T lookahead queries, so
+    # launch latency bounds it; the HBM rate is over the lookahead rows read
+    print("[bench] reliability weights", file=sys.stderr, flush=True)
+    logp, ent = trajectory_token_stats(cfg, 0, device=dev)
+    ev.weights(x["Q"], logp, ent)
+    torch.cuda.synchronize()
+    kv.kvs_timing_reset()
+    kv.kvs_timing_enable(True)
+    for _ in range(5):
+        ev.weights(x["Q"], logp, ent)
+    torch.cuda.synchronize()
+    rrec = kv.kvs_timing_records()
+    kv.kvs_timing_enable(False)
+    kv.kvs_timing_reset()
+    rms = sum(ms for _, ms in rrec) / 5
+    cms = [ms for nm, ms in rrec if nm == "traj_cosine"]
+    cms = sum(cms) / len(cms)
+    qbytes = cfg.batch * cfg.h_q * cfg.m * cfg.t * cfg.d * 2
+    out["reliability_weights"] = {
+        "kernels_ms": round(rms, 4), "launches_per_call": len(rrec) // 5,
+        "roofline": {"kernel": "traj_cosine", "bound": "hbm",
+                     "achieved": round(qbytes / (cms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(qbytes / (cms * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
+                     "traffic": None}}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, data[0])

@@ -19,7 +19,10 @@
  *  - Every tensor pointer is a DEVICE pointer to memory the caller owns and
  *    keeps alive until the enqueued work has finished.  The library keeps no
  *    device memory between calls; scratch comes from a caller workspace.
- *  - Tensors are dense, row-major, in the layouts stated per argument.
+ *  - Tensors are dense, row-major, in the layouts stated per argument.  The
+ *    base address of every tensor of the descriptor's dtype (and of O) must
+ *    be 16-byte aligned (KVS_ERR_INVALID otherwise): rows are moved with
+ *    16-byte vector accesses.
  *    Element type of Q, K, V, W_O (and of the H2O inputs) is the descriptor's
  *    dtype; statistics and scores are fp32; indices are int32.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
@@ -131,6 +134,39 @@ kvs_status kvscore_deletion(const kvs_lore_desc *desc, const void *Q, const void
                             const void *W_O, const float *omega,
                             const float *row_max, const float *row_sum, const float *O,
                             float *S, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Trajectory reliability weights omega, the input of kvscore_deletion's
+ * lookahead term (LORE-KV Method, "Reliability weights", Eqs. 2-4 and 10):
+ *   c_u = log q(y_u) + H_u per sampled token; cbar_m, Hbar_m = means over the
+ *   trajectory's t tokens; R_m = beta cbar_m - gamma Hbar_m - lambda_d Dhat_m;
+ *   omega = softmax(R) over the m trajectories of each sequence.
+ * Dhat_m is the trajectory's standardized cosine disagreement, read as: D_m =
+ * mean of (1 - cos) over every query head and every pair (a query of
+ * trajectory m, a query of another trajectory) at that head (a zero query has
+ * cosine 0); Dhat = (D - mean D) / std D over the trajectories (population
+ * std), and 0 when that std is below 1e-6 (m = 2 always gives 0).  The window
+ * rows are not read.  Presets: LORE-KV /E (beta, gamma, lambda_d) = (1, 1.3, 0),
+ * /D = (1, 1, 0.3) (KVS_RELIABILITY_E / KVS_RELIABILITY_D below).
+ *
+ *  Q        [batch][h_q][n_q][d]  the scoring queries (as for kvscore_probs);
+ *           rows w + j*t .. w + j*t + t - 1 are trajectory j's.
+ *  logp     [batch][m][t] fp32    log-probability of each sampled token.
+ *  entropy  [batch][m][t] fp32    entropy of the distribution it was drawn from.
+ *  omega    [batch][m] fp32       out: the weights (each row sums to 1).
+ *  dhat     [batch][m] fp32       out, nullable: Dhat.
+ *  ws, ws_bytes                   workspace (>= kvs_lore_workspace_bytes; not
+ *                                 read when m = 1).
+ * m = 0 is a no-op; m above 64 is KVS_ERR_UNSUPPORTED.  Cosines, norms and all
+ * sums run in fp64 in a fixed order (deterministic).
+ */
+#define KVS_RELIABILITY_E 1.0f, 1.3f, 0.0f
+#define KVS_RELIABILITY_D 1.0f, 1.0f, 0.3f
+kvs_status kvscore_reliability_weights(const kvs_lore_desc *desc, const void *Q,
+                                       const float *logp, const float *entropy,
+                                       float beta, float gamma, float lambda_d,
+                                       float *omega, float *dhat,
+                                       void *ws, size_t ws_bytes, void *stream);
 
 /* Which prompt-side baseline kvscore_baseline_scores computes. */
 typedef enum { KVS_BASELINE_WINDOW = 0, KVS_BASELINE_TOVA = 1 } kvs_baseline;

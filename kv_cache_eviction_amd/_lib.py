@@ -22,7 +22,7 @@ DTYPE_CODE = {torch.float32: KVS_F32, torch.bfloat16: KVS_BF16, torch.float16: K
 CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
 
 EXPORTS = ("kvs_lore_workspace_bytes", "kvs_topb_workspace_bytes", "kvscore_probs", "kvscore_deletion",
-           "kvscore_baseline_scores", "kvscore_topb_select", "kv_compact", "kvs_h2o_workspace_bytes",
+           "kvscore_baseline_scores", "kvscore_reliability_weights", "kvscore_topb_select", "kv_compact", "kvs_h2o_workspace_bytes",
            "kvscore_h2o_accumulate", "kvs_timing_enable", "kvs_timing_count", "kvs_timing_read",
            "kvs_timing_reset", "kvs_last_error")
 
@@ -76,6 +76,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvscore_deletion.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kvscore_baseline_scores.restype = i32
     lib.kvscore_baseline_scores.argtypes = [LP, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    f32 = ctypes.c_float
+    lib.kvscore_reliability_weights.restype = i32
+    lib.kvscore_reliability_weights.argtypes = [LP, vp, vp, vp, f32, f32, f32, vp, vp, vp, sz, vp]
     lib.kvs_topb_workspace_bytes.restype = sz
     lib.kvs_topb_workspace_bytes.argtypes = [LP]
     lib.kvscore_topb_select.restype = i32
@@ -207,6 +210,31 @@ def kvscore_baseline_scores(desc, kind, Q, K, row_max, row_sum, S, ws, stream=No
                                           _ptr(row_max), _ptr(row_sum), _ptr(S), _ptr(ws),
                                           ws.numel() * ws.element_size(), _stream(stream)),
            "kvscore_baseline_scores")
+
+
+RELIABILITY_E = (1.0, 1.3, 0.0)  # LORE-KV /E (beta, gamma, lambda_d)
+RELIABILITY_D = (1.0, 1.0, 0.3)  # LORE-KV /D
+
+
+def kvscore_reliability_weights(desc, Q, logp, entropy, omega, coef=RELIABILITY_D, dhat=None,
+                                ws=None, stream=None):
+    """Trajectory weights omega [batch][m] from the lookahead queries in Q and
+    the per-token log-probability and entropy [batch][m][t]; coef = (beta,
+    gamma, lambda_d)."""
+    dt = CODE_DTYPE[desc.dtype]
+    b, hq, nq, d, m, t = desc.batch, desc.h_q, desc.n_q, desc.d, desc.m, desc.t
+    _need(Q, "Q", (b, hq, nq, d), dt)
+    _need(logp, "logp", (b, m, t), torch.float32)
+    _need(entropy, "entropy", (b, m, t), torch.float32)
+    _need(omega, "omega", (b, m), torch.float32)
+    _need(dhat, "dhat", (b, m), torch.float32, optional=True)
+    beta, gamma, lambda_d = (float(c) for c in coef)
+    if ws is not None:
+        _ws_check(ws, kvs_lore_workspace_bytes(desc))
+    _check(load().kvscore_reliability_weights(
+        ctypes.byref(desc), _ptr(Q), _ptr(logp), _ptr(entropy), beta, gamma, lambda_d,
+        _ptr(omega), _ptr(dhat), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream)), "kvscore_reliability_weights")
 
 
 def kvs_topb_workspace_bytes(desc: LoreDesc) -> int:

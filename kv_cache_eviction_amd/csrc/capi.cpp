@@ -5,7 +5,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 
 #include "launch.hpp"
@@ -20,6 +22,15 @@ thread_local std::string g_err;
 kvs_status fail(kvs_status st, const std::string &msg) {
   g_err = msg;
   return st;
+}
+
+// Element-type tensors (and O) are read and written with 16-byte vector
+// accesses, so their base addresses must be 16-byte aligned.
+kvs_status check_aligned(const char *who, std::initializer_list<const void *> ptrs) {
+  for (const void *p : ptrs)
+    if (p && (reinterpret_cast<uintptr_t>(p) & 15u))
+      return fail(KVS_ERR_INVALID, std::string(who) + ": tensor pointers must be 16-byte aligned");
+  return KVS_OK;
 }
 
 kvs_status ok() {
@@ -41,7 +52,7 @@ int n_pad_of(int n) { return (n + 63) / 64 * 64; }
 struct LorePlan {
   kvs::SplitPlan split;
   int gsplits;
-  size_t probs_bytes, deletion_bytes, topb_bytes;
+  size_t probs_bytes, deletion_bytes, topb_bytes, reliability_bytes;
   // deletion layout
   size_t off_gpart, off_gv, off_gr, off_yhi, off_ylo, off_consts, off_n;
   // probs layout
@@ -97,6 +108,7 @@ LorePlan plan_lore(const kvs_lore_desc *d) {
   p.deletion_bytes = align_up(p.off_n + heads * (size_t)n_pad_of(d->n) * 4);
 
   p.topb_bytes = topb_bytes_of(d);
+  p.reliability_bytes = align_up(kvs::reliability_ws_bytes(d->batch, d->h_q, d->m));
   return p;
 }
 
@@ -146,6 +158,7 @@ KVS_API size_t kvs_lore_workspace_bytes(const kvs_lore_desc *desc) {
   size_t m = p.probs_bytes;
   if (p.deletion_bytes > m) m = p.deletion_bytes;
   if (p.topb_bytes > m) m = p.topb_bytes;
+  if (p.reliability_bytes > m) m = p.reliability_bytes;
   return m;
 }
 
@@ -156,6 +169,8 @@ KVS_API kvs_status kvscore_probs(const kvs_lore_desc *desc, const void *Q, const
   if (st != KVS_OK) return st;
   if (!Q || !K || !V || !row_max || !row_sum || !O)
     return fail(KVS_ERR_INVALID, "kvscore_probs: a required pointer is NULL");
+  st = check_aligned("kvscore_probs", {Q, K, V, O});
+  if (st != KVS_OK) return st;
   const LorePlan p = plan_lore(desc);
   st = check_ws(ws, ws_bytes, p.probs_bytes);
   if (st != KVS_OK) return st;
@@ -179,6 +194,8 @@ KVS_API kvs_status kvscore_deletion(const kvs_lore_desc *desc, const void *Q, co
   if (!Q || !K || !V || !W_O || !row_max || !row_sum || !O || !S)
     return fail(KVS_ERR_INVALID, "kvscore_deletion: a required pointer is NULL");
   if (desc->m > 0 && !omega) return fail(KVS_ERR_INVALID, "kvscore_deletion: omega is NULL");
+  st = check_aligned("kvscore_deletion", {Q, K, V, W_O, O});
+  if (st != KVS_OK) return st;
   const LorePlan p = plan_lore(desc);
   st = check_ws(ws, ws_bytes, p.deletion_bytes);
   if (st != KVS_OK) return st;
@@ -217,6 +234,8 @@ KVS_API kvs_status kvscore_baseline_scores(const kvs_lore_desc *desc, int kind, 
   if (desc->w < 1) return fail(KVS_ERR_INVALID, "kvscore_baseline_scores: needs w >= 1 window rows");
   if (!Q || !K || !row_max || !row_sum || !S)
     return fail(KVS_ERR_INVALID, "kvscore_baseline_scores: a required pointer is NULL");
+  st = check_aligned("kvscore_baseline_scores", {Q, K});
+  if (st != KVS_OK) return st;
   const LorePlan p = plan_lore(desc);
   st = check_ws(ws, ws_bytes, p.deletion_bytes);
   if (st != KVS_OK) return st;
@@ -230,6 +249,34 @@ KVS_API kvs_status kvscore_baseline_scores(const kvs_lore_desc *desc, int kind, 
                         n_pad_of(desc->n), geo, desc->batch, desc->h_kv, desc->eps,
                         1.f / (float)geo.group, S, s);
   return hip_status(e, "baseline score");
+}
+
+KVS_API kvs_status kvscore_reliability_weights(const kvs_lore_desc *desc, const void *Q,
+                                               const float *logp, const float *entropy,
+                                               float beta, float gamma, float lambda_d,
+                                               float *omega, float *dhat, void *ws,
+                                               size_t ws_bytes, void *stream) {
+  kvs_status st = check_lore(desc);
+  if (st != KVS_OK) return st;
+  if (desc->m < 1) return ok();  // no trajectories: nothing to weight
+  if (desc->m > 64) return fail(KVS_ERR_UNSUPPORTED, "kvscore_reliability_weights: m above 64");
+  if (!Q || !logp || !entropy || !omega)
+    return fail(KVS_ERR_INVALID, "kvscore_reliability_weights: a required pointer is NULL");
+  st = check_aligned("kvscore_reliability_weights", {Q});
+  if (st != KVS_OK) return st;
+  if (!(std::isfinite(beta) && std::isfinite(gamma) && std::isfinite(lambda_d)))
+    return fail(KVS_ERR_INVALID, "kvscore_reliability_weights: beta, gamma, lambda_d must be finite");
+  const LorePlan p = plan_lore(desc);
+  if (desc->m > 1) {
+    st = check_ws(ws, ws_bytes, p.reliability_bytes);
+    if (st != KVS_OK) return st;
+  }
+  const int nq = desc->w + desc->m * desc->t;
+  hipError_t e = kvs::launch_reliability(desc->dtype, Q, desc->batch, desc->h_q, nq, desc->d,
+                                         desc->w, desc->m, desc->t, logp, entropy, beta, gamma,
+                                         lambda_d, omega, dhat, at<double>(ws, 0),
+                                         static_cast<hipStream_t>(stream));
+  return hip_status(e, "reliability weights");
 }
 
 KVS_API size_t kvs_topb_workspace_bytes(const kvs_lore_desc *desc) {
@@ -269,6 +316,7 @@ KVS_API kvs_status kv_compact(int32_t batch, int32_t heads, int32_t n_src, int32
     return fail(KVS_ERR_INVALID, "kv_compact: a required pointer is NULL");
   if ((score_in == nullptr) != (score_out == nullptr))
     return fail(KVS_ERR_INVALID, "kv_compact: score_in and score_out go together");
+  if (check_aligned("kv_compact", {K, V, K_out, V_out}) != KVS_OK) return KVS_ERR_INVALID;
   const int row_bytes = d * (int)kvs::elem_bytes(dtype);
   hipError_t e = kvs::launch_compact(batch * heads, n_src, n_keep, cap_dst, row_bytes, K, V, kept,
                                      K_out, V_out, pos_out, score_in, score_out,
@@ -334,6 +382,8 @@ KVS_API kvs_status kvscore_h2o_accumulate(const kvs_h2o_desc *desc, int32_t mode
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (mode == KVS_H2O_PREFILL) {
     if (!q || !K || !acc) return fail(KVS_ERR_INVALID, "prefill: q, K and acc are required");
+    st = check_aligned("prefill", {q, K});
+    if (st != KVS_OK) return st;
     const H2OPlan p = plan_h2o(desc);
     st = check_ws(ws, ws_bytes, p.bytes);
     if (st != KVS_OK) return st;
@@ -352,6 +402,8 @@ KVS_API kvs_status kvscore_h2o_accumulate(const kvs_h2o_desc *desc, int32_t mode
   }
   if (!q || !K || !V || !k_new || !v_new || !slot_pos || !acc)
     return fail(KVS_ERR_INVALID, "decode: q, K, V, k_new, v_new, slot_pos and acc are required");
+  st = check_aligned("decode", {q, K, V, k_new, v_new, O});
+  if (st != KVS_OK) return st;
   hipError_t e = kvs::launch_h2o_decode(desc->dtype, desc->d, desc->batch * desc->heads, desc->cap,
                                         desc->cur_len, desc->k_heavy, desc->k_recent, q, K, V,
                                         k_new, v_new,

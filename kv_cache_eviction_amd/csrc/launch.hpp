@@ -47,6 +47,14 @@ hipError_t launch_attn_combine_lore(int d, const float *part_m, const float *par
 hipError_t launch_attn_combine_rows(const float *part_m, const float *part_l, int heads,
                                     int splits, int group, int P, float4 *consts, hipStream_t st);
 
+// Trajectory reliability weights: per-head cosine sums per trajectory pair
+// (pair_sum: reliability_ws_bytes), then D, Dhat, R and omega per sequence.
+size_t reliability_ws_bytes(int batch, int h_q, int m);
+hipError_t launch_reliability(int etype, const void *Q, int batch, int h_q, int nq, int d, int w,
+                              int m, int t, const float *logp, const float *entropy, float beta,
+                              float gamma, float lambda_d, float *omega, float *dhat,
+                              double *pair_sum, hipStream_t st);
+
 // Deletion score pieces.
 int gram_splits(int h_q, int d_model, int elem_bytes);
 // Row constants for the prompt-side baselines (window rows, or the last one).

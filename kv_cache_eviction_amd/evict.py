@@ -27,6 +27,14 @@ class LoreEviction:
         self.S = torch.empty(b, hk, n, **f32)
         self.kept = torch.empty(b, hk, desc.n_keep, dtype=torch.int32, device=device)
         self.ws = torch.empty(L.kvs_lore_workspace_bytes(desc), dtype=torch.uint8, device=device)
+        self.omega = torch.empty(b, desc.m, **f32)
+
+    def weights(self, Q, logp, entropy, coef=L.RELIABILITY_D, stream=None):
+        """Trajectory weights omega (Eq. 10) from the lookahead rows of Q and the
+        sampled tokens' log-probabilities and entropies [batch][m][t]."""
+        L.kvscore_reliability_weights(self.desc, Q, logp, entropy, self.omega, coef, ws=self.ws,
+                                      stream=stream)
+        return self.omega
 
     def score(self, Q, K, V, W_O, omega, stream=None):
         L.kvscore_probs(self.desc, Q, K, V, self.row_max, self.row_sum, self.O, self.ws, stream)

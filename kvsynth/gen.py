@@ -124,6 +124,19 @@ def lore_inputs(cfg: LoreConfig, layer: int = 0, device="cpu"):
     }
 
 
+def trajectory_token_stats(cfg: LoreConfig, layer: int = 0, device="cpu"):
+    """Per-token statistics of the M sampled continuations, which a model's
+    next-token distributions would give: entropy [b][m][t] ~ U(0.5, 4) nats
+    and log-probability [b][m][t] = min(0, -entropy + 0.8 z), z ~ N(0, 1)
+    (tokens about as likely as the distribution they came from, with noise).
+    Returns (logp, entropy), fp32."""
+    gen = _generator(20_000 + cfg.seed + layer, device)
+    shape = (cfg.batch, cfg.m, cfg.t)
+    ent = 0.5 + 3.5 * torch.rand(*shape, generator=gen, device=device, dtype=torch.float32)
+    logp = torch.clamp(-ent + 0.8 * _randn(gen, *shape, device=device), max=0.0)
+    return logp, ent
+
+
 def h2o_inputs(cfg: H2OConfig, device="cpu"):
     """Inputs for an H2O prompt + decode run.
 

@@ -90,6 +90,35 @@ def test_null_pointers_and_workspace():
                           None, None) == 1
 
 
+def test_reliability_weights_host_checks():
+    kv, lib = _lib()
+    d = _desc(kv)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: a host check fails first
+    f = ctypes.c_float
+    big = 1 << 30
+    rc = lib.kvscore_reliability_weights(ctypes.byref(d), fake, None, fake, f(1), f(1), f(0.3),
+                                         fake, None, fake, big, None)
+    assert rc == 1 and "NULL" in kv.last_error()
+    rc = lib.kvscore_reliability_weights(ctypes.byref(d), fake, fake, fake, f(float("nan")), f(1),
+                                         f(0.3), fake, None, fake, big, None)
+    assert rc == 1 and "finite" in kv.last_error()
+    rc = lib.kvscore_reliability_weights(ctypes.byref(d), fake, fake, fake, f(1), f(1), f(0.3),
+                                         fake, None, fake, 16, None)
+    assert rc == 3 and "workspace" in kv.last_error()
+    odd = ctypes.c_void_p(0x1008)  # 8-byte aligned only
+    rc = lib.kvscore_reliability_weights(ctypes.byref(d), odd, fake, fake, f(1), f(1), f(0.3),
+                                         fake, None, fake, big, None)
+    assert rc == 1 and "aligned" in kv.last_error()
+    rc = lib.kvscore_probs(ctypes.byref(d), fake, odd, fake, fake, fake, fake, fake, big, None)
+    assert rc == 1 and "aligned" in kv.last_error()
+    assert lib.kv_compact(1, 1, 10, 5, 5, 128, 1, fake, fake, fake, odd, fake, None, None,
+                          None, None) == 1
+    # no trajectories: nothing to weight, no pointer is read
+    d0 = _desc(kv, m=0, t=0)
+    assert lib.kvscore_reliability_weights(ctypes.byref(d0), None, None, None, f(1), f(1), f(0),
+                                           None, None, None, 0, None) == 0
+
+
 def test_selection_descriptor_needs_only_selection_fields():
     kv, lib = _lib()
     d = kv.lore_desc(batch=2, n=1024, h_q=3, h_kv=3, d=128, d_model=1, w=102, m=0, t=0,
