@@ -12,7 +12,8 @@ Sources followed (cited per function):
     formulation (Defs. 2.1-2.2), the H2O eviction algorithm (accumulated
     scores, greedy eviction, budget split), System Implementation Details.
   * LORE-KV page, Method, "Reliability weights" (Eqs. 2-4, 10): the
-    trajectory weights omega.
+    trajectory weights omega; "Why it works", "Output fidelity": the
+    attention-output fidelity of a retained cache.
   * LORE-KV page, "The query-reference mismatch" ("Prompt-side eviction") and
     the counter-causal review "Back from the Future", "Prerequisites"
     (TOVA): the prompt-side baseline scores.
@@ -27,7 +28,9 @@ the budget by accumulated column sums before decoding; the prompt-side
 baseline scores sum the window rows' attention (TOVA: the last window row
 only) and take the GQA group mean; the trajectory disagreement D_m is the mean
 (1 - cosine) between its lookahead queries and every other trajectory's, per
-query head, standardized over the trajectories (zero below a spread of 1e-6).
+query head, standardized over the trajectories (zero below a spread of 1e-6); output
+fidelity is the mean cosine between per-head attention outputs over the full
+and the retained cache.
 """
 
 import ctypes
@@ -187,6 +190,46 @@ def baseline_scores(Q, K, *, w, kind):
                 s = np.exp(s - s.max())
                 S[bb, g] += s / s.sum() / G
     return S
+
+
+def output_fidelity(Qf, K, V, kept):
+    """Attention-output fidelity of a retained cache (LORE-KV page, "Why it
+    works", "Output fidelity": how closely the retained cache reproduces the
+    full cache's attention outputs).
+
+    Read as: for every held-out query row r of query head h, the cosine between
+    o_full = softmax(q K^T / sqrt(d)) V over all n tokens of the head's KV head
+    and o_kept, the same over the kept tokens only (renormalised), both in the
+    head's value space; the fidelity is the mean over heads and rows.  Two zero
+    outputs agree (cosine 1); one zero output has cosine 0.
+    Qf [b][h_q][n_f][d]; K, V [b][h_kv][n][d]; kept [b][h_kv][n_keep] indices.
+    Returns dict(cos [b][h_q][n_f], fidelity [b]).
+    """
+    Qf, K, V = _f64(Qf), _f64(K), _f64(V)
+    kept = np.asarray(kept.cpu() if hasattr(kept, "cpu") else kept).astype(np.int64)
+    b, h_q, n_f, d = Qf.shape
+    h_kv = K.shape[1]
+    G = h_q // h_kv
+
+    def attend(q, Kx, Vx):
+        s = q @ Kx.T / math.sqrt(d)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        return (p / p.sum(axis=1, keepdims=True)) @ Vx
+
+    cos = np.empty((b, h_q, n_f))
+    for bb in range(b):
+        for h in range(h_q):
+            g = h // G
+            idx = kept[bb, g]
+            of = attend(Qf[bb, h], K[bb, g], V[bb, g])
+            ok = attend(Qf[bb, h], K[bb, g][idx], V[bb, g][idx])
+            nf, nk = np.linalg.norm(of, axis=1), np.linalg.norm(ok, axis=1)
+            both = (nf == 0) & (nk == 0)
+            one = (nf == 0) ^ (nk == 0)
+            den = np.where((nf == 0) | (nk == 0), 1.0, nf * nk)
+            c = (of * ok).sum(axis=1) / den
+            cos[bb, h] = np.where(both, 1.0, np.where(one, 0.0, c))
+    return {"cos": cos, "fidelity": cos.mean(axis=(1, 2))}
 
 
 STD_FLOOR = 1e-6  # below this spread the disagreements are taken as equal
