@@ -243,7 +243,8 @@ def main():
 
     import torch
     import kv_cache_eviction_amd as kv
-    from kvsynth import LORE_CONFIGS, lore_inputs, trajectory_token_stats, TORCH_DTYPES
+    from kvsynth import (LORE_CONFIGS, lore_inputs, trajectory_token_stats, future_queries,
+                         TORCH_DTYPES)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -263,7 +264,7 @@ def main():
     data = []
     for l in range(layers):
         inp = lore_inputs(cfg, layer=l, device=dev)
-        data.append({k: inp[k].contiguous() for k in ("Q", "K", "V", "W_O", "omega")})
+        data.append({k: inp[k].contiguous() for k in ("Q", "K", "V", "W_O", "omega", "marks")})
     desc = kv.lore_desc(batch=cfg.batch, n=cfg.n, h_q=cfg.h_q, h_kv=cfg.h_kv, d=cfg.d,
                         d_model=cfg.d_model, w=cfg.w, m=cfg.m, t=cfg.t, n_sink=cfg.n_sink,
                         chunk=cfg.chunk, budget=cfg.budget, eps=cfg.eps,
@@ -400,6 +401,44 @@ def main():
         "roofline": {"kernel": "traj_cosine", "bound": "hbm",
                      "achieved": round(qbytes / (cms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(qbytes / (cms * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
+                     "traffic": None}}
+    # attention-output fidelity of layer 0's retained cache under 64 held-out
+    # queries per head aimed at the planted facts, for the LORE-KV selection
+    # and for the window baseline's; timed on the LORE-KV cache (its cost is
+    # the full-cache attention pass, MFMA-bound like pass 1)
+    print("[bench] output fidelity", file=sys.stderr, flush=True)
+    Qf = future_queries(cfg, x, 64, device=dev)
+    _, fid_lore = ev.fidelity(Qf, x["K"], x["V"], outs[0][0], outs[0][1])
+    ev.baseline(kv.KVS_BASELINE_WINDOW, x["Q"], x["K"], x["V"])
+    ev.select()
+    Kw, Vw = torch.empty_like(outs[0][0]), torch.empty_like(outs[0][1])
+    ev.compact(x["K"], x["V"], Kw, Vw)
+    _, fid_win = ev.fidelity(Qf, x["K"], x["V"], Kw, Vw)
+    torch.cuda.synchronize()
+    kv.kvs_timing_reset()
+    kv.kvs_timing_enable(True)
+    for _ in range(5):
+        ev.fidelity(Qf, x["K"], x["V"], outs[0][0], outs[0][1])
+    torch.cuda.synchronize()
+    frec = kv.kvs_timing_records()
+    kv.kvs_timing_enable(False)
+    kv.kvs_timing_reset()
+    fms = sum(ms for _, ms in frec) / 5
+    aff = [ms for nm, ms in frec if nm == "attn_partial"][0::2]  # the full-cache launch of each call
+    aff = sum(aff) / len(aff)
+    fper = {}
+    for nm, ms in frec:
+        fper.setdefault(nm, []).append(ms)
+    fflops = 2 * 2 * 64 * cfg.n * cfg.d * cfg.h_q * cfg.batch
+    out["output_fidelity"] = {
+        "held_out_queries_per_head": 64, "lore": round(float(fid_lore.mean()), 4),
+        "window_baseline": round(float(fid_win.mean()), 4),
+        "kernels_ms": round(fms, 4), "launches_per_call": len(frec) // 5,
+        "per_kernel_ms": {nm: [round(v, 4) for v in vs[:4]] for nm, vs in fper.items()},
+        "roofline": {"kernel": "attn_partial", "bound": "mfma",
+                     "achieved": round(fflops / (aff * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s",
+                     "frac": round(fflops / (aff * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "traffic": None}}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

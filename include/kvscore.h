@@ -168,6 +168,34 @@ kvs_status kvscore_reliability_weights(const kvs_lore_desc *desc, const void *Q,
                                        float *omega, float *dhat,
                                        void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Attention-output fidelity of a retained cache (LORE-KV page, "Why it
+ * works", "Output fidelity": how closely the retained cache reproduces the
+ * full cache's attention outputs), read as: for each held-out query row r of
+ * query head h, the cosine between o_full = softmax(q K^T / sqrt(d)) V over all
+ * n tokens of the head's KV head and o_kept, the same over the n_keep kept
+ * tokens (renormalised), in the head's value space; fidelity = the mean over
+ * the sequence's heads and rows.  Two zero outputs agree (1); one zero output
+ * gives 0.  Reads desc->batch, n, h_q, h_kv, d, dtype only.
+ *
+ *  Qf       [batch][h_q][n_f][d]      held-out queries, 1 <= n_f <= 64; every
+ *                                     row sees every token (no mask).
+ *  K, V     [batch][h_kv][n][d]       the full cache.
+ *  K_keep, V_keep [batch][h_kv][n_keep][d]  the retained cache (e.g.
+ *                                     kv_compact's output), 1 <= n_keep <= n.
+ *  cos_out  [batch][h_q][n_f] fp32    out: per-row cosines.
+ *  fidelity [batch] fp32              out: their mean per sequence.
+ *  ws, ws_bytes                       workspace (>= kvs_fidelity_workspace_bytes).
+ * The attention outputs carry the precision of kvscore_probs' O; the cosines
+ * are fp32.
+ */
+size_t kvs_fidelity_workspace_bytes(const kvs_lore_desc *desc, int32_t n_f, int32_t n_keep);
+kvs_status kvscore_output_fidelity(const kvs_lore_desc *desc, int32_t n_f, int32_t n_keep,
+                                   const void *Qf, const void *K, const void *V,
+                                   const void *K_keep, const void *V_keep,
+                                   float *cos_out, float *fidelity,
+                                   void *ws, size_t ws_bytes, void *stream);
+
 /* Which prompt-side baseline kvscore_baseline_scores computes. */
 typedef enum { KVS_BASELINE_WINDOW = 0, KVS_BASELINE_TOVA = 1 } kvs_baseline;
 

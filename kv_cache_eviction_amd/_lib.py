@@ -22,7 +22,8 @@ DTYPE_CODE = {torch.float32: KVS_F32, torch.bfloat16: KVS_BF16, torch.float16: K
 CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
 
 EXPORTS = ("kvs_lore_workspace_bytes", "kvs_topb_workspace_bytes", "kvscore_probs", "kvscore_deletion",
-           "kvscore_baseline_scores", "kvscore_reliability_weights", "kvscore_topb_select", "kv_compact", "kvs_h2o_workspace_bytes",
+           "kvscore_baseline_scores", "kvscore_reliability_weights", "kvs_fidelity_workspace_bytes",
+           "kvscore_output_fidelity", "kvscore_topb_select", "kv_compact", "kvs_h2o_workspace_bytes",
            "kvscore_h2o_accumulate", "kvs_timing_enable", "kvs_timing_count", "kvs_timing_read",
            "kvs_timing_reset", "kvs_last_error")
 
@@ -79,6 +80,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     f32 = ctypes.c_float
     lib.kvscore_reliability_weights.restype = i32
     lib.kvscore_reliability_weights.argtypes = [LP, vp, vp, vp, f32, f32, f32, vp, vp, vp, sz, vp]
+    lib.kvs_fidelity_workspace_bytes.restype = sz
+    lib.kvs_fidelity_workspace_bytes.argtypes = [LP, i32, i32]
+    lib.kvscore_output_fidelity.restype = i32
+    lib.kvscore_output_fidelity.argtypes = [LP, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kvs_topb_workspace_bytes.restype = sz
     lib.kvs_topb_workspace_bytes.argtypes = [LP]
     lib.kvscore_topb_select.restype = i32
@@ -235,6 +240,37 @@ def kvscore_reliability_weights(desc, Q, logp, entropy, omega, coef=RELIABILITY_
         ctypes.byref(desc), _ptr(Q), _ptr(logp), _ptr(entropy), beta, gamma, lambda_d,
         _ptr(omega), _ptr(dhat), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)), "kvscore_reliability_weights")
+
+
+def kvs_fidelity_workspace_bytes(desc: LoreDesc, n_f: int, n_keep: int) -> int:
+    nb = load().kvs_fidelity_workspace_bytes(ctypes.byref(desc), int(n_f), int(n_keep))
+    if nb == 0:
+        raise KvsError("invalid fidelity arguments: " + last_error())
+    return nb
+
+
+def kvscore_output_fidelity(desc, Qf, K, V, K_keep, V_keep, cos_out, fidelity, ws, stream=None):
+    """Cosine between each held-out query's attention output over the full
+    cache (K, V) and over the retained cache (K_keep, V_keep), per query head,
+    and the mean per sequence."""
+    dt = CODE_DTYPE[desc.dtype]
+    b, hq, hk, n, d = desc.batch, desc.h_q, desc.h_kv, desc.n, desc.d
+    if Qf is None or K_keep is None:
+        raise KvsError("Qf and K_keep are required")
+    n_f, n_keep = Qf.shape[2], K_keep.shape[2]
+    _need(Qf, "Qf", (b, hq, n_f, d), dt)
+    _need(K, "K", (b, hk, n, d), dt)
+    _need(V, "V", (b, hk, n, d), dt)
+    _need(K_keep, "K_keep", (b, hk, n_keep, d), dt)
+    _need(V_keep, "V_keep", (b, hk, n_keep, d), dt)
+    _need(cos_out, "cos_out", (b, hq, n_f), torch.float32)
+    _need(fidelity, "fidelity", (b,), torch.float32)
+    _ws_check(ws, kvs_fidelity_workspace_bytes(desc, n_f, n_keep))
+    _check(load().kvscore_output_fidelity(ctypes.byref(desc), n_f, n_keep, _ptr(Qf), _ptr(K),
+                                          _ptr(V), _ptr(K_keep), _ptr(V_keep), _ptr(cos_out),
+                                          _ptr(fidelity), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream)),
+           "kvscore_output_fidelity")
 
 
 def kvs_topb_workspace_bytes(desc: LoreDesc) -> int:

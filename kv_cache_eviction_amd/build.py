@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvscore.so")
-SOURCES = ["attn.hip", "deletion.hip", "select.hip", "h2o.hip", "reliability.hip", "timing.cpp",
+SOURCES = ["attn.hip", "deletion.hip", "select.hip", "h2o.hip", "reliability.hip", "fidelity.hip",
+           "timing.cpp",
            "capi.cpp"]
 ARCH = "gfx950"
 

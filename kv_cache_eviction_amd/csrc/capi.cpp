@@ -279,6 +279,90 @@ KVS_API kvs_status kvscore_reliability_weights(const kvs_lore_desc *desc, const 
   return hip_status(e, "reliability weights");
 }
 
+// ---------------------------------------------------------------------------
+// Output fidelity: the attention pass on the full and on the kept cache, then
+// per-row cosines.
+
+kvs_status check_fidelity(const kvs_lore_desc *d, int n_f, int n_keep) {
+  if (!d) return fail(KVS_ERR_INVALID, "descriptor is NULL");
+  if (d->batch < 1 || d->n < 1 || d->h_q < 1 || d->h_kv < 1)
+    return fail(KVS_ERR_INVALID, "batch, n, h_q and h_kv must be >= 1");
+  if (d->h_q % d->h_kv != 0) return fail(KVS_ERR_INVALID, "h_q must be a multiple of h_kv");
+  if (d->h_q / d->h_kv > 16) return fail(KVS_ERR_UNSUPPORTED, "query-head group larger than 16");
+  if (d->d != 64 && d->d != 128) return fail(KVS_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  if (d->n > (1 << 28)) return fail(KVS_ERR_UNSUPPORTED, "n above 2^28 tokens");
+  if (d->dtype != KVS_F32 && d->dtype != KVS_BF16 && d->dtype != KVS_F16)
+    return fail(KVS_ERR_INVALID, "unknown dtype");
+  if (n_f < 1 || n_f > 64) return fail(KVS_ERR_UNSUPPORTED, "n_f must be in [1, 64]");
+  if (n_keep < 1 || n_keep > d->n) return fail(KVS_ERR_INVALID, "n_keep must be in [1, n]");
+  return ok();
+}
+
+struct FidelityPlan {
+  kvs::SplitPlan full, kept;
+  size_t off_pm, off_pl, off_po, off_m, off_l, off_of, off_ok, bytes;
+};
+
+FidelityPlan plan_fidelity(const kvs_lore_desc *d, int n_f, int n_keep) {
+  FidelityPlan p{};
+  const size_t heads = (size_t)d->batch * d->h_q, D = d->d;
+  const int units = d->batch * d->h_kv * kvs::attn_head_split(d->h_q / d->h_kv, true).hsplit;
+  p.full = kvs::attn_split_plan(units, d->n);
+  p.kept = kvs::attn_split_plan(units, n_keep);
+  const size_t S = p.full.splits > p.kept.splits ? p.full.splits : p.kept.splits;
+  p.off_pm = 0;
+  p.off_pl = align_up(p.off_pm + heads * S * 64 * 4);
+  p.off_po = align_up(p.off_pl + heads * S * 64 * 4);
+  p.off_m = align_up(p.off_po + heads * S * D * 64 * 4);
+  p.off_l = align_up(p.off_m + heads * n_f * 4);
+  p.off_of = align_up(p.off_l + heads * n_f * 4);
+  p.off_ok = align_up(p.off_of + heads * n_f * D * 4);
+  p.bytes = align_up(p.off_ok + heads * n_f * D * 4);
+  return p;
+}
+
+KVS_API size_t kvs_fidelity_workspace_bytes(const kvs_lore_desc *desc, int32_t n_f,
+                                            int32_t n_keep) {
+  if (check_fidelity(desc, n_f, n_keep) != KVS_OK) return 0;
+  return plan_fidelity(desc, n_f, n_keep).bytes;
+}
+
+KVS_API kvs_status kvscore_output_fidelity(const kvs_lore_desc *desc, int32_t n_f, int32_t n_keep,
+                                           const void *Qf, const void *K, const void *V,
+                                           const void *K_keep, const void *V_keep,
+                                           float *cos_out, float *fidelity, void *ws,
+                                           size_t ws_bytes, void *stream) {
+  kvs_status st = check_fidelity(desc, n_f, n_keep);
+  if (st != KVS_OK) return st;
+  if (!Qf || !K || !V || !K_keep || !V_keep || !cos_out || !fidelity)
+    return fail(KVS_ERR_INVALID, "kvscore_output_fidelity: a required pointer is NULL");
+  st = check_aligned("kvscore_output_fidelity", {Qf, K, V, K_keep, V_keep});
+  if (st != KVS_OK) return st;
+  const FidelityPlan p = plan_fidelity(desc, n_f, n_keep);
+  st = check_ws(ws, ws_bytes, p.bytes);
+  if (st != KVS_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int group = desc->h_q / desc->h_kv, heads = desc->batch * desc->h_q;
+  float *pm = at<float>(ws, p.off_pm), *pl = at<float>(ws, p.off_pl), *po = at<float>(ws, p.off_po);
+  float *rm = at<float>(ws, p.off_m), *rl = at<float>(ws, p.off_l);
+  float *Of = at<float>(ws, p.off_of), *Ok = at<float>(ws, p.off_ok);
+  // every held-out row sees every token of its cache (no window rows)
+  const kvs::RowGeom gf{0, desc->n, n_f, 0, group}, gk{0, n_keep, n_f, 0, group};
+  hipError_t e = kvs::launch_attn_partial(desc->dtype, desc->d, true, Qf, K, V, gf, desc->batch,
+                                          desc->h_kv, p.full, pm, pl, po, s);
+  if (e != hipSuccess) return hip_status(e, "full-cache attention");
+  e = kvs::launch_attn_combine_lore(desc->d, pm, pl, po, heads, p.full.splits, n_f, rm, rl, Of, s);
+  if (e != hipSuccess) return hip_status(e, "full-cache combine");
+  e = kvs::launch_attn_partial(desc->dtype, desc->d, true, Qf, K_keep, V_keep, gk, desc->batch,
+                               desc->h_kv, p.kept, pm, pl, po, s);
+  if (e != hipSuccess) return hip_status(e, "kept-cache attention");
+  e = kvs::launch_attn_combine_lore(desc->d, pm, pl, po, heads, p.kept.splits, n_f, rm, rl, Ok, s);
+  if (e != hipSuccess) return hip_status(e, "kept-cache combine");
+  e = kvs::launch_output_cosine(desc->d, Of, Ok, desc->batch, desc->h_q * n_f, cos_out, fidelity,
+                                s);
+  return hip_status(e, "output cosine");
+}
+
 KVS_API size_t kvs_topb_workspace_bytes(const kvs_lore_desc *desc) {
   if (check_select(desc) != KVS_OK) return 0;
   return topb_bytes_of(desc);

@@ -55,6 +55,11 @@ hipError_t launch_reliability(int etype, const void *Q, int batch, int h_q, int 
                               float gamma, float lambda_d, float *omega, float *dhat,
                               double *pair_sum, hipStream_t st);
 
+// Output fidelity: cos_out [batch][rows] and its mean per sequence, from the
+// fp32 attention outputs over the full and the kept cache, [batch][rows][d].
+hipError_t launch_output_cosine(int d, const float *Of, const float *Ok, int batch, int rows,
+                                float *cos_out, float *fidelity, hipStream_t st);
+
 // Deletion score pieces.
 int gram_splits(int h_q, int d_model, int elem_bytes);
 // Row constants for the prompt-side baselines (window rows, or the last one).

@@ -50,6 +50,18 @@ class LoreEviction:
                                   self.ws, stream)
         return self.S
 
+    def fidelity(self, Qf, K, V, K_keep, V_keep, stream=None):
+        """Attention-output fidelity of the retained cache under held-out
+        queries Qf [batch][h_q][n_f][d]: (cos [batch][h_q][n_f], mean [batch])."""
+        b, hq, n_f = Qf.shape[0], Qf.shape[1], Qf.shape[2]
+        dev = Qf.device
+        cos = torch.empty(b, hq, n_f, dtype=torch.float32, device=dev)
+        fid = torch.empty(b, dtype=torch.float32, device=dev)
+        nb = L.kvs_fidelity_workspace_bytes(self.desc, n_f, K_keep.shape[2])
+        ws = self.ws if self.ws.numel() >= nb else torch.empty(nb, dtype=torch.uint8, device=dev)
+        L.kvscore_output_fidelity(self.desc, Qf, K, V, K_keep, V_keep, cos, fid, ws, stream)
+        return cos, fid
+
     def select(self, pooled=None, stream=None):
         L.kvscore_topb_select(self.desc, self.S, self.kept, pooled, self.ws, stream)
         return self.kept

@@ -6,8 +6,10 @@ arithmetic lives here.
 
 from .configs import (LoreConfig, H2OConfig, TINY, MISTRAL_16K, LLAMA_128K,
                       QWEN_14B_BATCH, OPT30B_H2O, LORE_CONFIGS, H2O_CONFIGS)
-from .gen import lore_inputs, h2o_inputs, trajectory_token_stats, TORCH_DTYPES
+from .gen import (lore_inputs, h2o_inputs, trajectory_token_stats, future_queries,
+                  TORCH_DTYPES)
 
 __all__ = ["LoreConfig", "H2OConfig", "TINY", "MISTRAL_16K", "LLAMA_128K",
            "QWEN_14B_BATCH", "OPT30B_H2O", "LORE_CONFIGS", "H2O_CONFIGS",
-           "lore_inputs", "h2o_inputs", "trajectory_token_stats", "TORCH_DTYPES"]
+           "lore_inputs", "h2o_inputs", "trajectory_token_stats", "future_queries",
+           "TORCH_DTYPES"]

@@ -124,6 +124,25 @@ def lore_inputs(cfg: LoreConfig, layer: int = 0, device="cpu"):
     }
 
 
+def future_queries(cfg: LoreConfig, inputs, n_f: int, layer: int = 0, device="cpu"):
+    """Held-out "future" queries [b][h_q][n_f][d] (workload dtype) for one
+    layer's inputs: each is 0.6 * k_target + 0.4 * z, z ~ N(0, I), with the
+    target drawn uniformly from the sequence's planted positions (facts or
+    heavy hitters) and k_target its key at the query head's KV head; a stream
+    of its own, separate from the scoring queries'."""
+    gen = _generator(30_000 + cfg.seed + layer, device)
+    K = inputs["K"].to(device=device, dtype=torch.float32)
+    marks = inputs["marks"].to(device)
+    g_of_h = torch.arange(cfg.h_q, device=device) // cfg.group
+    out = []
+    for b in range(cfg.batch):
+        pick = torch.randint(0, marks.shape[1], (cfg.h_q, n_f), generator=gen, device=device)
+        target = marks[b][pick]
+        z = _randn(gen, cfg.h_q, n_f, cfg.d, device=device)
+        out.append(0.6 * K[b][g_of_h[:, None], target] + 0.4 * z)
+    return torch.stack(out).to(TORCH_DTYPES[cfg.dtype])
+
+
 def trajectory_token_stats(cfg: LoreConfig, layer: int = 0, device="cpu"):
     """Per-token statistics of the M sampled continuations, which a model's
     next-token distributions would give: entropy [b][m][t] ~ U(0.5, 4) nats

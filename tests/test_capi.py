@@ -119,6 +119,26 @@ def test_reliability_weights_host_checks():
                                            None, None, None, 0, None) == 0
 
 
+def test_output_fidelity_host_checks():
+    kv, lib = _lib()
+    d = _desc(kv)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: a host check fails first
+    odd = ctypes.c_void_p(0x1008)
+    assert lib.kvs_fidelity_workspace_bytes(ctypes.byref(d), 0, 10) == 0      # no queries
+    assert lib.kvs_fidelity_workspace_bytes(ctypes.byref(d), 65, 10) == 0     # above 64 rows
+    assert lib.kvs_fidelity_workspace_bytes(ctypes.byref(d), 8, 1025) == 0    # n_keep > n
+    need = lib.kvs_fidelity_workspace_bytes(ctypes.byref(d), 8, 200)
+    assert need > 0
+    f = lib.kvscore_output_fidelity
+    assert f(ctypes.byref(d), 8, 0, *([fake] * 7), fake, need, None) == 1
+    assert f(ctypes.byref(d), 8, 200, fake, fake, fake, None, fake, fake, fake, fake, need,
+             None) == 1
+    assert f(ctypes.byref(d), 8, 200, fake, fake, fake, fake, odd, fake, fake, fake, need,
+             None) == 1 and "aligned" in kv.last_error()
+    rc = f(ctypes.byref(d), 8, 200, *([fake] * 7), fake, need - 1, None)
+    assert rc == 3 and "workspace" in kv.last_error()
+
+
 def test_selection_descriptor_needs_only_selection_fields():
     kv, lib = _lib()
     d = kv.lore_desc(batch=2, n=1024, h_q=3, h_kv=3, d=128, d_model=1, w=102, m=0, t=0,

@@ -1,0 +1,113 @@
+"""GPU parity of the attention-output fidelity of a retained cache (LORE-KV
+page, "Why it works", "Output fidelity") against the oracle, through the C
+ABI: the retained cache is the one the GPU path selects and compacts, the
+held-out queries are fresh draws aimed at the planted tokens.
+
+Bar: each cosine within 2e-3 and the mean within 5e-4 of the fp64 oracle on
+the same kept set.  The two attention outputs carry kvscore_probs' error (O
+within 1e-3 of a row's largest component, value-side products on fp16 MFMA
+for 16-bit inputs), and a cosine moves by at most the sum of the two
+outputs' relative errors."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import kv_cache_eviction_amd as kv
+from kvsynth import (TINY, MISTRAL_16K, LLAMA_128K, QWEN_14B_BATCH, lore_inputs, future_queries,
+                     TORCH_DTYPES)
+from parity import lore_desc_kwargs
+
+pytestmark = pytest.mark.gpu
+
+COS_TOL, MEAN_TOL = 2e-3, 5e-4
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kv.load()
+    return torch.device("cuda")
+
+
+def retained(cfg, dev, inp):
+    desc = kv.lore_desc(dtype=TORCH_DTYPES[cfg.dtype], **lore_desc_kwargs(cfg))
+    ev = kv.LoreEviction(desc, dev)
+    Q, K, V, W = (inp[k].to(dev).contiguous() for k in ("Q", "K", "V", "W_O"))
+    omega = inp["omega"].to(dev).contiguous()
+    Ko = torch.empty(cfg.batch, cfg.h_kv, desc.n_keep, cfg.d, dtype=K.dtype, device=dev)
+    Vo = torch.empty_like(Ko)
+    ev.run(Q, K, V, W, omega, Ko, Vo)
+    return desc, ev, K, V, Ko, Vo
+
+
+def compare(cos, fid, ref, name, heads=None):
+    c = cos.cpu().double().numpy()
+    rc = ref["cos"]
+    if heads is not None:
+        c = c[:, heads]
+    err = np.abs(c - rc).max()
+    print("%s: fidelity %s (oracle %s), max |dcos| %.3g" % (
+        name, np.round(fid.cpu().numpy(), 4), np.round(ref["fidelity"], 4), err))
+    assert err <= COS_TOL, name
+    if heads is None:
+        assert np.abs(fid.cpu().double().numpy() - ref["fidelity"]).max() <= MEAN_TOL, name
+
+
+SMALL = [
+    TINY,
+    TINY.with_(name="bf16-d128-g4-b2-n1000", dtype="bf16", d=128, h_q=8, h_kv=2, n=1000,
+               d_model=512, budget=64, batch=2, seed_per_seq=True, seed=31),
+    TINY.with_(name="f16-d64-mha-n777", dtype="f16", d=64, h_q=3, h_kv=3, n=777, d_model=192,
+               w=5, m=2, t=3, chunk=1, budget=50, n_sink=2, seed=32),
+    MISTRAL_16K,
+]
+
+
+@pytest.mark.parametrize("n_f", [64, 7])
+@pytest.mark.parametrize("cfg", SMALL, ids=[c.name for c in SMALL])
+def test_retained_cache(dev, cfg, n_f):
+    inp = lore_inputs(cfg, 0, device=dev)
+    desc, ev, K, V, Ko, Vo = retained(cfg, dev, inp)
+    Qf = future_queries(cfg, inp, n_f, device=dev)
+    cos, fid = ev.fidelity(Qf, K, V, Ko, Vo)
+    torch.cuda.synchronize()
+    ref = oracle.output_fidelity(Qf.cpu(), K.cpu(), V.cpu(), ev.kept.cpu())
+    compare(cos, fid, ref, "%s n_f=%d" % (cfg.name, n_f))
+
+
+def test_keeping_everything_and_one_token(dev):
+    cfg = SMALL[1]
+    inp = lore_inputs(cfg, 0, device=dev)
+    desc = kv.lore_desc(dtype=TORCH_DTYPES[cfg.dtype], **lore_desc_kwargs(cfg))
+    ev = kv.LoreEviction(desc, dev)
+    K, V = inp["K"].contiguous(), inp["V"].contiguous()
+    Qf = future_queries(cfg, inp, 16, device=dev)
+    cos, fid = ev.fidelity(Qf, K, V, K, V)  # the "retained" cache is the whole cache
+    torch.cuda.synchronize()
+    assert torch.all((cos - 1).abs() <= 1e-5)
+    kept = torch.full((cfg.batch, cfg.h_kv, 1), 17, dtype=torch.int64)
+    Ko = K[:, :, 17:18].contiguous()
+    Vo = V[:, :, 17:18].contiguous()
+    cos, fid = ev.fidelity(Qf, K, V, Ko, Vo)  # one kept token: o_kept = v_17
+    torch.cuda.synchronize()
+    ref = oracle.output_fidelity(Qf.cpu(), K.cpu(), V.cpu(), kept)
+    compare(cos, fid, ref, "one kept token")
+
+
+@pytest.mark.parametrize("cfg", [LLAMA_128K, QWEN_14B_BATCH], ids=["llama128k", "qwen14b"])
+def test_full_size_sampled_kv_head(dev, cfg):
+    inp = lore_inputs(cfg, 0, device=dev)
+    desc, ev, K, V, Ko, Vo = retained(cfg, dev, inp)
+    Qf = future_queries(cfg, inp, 64, device=dev)
+    cos, fid = ev.fidelity(Qf, K, V, Ko, Vo)
+    torch.cuda.synchronize()
+    g = 3 % cfg.h_kv
+    bb = cfg.batch - 1
+    heads = list(range(g * cfg.group, (g + 1) * cfg.group))
+    # the oracle on one KV head of one sequence: its query heads against it
+    ref = oracle.output_fidelity(Qf[bb:bb + 1, heads].cpu(), K[bb:bb + 1, g:g + 1].cpu(),
+                                 V[bb:bb + 1, g:g + 1].cpu(), ev.kept[bb:bb + 1, g:g + 1].cpu())
+    compare(cos[bb:bb + 1], fid, ref, "%s seq %d kv head %d" % (cfg.name, bb, g), heads=heads)
