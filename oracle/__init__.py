@@ -14,6 +14,9 @@ Sources followed (cited per function):
   * LORE-KV page, Method, "Reliability weights" (Eqs. 2-4, 10): the
     trajectory weights omega; "Why it works", "Output fidelity": the
     attention-output fidelity of a retained cache.
+  * counter-causal review "Back from the Future", 3.2 (reversed mask over
+    the cached keys and values) and Alg. 3 (memory refresh): counter-causal
+    attention and the refresh selection.
   * LORE-KV page, "The query-reference mismatch" ("Prompt-side eviction") and
     the counter-causal review "Back from the Future", "Prerequisites"
     (TOVA): the prompt-side baseline scores.
@@ -190,6 +193,76 @@ def baseline_scores(Q, K, *, w, kind):
                 s = np.exp(s - s.max())
                 S[bb, g] += s / s.sum() / G
     return S
+
+
+def counter_causal_attention(Q, K, V):
+    """Counter-causal attention over a cache (counter-causal review, 3.2
+    "The approximation: reusing cached K/V with a reversed mask", Steps 1 and
+    3): the fresh query of every cached position i attends only to the cached
+    keys of positions j > i (a strictly upper-triangular mask) with the usual
+    softmax(q k^T / sqrt(d)) weights and original positions.  The last position
+    sees no key (Step 5 treats it separately): its row_max is -inf, row_sum 0
+    and output 0.
+    Q [b][h_q][n][d]; K, V [b][h_kv][n][d] (query head h uses KV head h // G).
+    Returns (row_max [b][h_q][n] in units of q.k/sqrt(d), row_sum, O [b][h_q][n][d]).
+    """
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    b, h_q, n, d = Q.shape
+    G = h_q // K.shape[1]
+    row_max = np.full((b, h_q, n), -np.inf)
+    row_sum = np.zeros((b, h_q, n))
+    O = np.zeros((b, h_q, n, d))
+    for bb in range(b):
+        for h in range(h_q):
+            g = h // G
+            s = Q[bb, h] @ K[bb, g].T / math.sqrt(d)
+            for i in range(n - 1):
+                row = s[i, i + 1:]
+                mx = row.max()
+                p = np.exp(row - mx)
+                row_max[bb, h, i] = mx
+                row_sum[bb, h, i] = p.sum()
+                O[bb, h, i] = p @ V[bb, g, i + 1:] / p.sum()
+    return row_max, row_sum, O
+
+
+def refresh_select(surprise, *, n_sys, J):
+    """Memory refresh selection (counter-causal review, Alg. 3 with design
+    choice 4 and the boundary rule of 3.2 Step 5): of the n = J + h cached
+    tokens keep the J of largest surprise; the n_sys system-prompt tokens are
+    never evicted and the last token is always kept.  Ties go to the lower
+    position; the kept positions are returned in ascending order (so the next
+    refresh's mask still means "later positions").  J = 0 keeps nothing.
+    surprise [b][n]; needs J = 0 or J >= min(n, n_sys + 1).
+    Returns kept [b][min(J, n)] int64.
+    """
+    S = _f64(surprise)
+    b, n = S.shape
+    keep = min(J, n)
+    if keep == 0:
+        return np.zeros((b, 0), dtype=np.int64)
+    protected = sorted(set(range(min(n_sys, n))) | {n - 1})
+    if keep < len(protected):
+        raise ValueError("J smaller than the protected set")
+    kept = np.empty((b, keep), dtype=np.int64)
+    for bb in range(b):
+        rest = [i for i in range(n) if i not in protected]
+        rest.sort(key=lambda i: (-S[bb, i], i))
+        kept[bb] = sorted(protected + rest[:keep - len(protected)])
+    return kept
+
+
+def refresh_gather(K, V, ids, kept):
+    """K' = K[kept], V' = V[kept] on every head, X' = X[kept] (Alg. 3: the kept
+    entries of K, V and the token ids stay in one-to-one correspondence).
+    K, V [b][h][n][d]; ids [b][n]; kept [b][J].  Returns (K', V', X')."""
+    K, V = np.asarray(K), np.asarray(V)
+    ids, kept = np.asarray(ids), np.asarray(kept)
+    b = K.shape[0]
+    Ko = np.stack([K[bb][:, kept[bb]] for bb in range(b)])
+    Vo = np.stack([V[bb][:, kept[bb]] for bb in range(b)])
+    Xo = np.stack([ids[bb][kept[bb]] for bb in range(b)])
+    return Ko, Vo, Xo
 
 
 def output_fidelity(Qf, K, V, kept):
