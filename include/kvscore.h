@@ -196,6 +196,56 @@ kvs_status kvscore_output_fidelity(const kvs_lore_desc *desc, int32_t n_f, int32
                                    float *cos_out, float *fidelity,
                                    void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Counter-causal attention over a cache (counter-causal review "Back from the
+ * Future", 3.2: a strictly upper-triangular mask over the cached keys and
+ * values, with fresh queries at the original positions).  The query of cached
+ * position i attends to the keys of positions j > i only; the last position
+ * sees none (row_max -inf, row_sum 0, O 0; the refresh keeps it regardless).
+ * The outputs feed the caller's layer output and LM head, which turn them into
+ * the surprise logits that kvscore_refresh ranks.  Reads desc->batch, n, h_q,
+ * h_kv, d, dtype only.
+ *
+ *  Q        [batch][h_q][n][d]      the fresh query of every cached position.
+ *  K, V     [batch][h_kv][n][d]     the cache (query head h uses KV head h / (h_q/h_kv)).
+ *  row_max  [batch][h_q][n] fp32    out: max_{j>i} q_i.k_j / sqrt(d).
+ *  row_sum  [batch][h_q][n] fp32    out: sum_{j>i} exp(q_i.k_j/sqrt(d) - row_max).
+ *  O        [batch][h_q][n][d] fp32 out: the attention output of each position.
+ *  ws, ws_bytes                     workspace (>= kvs_counter_causal_workspace_bytes).
+ * Cost: about n^2/2 key visits per query head.  h_q * ceil(n/64) above about
+ * 262000 (one launch's grid) is KVS_ERR_UNSUPPORTED.
+ */
+size_t kvs_counter_causal_workspace_bytes(const kvs_lore_desc *desc);
+kvs_status kvscore_counter_causal(const kvs_lore_desc *desc, const void *Q, const void *K,
+                                  const void *V, float *row_max, float *row_sum, float *O,
+                                  void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Memory refresh (counter-causal review, Alg. 3 "Memory refresh step", design
+ * choice 4, and the last-token rule of 3.2 Step 5): of the n cached tokens
+ * (memory J plus buffer h) keep the J of largest surprise, with the n_sys
+ * system-prompt tokens never evicted and the last token always kept; ties go
+ * to the lower position.  One token-level kept list per sequence serves every
+ * head; K, V and the token ids are gathered with it, in ascending position
+ * order.  J = 0 keeps nothing (no work is enqueued); J >= n keeps all.
+ *
+ *  surprise [batch][n] fp32          the score of each token (larger = keep).
+ *  K, V     [batch][heads][n][d]     the cache (dtype).
+ *  ids      [batch][n] int32, nullable  token ids (with ids_out).
+ *  kept     [batch][min(J,n)] int32  out: kept positions, ascending.
+ *  K_out, V_out [batch][heads][min(J,n)][d]  out: the new memory.
+ *  ids_out  [batch][min(J,n)] int32, nullable  out: their token ids.
+ *  ws, ws_bytes                      workspace (>= kvs_refresh_workspace_bytes).
+ * J in [1, n_sys] (no room for the last token beside the system prompt) is
+ * KVS_ERR_INVALID.
+ */
+size_t kvs_refresh_workspace_bytes(int32_t batch, int32_t n);
+kvs_status kvscore_refresh(int32_t batch, int32_t heads, int32_t n, int32_t d, int32_t dtype,
+                           int32_t n_sys, int32_t J, const float *surprise, const void *K,
+                           const void *V, const int32_t *ids, int32_t *kept, void *K_out,
+                           void *V_out, int32_t *ids_out, void *ws, size_t ws_bytes,
+                           void *stream);
+
 /* Which prompt-side baseline kvscore_baseline_scores computes. */
 typedef enum { KVS_BASELINE_WINDOW = 0, KVS_BASELINE_TOVA = 1 } kvs_baseline;
 

@@ -10,6 +10,8 @@ from ._lib import (KvsError, LoreDesc, H2ODesc, load, last_error, lore_desc, h2o
                    kvs_lore_workspace_bytes, kvs_topb_workspace_bytes, kvscore_probs, kvscore_deletion,
                    kvscore_baseline_scores, kvscore_reliability_weights, RELIABILITY_E,
                    kvs_fidelity_workspace_bytes, kvscore_output_fidelity,
+                   kvs_counter_causal_workspace_bytes, kvscore_counter_causal,
+                   kvs_refresh_workspace_bytes, kvscore_refresh,
                    RELIABILITY_D, kvscore_topb_select, kv_compact, kvs_h2o_workspace_bytes,
                    kvscore_h2o_accumulate, KVS_F32, KVS_BF16, KVS_F16, KVS_H2O_PREFILL,
                    KVS_H2O_DECODE, KVS_BASELINE_WINDOW, KVS_BASELINE_TOVA, DTYPE_CODE, EXPORTS, LIB_PATH, kvs_timing_enable,
@@ -20,6 +22,8 @@ __all__ = ["KvsError", "LoreDesc", "H2ODesc", "load", "last_error", "lore_desc",
            "kvs_lore_workspace_bytes", "kvs_topb_workspace_bytes", "kvscore_probs", "kvscore_deletion",
            "kvscore_baseline_scores", "kvscore_reliability_weights", "RELIABILITY_E",
            "kvs_fidelity_workspace_bytes", "kvscore_output_fidelity",
+           "kvs_counter_causal_workspace_bytes", "kvscore_counter_causal",
+           "kvs_refresh_workspace_bytes", "kvscore_refresh",
            "RELIABILITY_D", "KVS_BASELINE_WINDOW", "KVS_BASELINE_TOVA", "kvscore_topb_select", "kv_compact", "kvs_h2o_workspace_bytes",
            "kvscore_h2o_accumulate", "KVS_F32", "KVS_BF16", "KVS_F16", "KVS_H2O_PREFILL",
            "KVS_H2O_DECODE", "DTYPE_CODE", "EXPORTS", "LIB_PATH", "LoreEviction", "H2OCache",

@@ -23,7 +23,8 @@ CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
 
 EXPORTS = ("kvs_lore_workspace_bytes", "kvs_topb_workspace_bytes", "kvscore_probs", "kvscore_deletion",
            "kvscore_baseline_scores", "kvscore_reliability_weights", "kvs_fidelity_workspace_bytes",
-           "kvscore_output_fidelity", "kvscore_topb_select", "kv_compact", "kvs_h2o_workspace_bytes",
+           "kvscore_output_fidelity", "kvs_counter_causal_workspace_bytes", "kvscore_counter_causal",
+           "kvs_refresh_workspace_bytes", "kvscore_refresh", "kvscore_topb_select", "kv_compact", "kvs_h2o_workspace_bytes",
            "kvscore_h2o_accumulate", "kvs_timing_enable", "kvs_timing_count", "kvs_timing_read",
            "kvs_timing_reset", "kvs_last_error")
 
@@ -84,6 +85,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvs_fidelity_workspace_bytes.argtypes = [LP, i32, i32]
     lib.kvscore_output_fidelity.restype = i32
     lib.kvscore_output_fidelity.argtypes = [LP, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kvs_counter_causal_workspace_bytes.restype = sz
+    lib.kvs_counter_causal_workspace_bytes.argtypes = [LP]
+    lib.kvscore_counter_causal.restype = i32
+    lib.kvscore_counter_causal.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kvs_refresh_workspace_bytes.restype = sz
+    lib.kvs_refresh_workspace_bytes.argtypes = [i32, i32]
+    lib.kvscore_refresh.restype = i32
+    lib.kvscore_refresh.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                    vp, vp, sz, vp]
     lib.kvs_topb_workspace_bytes.restype = sz
     lib.kvs_topb_workspace_bytes.argtypes = [LP]
     lib.kvscore_topb_select.restype = i32
@@ -271,6 +281,60 @@ def kvscore_output_fidelity(desc, Qf, K, V, K_keep, V_keep, cos_out, fidelity, w
                                           _ptr(fidelity), _ptr(ws),
                                           ws.numel() * ws.element_size(), _stream(stream)),
            "kvscore_output_fidelity")
+
+
+def kvs_counter_causal_workspace_bytes(desc: LoreDesc) -> int:
+    nb = load().kvs_counter_causal_workspace_bytes(ctypes.byref(desc))
+    if nb == 0:
+        raise KvsError("invalid descriptor: " + last_error())
+    return nb
+
+
+def kvscore_counter_causal(desc, Q, K, V, row_max, row_sum, O, ws, stream=None):
+    """Every cached position's fresh query attends to the keys after it."""
+    dt = CODE_DTYPE[desc.dtype]
+    b, hq, hk, n, d = desc.batch, desc.h_q, desc.h_kv, desc.n, desc.d
+    _need(Q, "Q", (b, hq, n, d), dt)
+    _need(K, "K", (b, hk, n, d), dt)
+    _need(V, "V", (b, hk, n, d), dt)
+    _need(row_max, "row_max", (b, hq, n), torch.float32)
+    _need(row_sum, "row_sum", (b, hq, n), torch.float32)
+    _need(O, "O", (b, hq, n, d), torch.float32)
+    _ws_check(ws, kvs_counter_causal_workspace_bytes(desc))
+    _check(load().kvscore_counter_causal(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V),
+                                         _ptr(row_max), _ptr(row_sum), _ptr(O), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(stream)),
+           "kvscore_counter_causal")
+
+
+def kvs_refresh_workspace_bytes(batch: int, n: int) -> int:
+    nb = load().kvs_refresh_workspace_bytes(int(batch), int(n))
+    if nb == 0:
+        raise KvsError("invalid refresh sizes: " + last_error())
+    return nb
+
+
+def kvscore_refresh(surprise, K, V, kept, K_out, V_out, *, n_sys, J, ids=None, ids_out=None,
+                    ws=None, stream=None):
+    """Keep the J most surprising of the n cached tokens per sequence (system
+    prompt and last token protected) and gather K, V (and token ids)."""
+    if K is None:
+        raise KvsError("K is required")
+    b, heads, n, d = K.shape
+    keep = min(int(J), n)
+    _need(surprise, "surprise", (b, n), torch.float32)
+    _need(V, "V", (b, heads, n, d), K.dtype)
+    _need(kept, "kept", (b, keep), torch.int32)
+    _need(K_out, "K_out", (b, heads, keep, d), K.dtype)
+    _need(V_out, "V_out", (b, heads, keep, d), K.dtype)
+    _need(ids, "ids", (b, n), torch.int32, optional=True)
+    _need(ids_out, "ids_out", (b, keep), torch.int32, optional=True)
+    _ws_check(ws, kvs_refresh_workspace_bytes(b, n))
+    _check(load().kvscore_refresh(b, heads, n, d, DTYPE_CODE[K.dtype], int(n_sys), int(J),
+                                  _ptr(surprise), _ptr(K), _ptr(V), _ptr(ids), _ptr(kept),
+                                  _ptr(K_out), _ptr(V_out), _ptr(ids_out), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)),
+           "kvscore_refresh")
 
 
 def kvs_topb_workspace_bytes(desc: LoreDesc) -> int:

@@ -29,7 +29,17 @@
 
 namespace kvs {
 
+// Last key row r of virtual head hv sees (-1: none).  Mode 2 (counter-causal):
+// virtual head hv = (query head in the group) * nq + block, row position
+// R = block * 64 + r sees keys R+1 .. n-1, so the last position sees none.
+// The counter-causal forms (REV) are compiled only into the kernels launched
+// with mode 2.
+template <bool REV>
 __device__ __forceinline__ int row_last(const RowGeom &g, int hv, int r) {
+  if constexpr (REV) {
+    const int R = (hv % g.nq) * 64 + r;
+    return R < g.n - 1 ? g.n - 1 : -1;
+  }
   if (g.mode == 0) {
     if (r >= g.nq) return -1;
     return r < g.w ? g.n - g.w + r : g.n - 1;
@@ -38,8 +48,18 @@ __device__ __forceinline__ int row_last(const RowGeom &g, int hv, int r) {
   return R < g.n ? R : -1;
 }
 
+// First key row r of virtual head hv sees (mode 2 only; 0 otherwise).
+template <bool REV>
+__device__ __forceinline__ int row_first(const RowGeom &g, int hv, int r) {
+  if constexpr (REV) return (hv % g.nq) * 64 + r + 1;
+  return 0;
+}
+
 // Index of scoring row r of query head hv (within KV head kvh's group) in Q.
+template <bool REV>
 __device__ __forceinline__ long q_row(const RowGeom &g, int b, int h_kv, int kvh, int hv, int r) {
+  if constexpr (REV)  // Q [b][h_q][n][d], query head kvh * G + hv / nq
+    return (((long)b * h_kv + kvh) * (g.group / g.nq) + hv / g.nq) * g.n + (long)(hv % g.nq) * 64 + r;
   if (g.mode == 0) return (((long)b * h_kv + kvh) * g.group + hv) * g.nq + r;
   return ((long)b * h_kv + kvh) * g.n + (long)hv * 64 + r;
 }
@@ -56,8 +76,11 @@ __device__ __forceinline__ long q_row(const RowGeom &g, int b, int h_kv, int kvh
 // maximum is tracked beside it and the partial (l, O) are brought to it once
 // at the end, so the split outputs are the plain (max, sum, unnormalised O).
 // The visibility mask is applied only on tiles that cross some row's last
-// visible key (or the end of the cache).
-template <typename Tin, int D, bool WITH_O, int MAXW, int QBW>
+// visible key (or the end of the cache).  REV (counter-causal rows, mode 2)
+// adds a first visible key per row: tiles wholly before a wave's rows are
+// skipped, a workgroup starts at the tile of its rows' earliest key, and the
+// tiles that cross a row's first key are masked too.
+template <typename Tin, int D, bool WITH_O, int MAXW, int QBW, bool REV = false>
 __global__ void __launch_bounds__(64 * MAXW)
 attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__restrict__ V,
                     RowGeom geo, int h_kv, int hsplit, int hpw, int tps, int splits,
@@ -102,16 +125,22 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
   const float c = kLog2e * rsqrtf((float)D);
 
   FQ qf[QBW][KS];
-  int lim[QBW];
+  int lim[QBW], lo[QBW];
   int wave_last = -1, wave_first = 0x7FFFFFFF;  // over this wave's visible rows
+  int wave_lo_min = 0x7FFFFFFF, wave_lo_max = 0;  // REV: earliest and latest first keys
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
     const int r = (qb0 + qb) * 16 + col;
-    lim[qb] = spare ? -1 : row_last(geo, hv, r);  // spare waves only stage tiles
+    lim[qb] = spare ? -1 : row_last<REV>(geo, hv, r);  // spare waves only stage tiles
+    lo[qb] = row_first<REV>(geo, hv, r);
     if (lim[qb] >= 0) {
       wave_last = max(wave_last, lim[qb]);
       wave_first = min(wave_first, lim[qb]);
-      const Tin *qp = Q + q_row(geo, b, h_kv, kvh, hv, r) * D;
+      if (REV) {
+        wave_lo_min = min(wave_lo_min, lo[qb]);
+        wave_lo_max = max(wave_lo_max, lo[qb]);
+      }
+      const Tin *qp = Q + q_row<REV>(geo, b, h_kv, kvh, hv, r) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = load8<Tin>(qp + ks * 32 + 8 * grp);
     } else {
@@ -123,6 +152,10 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
   for (int o = 1; o < 64; o <<= 1) {
     wave_last = max(wave_last, __shfl_xor(wave_last, o, 64));
     wave_first = min(wave_first, __shfl_xor(wave_first, o, 64));
+    if (REV) {
+      wave_lo_min = min(wave_lo_min, __shfl_xor(wave_lo_min, o, 64));
+      wave_lo_max = max(wave_lo_max, __shfl_xor(wave_lo_max, o, 64));
+    }
   }
 
   // mref: reference max of the exponentials (log2 units), negm = -mref (0
@@ -216,11 +249,22 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
     }
   };
 
+  // REV: no row of this workgroup sees a key before its heads' earliest first
+  // key, so the tiles before it are neither loaded nor computed
+  int it0 = 0;
+  if (REV) {
+    int wg_lo = 0x7FFFFFFF;
+    for (int h2 = 0; h2 < hpw; ++h2) {
+      const int v = hs * hpw + h2;
+      if (v < geo.group) wg_lo = min(wg_lo, (v % geo.nq) * 64 + 1);
+    }
+    if (wg_lo > t_begin) it0 = min(nt, (wg_lo - t_begin) / TN);
+  }
   wait_vmem_all();
-  prefetch(t_begin);
-  stash(0);
+  prefetch(t_begin + it0 * TN);
+  stash(it0 & 1);
   __syncthreads();
-  for (int it = 0; it < nt; ++it) {
+  for (int it = it0; it < nt; ++it) {
     const int t0 = t_begin + it * TN;
     const int cur = it & 1;
     prefetch(t0 + TN);  // past the split end this reads nothing
@@ -266,7 +310,7 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int tok = t0 + (tb >> 1) * 32 + 8 * grp + 4 * (tb & 1) + j;
-              if (tok > lim[qb]) sacc[tb][qb][j] = -INFINITY;
+              if (tok > lim[qb] || (REV && tok < lo[qb])) sacc[tb][qb][j] = -INFINITY;
             }
       }
 
@@ -326,8 +370,8 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
         }
       }
     };
-    if (t0 <= wave_last) {
-      if (t0 + TN - 1 > wave_first) tile(std::true_type{});
+    if (t0 <= wave_last && (!REV || t0 + TN - 1 >= wave_lo_min)) {
+      if (t0 + TN - 1 > wave_first || (REV && t0 < wave_lo_max)) tile(std::true_type{});
       else tile(std::false_type{});
     }
     stash(cur ^ 1);
@@ -366,10 +410,14 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
 // the four waves share the split weights: each takes every fourth split for
 // the row maximum and the weighted row sum, combined through LDS, so no
 // thread waits on a serial chain of loads.
+// With nblk > 0 (counter-causal rows) virtual head `head` is block
+// head % nblk of query head head / nblk, and its row q lands at position
+// (head % nblk) * 64 + q of that head's n_rows rows (positions >= n_rows are
+// padding).  A row that saw no key gets row_sum 0 and O = 0.
 template <int D>
 __global__ void __launch_bounds__(256)
 attn_combine_lore_kernel(const float *__restrict__ pm, const float *__restrict__ pl,
-                         const float *__restrict__ pO, int splits, int nq,
+                         const float *__restrict__ pO, int splits, int nq, int nblk, int n_rows,
                          float *__restrict__ row_max, float *__restrict__ row_sum,
                          float *__restrict__ O) {
   constexpr int CH = 32;           // partial-O values held in registers per pass
@@ -411,9 +459,19 @@ attn_combine_lore_kernel(const float *__restrict__ pm, const float *__restrict__
   psum[part * 64 + q] = lloc;
   __syncthreads();
   const float L = (psum[q] + psum[64 + q]) + (psum[128 + q] + psum[192 + q]);
-  if (part == 0 && q < nq && blockIdx.y == 0) {
-    row_max[head * nq + q] = M * kLn2;
-    row_sum[head * nq + q] = L;
+  long orow;
+  bool valid;
+  if (nblk > 0) {
+    const int pos = (int)(head % nblk) * 64 + q;
+    orow = (head / nblk) * n_rows + pos;
+    valid = pos < n_rows;
+  } else {
+    orow = head * nq + q;
+    valid = q < nq;
+  }
+  if (part == 0 && valid && blockIdx.y == 0) {
+    row_max[orow] = M * kLn2;
+    row_sum[orow] = L;
   }
   float o = 0.f;
   for (int s0 = 0; s0 < splits; s0 += CH) {
@@ -425,7 +483,7 @@ attn_combine_lore_kernel(const float *__restrict__ pm, const float *__restrict__
     for (int u = 0; u < CH; ++u)
       if (s0 + u < splits) o += ov[u] * wsh[(s0 + u) * 64 + q];
   }
-  if (q < nq) O[(head * nq + q) * D + d] = o * (1.f / L);
+  if (valid) O[orow * D + d] = L > 0.f ? o * (1.f / L) : 0.f;
 }
 
 // H2O prefill: merge the splits into per-row constants for the column-sum
@@ -478,7 +536,7 @@ HeadSplit attn_head_split(int group, bool with_o) {
   return h;
 }
 
-template <typename Tin, int D, bool WITH_O, int MAXW, int QBW>
+template <typename Tin, int D, bool WITH_O, int MAXW, int QBW, bool REV = false>
 static hipError_t run_partial(const void *Q, const void *K, const void *V, RowGeom geo, int batch,
                               int h_kv, HeadSplit hs, SplitPlan plan, float *pm, float *pl,
                               float *pO, hipStream_t st) {
@@ -489,7 +547,7 @@ static hipError_t run_partial(const void *Q, const void *K, const void *V, RowGe
   if (need < 1 || need > MAXW || hs.hsplit * hs.hpw < geo.group) return hipErrorInvalidConfiguration;
   {
     TimedLaunch tl_("attn_partial", st);
-    hipLaunchKernelGGL((attn_partial_kernel<Tin, D, WITH_O, MAXW, QBW>), grid, block, 0, st,
+    hipLaunchKernelGGL((attn_partial_kernel<Tin, D, WITH_O, MAXW, QBW, REV>), grid, block, 0, st,
                        (const Tin *)Q, (const Tin *)K, (const Tin *)V, geo, h_kv, hs.hsplit,
                        hs.hpw, plan.tps, plan.splits, pm, pl, pO);
   }
@@ -503,6 +561,12 @@ static hipError_t run_partial_d(bool with_o, const void *Q, const void *K, const
   const HeadSplit hs = attn_head_split(geo.group, with_o);
 #define KVS_RP(O, MAXW, QBW) \
   return run_partial<Tin, D, O, MAXW, QBW>(Q, K, V, geo, batch, h_kv, hs, plan, pm, pl, pO, st)
+  if (geo.mode == 2) {  // counter-causal rows: always with O
+    if (!with_o) return hipErrorInvalidValue;
+    if (hs.maxw == 2) return run_partial<Tin, D, true, 2, 2, true>(Q, K, V, geo, batch, h_kv, hs, plan, pm, pl, pO, st);
+    if (hs.maxw == 4) return run_partial<Tin, D, true, 4, 2, true>(Q, K, V, geo, batch, h_kv, hs, plan, pm, pl, pO, st);
+    return run_partial<Tin, D, true, 8, 2, true>(Q, K, V, geo, batch, h_kv, hs, plan, pm, pl, pO, st);
+  }
   if (!with_o) {
     if (hs.maxw == 2) KVS_RP(false, 2, 4);
     if (hs.maxw == 4) KVS_RP(false, 4, 4);
@@ -534,10 +598,27 @@ hipError_t launch_attn_combine_lore(int d, const float *part_m, const float *par
     TimedLaunch tl_("attn_combine", st);
     if (d == 64)
       hipLaunchKernelGGL(attn_combine_lore_kernel<64>, dim3(heads, 64 / 4), dim3(256), shm, st,
-                         part_m, part_l, part_O, splits, nq, row_max, row_sum, O);
+                         part_m, part_l, part_O, splits, nq, 0, 0, row_max, row_sum, O);
     else
       hipLaunchKernelGGL(attn_combine_lore_kernel<128>, dim3(heads, 128 / 4), dim3(256), shm, st,
-                         part_m, part_l, part_O, splits, nq, row_max, row_sum, O);
+                         part_m, part_l, part_O, splits, nq, 0, 0, row_max, row_sum, O);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_combine_rev(int d, const float *part_m, const float *part_l,
+                                   const float *part_O, int vheads, int splits, int nblk, int n,
+                                   float *row_max, float *row_sum, float *O, hipStream_t st) {
+  const size_t shm = sizeof(float) * 64 * ((size_t)splits + 8);
+  if (nblk < 1) return hipErrorInvalidValue;
+  {
+    TimedLaunch tl_("attn_combine", st);
+    if (d == 64)
+      hipLaunchKernelGGL(attn_combine_lore_kernel<64>, dim3(vheads, 64 / 4), dim3(256), shm, st,
+                         part_m, part_l, part_O, splits, 64, nblk, n, row_max, row_sum, O);
+    else
+      hipLaunchKernelGGL(attn_combine_lore_kernel<128>, dim3(vheads, 128 / 4), dim3(256), shm, st,
+                         part_m, part_l, part_O, splits, 64, nblk, n, row_max, row_sum, O);
   }
   return hipGetLastError();
 }

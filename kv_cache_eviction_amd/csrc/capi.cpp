@@ -363,6 +363,124 @@ KVS_API kvs_status kvscore_output_fidelity(const kvs_lore_desc *desc, int32_t n_
   return hip_status(e, "output cosine");
 }
 
+// ---------------------------------------------------------------------------
+// Counter-causal attention: every cached position's fresh query over the keys
+// after it (RowGeom mode 2, virtual heads of 64 positions).
+
+kvs_status check_counter_causal(const kvs_lore_desc *d) {
+  if (!d) return fail(KVS_ERR_INVALID, "descriptor is NULL");
+  if (d->batch < 1 || d->n < 1 || d->h_q < 1 || d->h_kv < 1)
+    return fail(KVS_ERR_INVALID, "batch, n, h_q and h_kv must be >= 1");
+  if (d->h_q % d->h_kv != 0) return fail(KVS_ERR_INVALID, "h_q must be a multiple of h_kv");
+  if (d->d != 64 && d->d != 128) return fail(KVS_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  if (d->n > (1 << 22)) return fail(KVS_ERR_UNSUPPORTED, "n above 2^22 tokens");
+  if (d->dtype != KVS_F32 && d->dtype != KVS_BF16 && d->dtype != KVS_F16)
+    return fail(KVS_ERR_INVALID, "unknown dtype");
+  // workgroups per KV head (grid y) grow with the query heads' 64-row blocks
+  const long group = (long)(d->h_q / d->h_kv) * ((d->n + 63) / 64);
+  if ((long)d->h_kv * ((group * 2 + 7) / 8) > 65535)
+    return fail(KVS_ERR_UNSUPPORTED, "counter-causal: h_q * ceil(n/64) too large for one launch");
+  return ok();
+}
+
+struct CounterCausalPlan {
+  kvs::RowGeom geo;
+  kvs::SplitPlan split;
+  int nblk, vheads;
+  size_t off_pm, off_pl, off_po, bytes;
+};
+
+CounterCausalPlan plan_counter_causal(const kvs_lore_desc *d) {
+  CounterCausalPlan p{};
+  const int G = d->h_q / d->h_kv;
+  p.nblk = (d->n + 63) / 64;
+  p.geo = kvs::RowGeom{2, d->n, p.nblk, 0, G * p.nblk};
+  p.vheads = d->batch * d->h_q * p.nblk;
+  p.split = kvs::attn_split_plan(
+      d->batch * d->h_kv * kvs::attn_head_split(p.geo.group, true).hsplit, d->n);
+  const size_t S = p.split.splits, V = (size_t)p.vheads;
+  p.off_pm = 0;
+  p.off_pl = align_up(p.off_pm + V * S * 64 * 4);
+  p.off_po = align_up(p.off_pl + V * S * 64 * 4);
+  p.bytes = align_up(p.off_po + V * S * (size_t)d->d * 64 * 4);
+  return p;
+}
+
+KVS_API size_t kvs_counter_causal_workspace_bytes(const kvs_lore_desc *desc) {
+  if (check_counter_causal(desc) != KVS_OK) return 0;
+  return plan_counter_causal(desc).bytes;
+}
+
+KVS_API kvs_status kvscore_counter_causal(const kvs_lore_desc *desc, const void *Q, const void *K,
+                                          const void *V, float *row_max, float *row_sum,
+                                          float *O, void *ws, size_t ws_bytes, void *stream) {
+  kvs_status st = check_counter_causal(desc);
+  if (st != KVS_OK) return st;
+  if (!Q || !K || !V || !row_max || !row_sum || !O)
+    return fail(KVS_ERR_INVALID, "kvscore_counter_causal: a required pointer is NULL");
+  st = check_aligned("kvscore_counter_causal", {Q, K, V, O});
+  if (st != KVS_OK) return st;
+  const CounterCausalPlan p = plan_counter_causal(desc);
+  st = check_ws(ws, ws_bytes, p.bytes);
+  if (st != KVS_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float *pm = at<float>(ws, p.off_pm), *pl = at<float>(ws, p.off_pl), *po = at<float>(ws, p.off_po);
+  hipError_t e = kvs::launch_attn_partial(desc->dtype, desc->d, true, Q, K, V, p.geo, desc->batch,
+                                          desc->h_kv, p.split, pm, pl, po, s);
+  if (e != hipSuccess) return hip_status(e, "counter-causal attention");
+  e = kvs::launch_attn_combine_rev(desc->d, pm, pl, po, p.vheads, p.split.splits, p.nblk, desc->n,
+                                   row_max, row_sum, O, s);
+  return hip_status(e, "counter-causal combine");
+}
+
+// ---------------------------------------------------------------------------
+// Memory refresh: keep the J most surprising of the n cached tokens (system
+// prompt and last token protected), then gather K, V and the token ids with
+// one token-level kept list per sequence.
+
+KVS_API size_t kvs_refresh_workspace_bytes(int32_t batch, int32_t n) {
+  if (batch < 1 || n < 1) {
+    fail(KVS_ERR_INVALID, "kvs_refresh_workspace_bytes: batch and n must be >= 1");
+    return 0;
+  }
+  return align_up(kvs::topb_workspace_bytes(batch, n, 1));
+}
+
+KVS_API kvs_status kvscore_refresh(int32_t batch, int32_t heads, int32_t n, int32_t d,
+                                   int32_t dtype, int32_t n_sys, int32_t J,
+                                   const float *surprise, const void *K, const void *V,
+                                   const int32_t *ids, int32_t *kept, void *K_out, void *V_out,
+                                   int32_t *ids_out, void *ws, size_t ws_bytes, void *stream) {
+  if (batch < 1 || heads < 1 || n < 1)
+    return fail(KVS_ERR_INVALID, "kvscore_refresh: batch, heads and n must be >= 1");
+  if (n > (1 << 28)) return fail(KVS_ERR_UNSUPPORTED, "kvscore_refresh: n above 2^28 tokens");
+  if (d != 64 && d != 128) return fail(KVS_ERR_UNSUPPORTED, "kvscore_refresh: head dim must be 64 or 128");
+  if (dtype != KVS_F32 && dtype != KVS_BF16 && dtype != KVS_F16)
+    return fail(KVS_ERR_INVALID, "kvscore_refresh: unknown dtype");
+  if (n_sys < 0 || J < 0) return fail(KVS_ERR_INVALID, "kvscore_refresh: n_sys and J must be >= 0");
+  if (J == 0) return ok();  // nothing survives the refresh
+  const int keep = J < n ? J : n;
+  const int n_sink = n_sys < n - 1 ? n_sys : n - 1;
+  if (keep < n_sink + 1)
+    return fail(KVS_ERR_INVALID, "kvscore_refresh: J leaves no room beside the system prompt for the last token");
+  if (!surprise || !K || !V || !kept || !K_out || !V_out)
+    return fail(KVS_ERR_INVALID, "kvscore_refresh: a required pointer is NULL");
+  if ((ids == nullptr) != (ids_out == nullptr))
+    return fail(KVS_ERR_INVALID, "kvscore_refresh: ids and ids_out go together");
+  kvs_status st = check_aligned("kvscore_refresh", {K, V, K_out, V_out});
+  if (st != KVS_OK) return st;
+  st = check_ws(ws, ws_bytes, align_up(kvs::topb_workspace_bytes(batch, n, 1)));
+  if (st != KVS_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = kvs::launch_topb(surprise, batch, n, n_sink, 1, 1, keep - n_sink - 1, keep, ws,
+                                  kept, nullptr, s);
+  if (e != hipSuccess) return hip_status(e, "refresh selection");
+  const int row_bytes = d * (int)kvs::elem_bytes(dtype);
+  e = kvs::launch_compact(batch * heads, n, keep, keep, row_bytes, K, V, kept, K_out, V_out,
+                          nullptr, ids, ids_out, s, heads);
+  return hip_status(e, "refresh gather");
+}
+
 KVS_API size_t kvs_topb_workspace_bytes(const kvs_lore_desc *desc) {
   if (check_select(desc) != KVS_OK) return 0;
   return topb_bytes_of(desc);

@@ -14,9 +14,10 @@ inline size_t elem_bytes(int t) { return t == E_F32 ? 4 : 2; }
 
 // Geometry of the scoring rows (see attn.hip).
 struct RowGeom {
-  int mode;   // 0: LORE scoring rows; 1: causal prompt rows (H2O prefill)
+  int mode;   // 0: LORE scoring rows; 1: causal prompt rows (H2O prefill);
+              // 2: counter-causal rows (row at position R sees keys R+1 .. n-1)
   int n;      // keys per KV head (LORE: cache length; H2O: prompt length)
-  int nq;     // LORE: rows per query head
+  int nq;     // LORE: rows per query head; counter-causal: 64-row blocks per query head
   int w;      // LORE: window rows
   int group;  // query heads (H2O: virtual heads of 64 prompt rows) per KV head
 };
@@ -43,6 +44,11 @@ hipError_t launch_attn_partial(int etype, int d, bool with_o, const void *Q, con
 hipError_t launch_attn_combine_lore(int d, const float *part_m, const float *part_l,
                                     const float *part_O, int heads, int splits, int nq,
                                     float *row_max, float *row_sum, float *O, hipStream_t st);
+// Counter-causal rows (RowGeom mode 2): vheads = batch * h_q * nblk virtual
+// heads of 64 rows; writes row_max, row_sum [batch*h_q][n] and O [batch*h_q][n][d].
+hipError_t launch_attn_combine_rev(int d, const float *part_m, const float *part_l,
+                                   const float *part_O, int vheads, int splits, int nblk, int n,
+                                   float *row_max, float *row_sum, float *O, hipStream_t st);
 // H2O: writes per-row constants {beta2, 0, 1, last-visible bits} [heads][64].
 hipError_t launch_attn_combine_rows(const float *part_m, const float *part_l, int heads,
                                     int splits, int group, int P, float4 *consts, hipStream_t st);
@@ -85,10 +91,12 @@ hipError_t launch_score(int etype, int d, int mode, const void *Q, const void *K
 size_t topb_workspace_bytes(int rows, int n, int chunk);
 hipError_t launch_topb(const float *S, int rows, int n, int n_sink, int w, int chunk, int budget,
                        int n_keep, void *ws, int32_t *kept, float *pooled, hipStream_t st);
+// kept [rows / kept_div][n_keep]: rows share lists in groups of kept_div;
+// pos_out and the 32-bit payload have one row per list.
 hipError_t launch_compact(int rows, int n_src, int n_keep, int cap_dst, int row_bytes,
                           const void *K, const void *V, const int32_t *kept, void *K_out,
-                          void *V_out, int32_t *pos_out, const float *score_in,
-                          float *score_out, hipStream_t st);
+                          void *V_out, int32_t *pos_out, const void *payload_in,
+                          void *payload_out, hipStream_t st, int kept_div = 1);
 
 // H2O decode step.
 hipError_t launch_h2o_decode(int etype, int d, int rows, int cap, int cur_len, int k_heavy,

@@ -370,45 +370,54 @@ hipError_t launch_topb(const float *S, int rows, int n, int n_sink, int w, int c
 }
 
 // Compaction: K'[row][r] = K[row][kept[r]] (and V), 16 bytes per thread.
+// Rows share kept lists in groups of kept_div (1: one list per row; the head
+// count: one token-level list per sequence).  pos_out and the 32-bit payload
+// (scores, or token ids) follow the kept list: one entry per list, written by
+// the first row of its group.
 __global__ void __launch_bounds__(256)
 compact_kernel(const uint8_t *__restrict__ K, const uint8_t *__restrict__ V,
-               const int32_t *__restrict__ kept, int n_src, int n_keep, int cap, int cpr,
-               uint8_t *__restrict__ Ko, uint8_t *__restrict__ Vo, int32_t *__restrict__ pos_out,
-               const float *__restrict__ sin, float *__restrict__ sout) {
+               const int32_t *__restrict__ kept, int kept_div, int n_src, int n_keep, int cap,
+               int cpr, uint8_t *__restrict__ Ko, uint8_t *__restrict__ Vo,
+               int32_t *__restrict__ pos_out, const uint32_t *__restrict__ pin,
+               uint32_t *__restrict__ pout) {
   const long row = blockIdx.y;
+  const long krow = row / kept_div;
+  const bool lead = row % kept_div == 0;
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const int r = (int)(idx / cpr), c = (int)(idx % cpr);
   if (r >= cap) return;
   const long rb = (long)cpr * 16;
-  const int src = r < n_keep ? kept[row * n_keep + r] : -1;
+  const int src = r < n_keep ? kept[krow * n_keep + r] : -1;
   if (src >= 0 && src < n_src) {
     const long so = (row * n_src + src) * rb + c * 16;
     const long dof = (row * cap + r) * rb + c * 16;
     *reinterpret_cast<U128 *>(Ko + dof) = *reinterpret_cast<const U128 *>(K + so);
     *reinterpret_cast<U128 *>(Vo + dof) = *reinterpret_cast<const U128 *>(V + so);
-    if (c == 0) {
-      if (pos_out) pos_out[row * cap + r] = src;
-      if (sout) sout[row * cap + r] = sin[row * n_src + src];
+    if (c == 0 && lead) {
+      if (pos_out) pos_out[krow * cap + r] = src;
+      if (pout) pout[krow * cap + r] = pin[krow * n_src + src];
     }
-  } else if (c == 0) {  // beyond n_keep, or an index outside [0, n_src): nothing copied
-    if (pos_out) pos_out[row * cap + r] = -1;
-    if (sout) sout[row * cap + r] = 0.f;
+  } else if (c == 0 && lead) {  // beyond n_keep, or an index outside [0, n_src): nothing copied
+    if (pos_out) pos_out[krow * cap + r] = -1;
+    if (pout) pout[krow * cap + r] = 0u;
   }
 }
 
 hipError_t launch_compact(int rows, int n_src, int n_keep, int cap_dst, int row_bytes,
                           const void *K, const void *V, const int32_t *kept, void *K_out,
-                          void *V_out, int32_t *pos_out, const float *score_in,
-                          float *score_out, hipStream_t st) {
+                          void *V_out, int32_t *pos_out, const void *payload_in,
+                          void *payload_out, hipStream_t st, int kept_div) {
   const int cpr = row_bytes / 16;
   const long threads = (long)cap_dst * cpr;
   const int blocks = (int)((threads + 255) / 256);
   if (blocks == 0 || rows == 0) return hipSuccess;
+  if (kept_div < 1 || rows % kept_div != 0) return hipErrorInvalidValue;
   {
     TimedLaunch tl_("compact", st);
     hipLaunchKernelGGL(compact_kernel, dim3(blocks, rows), dim3(256), 0, st, (const uint8_t *)K,
-                       (const uint8_t *)V, kept, n_src, n_keep, cap_dst, cpr, (uint8_t *)K_out,
-                       (uint8_t *)V_out, pos_out, score_in, score_out);
+                       (const uint8_t *)V, kept, kept_div, n_src, n_keep, cap_dst, cpr,
+                       (uint8_t *)K_out, (uint8_t *)V_out, pos_out, (const uint32_t *)payload_in,
+                       (uint32_t *)payload_out);
   }
   return hipGetLastError();
 }

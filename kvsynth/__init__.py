@@ -4,12 +4,12 @@ Holds input shapes and input draws only; no scoring, selection or eviction
 arithmetic lives here.
 """
 
-from .configs import (LoreConfig, H2OConfig, TINY, MISTRAL_16K, LLAMA_128K,
-                      QWEN_14B_BATCH, OPT30B_H2O, LORE_CONFIGS, H2O_CONFIGS)
+from .configs import (LoreConfig, H2OConfig, RefreshConfig, TINY, MISTRAL_16K, LLAMA_128K,
+                      QWEN_14B_BATCH, OPT30B_H2O, QWEN7B_REFRESH, LORE_CONFIGS, H2O_CONFIGS)
 from .gen import (lore_inputs, h2o_inputs, trajectory_token_stats, future_queries,
-                  TORCH_DTYPES)
+                  refresh_inputs, TORCH_DTYPES)
 
-__all__ = ["LoreConfig", "H2OConfig", "TINY", "MISTRAL_16K", "LLAMA_128K",
+__all__ = ["LoreConfig", "H2OConfig", "RefreshConfig", "QWEN7B_REFRESH", "refresh_inputs", "TINY", "MISTRAL_16K", "LLAMA_128K",
            "QWEN_14B_BATCH", "OPT30B_H2O", "LORE_CONFIGS", "H2O_CONFIGS",
            "lore_inputs", "h2o_inputs", "trajectory_token_stats", "future_queries",
            "TORCH_DTYPES"]

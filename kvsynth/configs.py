@@ -122,5 +122,36 @@ QWEN_14B_BATCH = LoreConfig(name="qwen2.5-14b-8x32k", batch=8, n=32768, h_q=40,
 OPT30B_H2O = H2OConfig(name="opt30b-h2o-b64-p1024-g512", batch=64, heads=56, d=128,
                        prompt=1024, steps=512, dtype="f16", seed=505)
 
+@dataclass(frozen=True)
+class RefreshConfig:
+    """A counter-causal memory refresh: memory J, buffer h = J/4 (the review's
+    Design choice 3), n = J + h cached tokens, n_sys system-prompt sinks."""
+    name: str
+    batch: int
+    h_q: int
+    h_kv: int
+    d: int
+    J: int
+    n_sys: int
+    dtype: str
+    seed: int
+
+    @property
+    def h(self) -> int:
+        return self.J // 4
+
+    @property
+    def n(self) -> int:
+        return self.J + self.h
+
+    def with_(self, **kw) -> "RefreshConfig":
+        return replace(self, **kw)
+
+
+# Qwen2.5-7B-shaped layer (28 query heads, 4 KV heads) at the largest cache
+# the counter-causal review times (4096 kept tokens), bf16.
+QWEN7B_REFRESH = RefreshConfig(name="qwen2.5-7b-refresh-J4096", batch=1, h_q=28, h_kv=4, d=128,
+                               J=4096, n_sys=64, dtype="bf16", seed=606)
+
 LORE_CONFIGS = {c.name: c for c in (TINY, MISTRAL_16K, LLAMA_128K, QWEN_14B_BATCH)}
 H2O_CONFIGS = {OPT30B_H2O.name: OPT30B_H2O}

@@ -34,7 +34,7 @@ draws the per-step q, k, v ~ N(0, 1) of shape [steps][b][H][d].
 
 import torch
 
-from .configs import LoreConfig, H2OConfig
+from .configs import LoreConfig, H2OConfig, RefreshConfig
 
 TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
@@ -141,6 +141,24 @@ def future_queries(cfg: LoreConfig, inputs, n_f: int, layer: int = 0, device="cp
         z = _randn(gen, cfg.h_q, n_f, cfg.d, device=device)
         out.append(0.6 * K[b][g_of_h[:, None], target] + 0.4 * z)
     return torch.stack(out).to(TORCH_DTYPES[cfg.dtype])
+
+
+def refresh_inputs(cfg: RefreshConfig, device="cpu"):
+    """Inputs of one counter-causal refresh: fresh queries Q [b][h_q][n][d] and
+    the cache K, V [b][h_kv][n][d] ~ N(0, 1) in the workload dtype; the
+    surprise [b][n] ~ N(0, 1) fp32 (what the LM head's logits would give) and
+    token ids [b][n] ~ U[0, 151936) int32 (Qwen2.5's vocabulary size)."""
+    gen = _generator(cfg.seed, device)
+    dt = TORCH_DTYPES[cfg.dtype]
+    n = cfg.n
+    return {
+        "Q": _randn(gen, cfg.batch, cfg.h_q, n, cfg.d, device=device).to(dt),
+        "K": _randn(gen, cfg.batch, cfg.h_kv, n, cfg.d, device=device).to(dt),
+        "V": _randn(gen, cfg.batch, cfg.h_kv, n, cfg.d, device=device).to(dt),
+        "surprise": _randn(gen, cfg.batch, n, device=device),
+        "ids": torch.randint(0, 151936, (cfg.batch, n), generator=gen, device=device,
+                             dtype=torch.int32),
+    }
 
 
 def trajectory_token_stats(cfg: LoreConfig, layer: int = 0, device="cpu"):

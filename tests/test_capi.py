@@ -139,6 +139,30 @@ def test_output_fidelity_host_checks():
     assert rc == 3 and "workspace" in kv.last_error()
 
 
+def test_counter_causal_and_refresh_host_checks():
+    kv, lib = _lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: a host check fails first
+    d = _desc(kv, n=5120, h_q=28, h_kv=4)
+    need = lib.kvs_counter_causal_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    assert lib.kvscore_counter_causal(ctypes.byref(d), fake, fake, None, fake, fake, fake, fake,
+                                      need, None) == 1
+    assert lib.kvscore_counter_causal(ctypes.byref(d), *([fake] * 7), need - 1, None) == 3
+    big = _desc(kv, n=1 << 21, h_q=64, h_kv=8)  # one launch's grid would be too tall
+    assert lib.kvs_counter_causal_workspace_bytes(ctypes.byref(big)) == 0
+    r = lib.kvscore_refresh
+    ws = lib.kvs_refresh_workspace_bytes(2, 640)
+    assert ws > 0 and lib.kvs_refresh_workspace_bytes(0, 640) == 0
+    args = (fake, fake, fake, None, fake, fake, fake, None, fake, ws, None)
+    # J = 0 enqueues nothing and reads no pointer
+    assert r(2, 4, 640, 128, 1, 16, 0, *([None] * 9), 0, None) == 0
+    assert r(2, 4, 640, 128, 1, 16, 16, *args) == 1       # no room for the last token
+    assert r(2, 4, 640, 96, 1, 16, 64, *args) == 2        # head dim
+    assert r(2, 4, 640, 128, 1, 16, 64, *([fake] * 7), None, fake, ws,
+             None) == 1                                   # ids without ids_out
+    assert r(2, 4, 640, 128, 1, 16, 64, *args[:-2], ws - 1, None) == 3
+
+
 def test_selection_descriptor_needs_only_selection_fields():
     kv, lib = _lib()
     d = kv.lore_desc(batch=2, n=1024, h_q=3, h_kv=3, d=128, d_model=1, w=102, m=0, t=0,
