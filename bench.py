@@ -222,6 +222,55 @@ def bench_compact_qwen(kv, torch, dev, reps=20):
                          "traffic": None}}
 
 
+def bench_refresh(kv, torch, dev, reps=10):
+    """Counter-causal memory refresh on a Qwen2.5-7B-shaped layer (J = 4096,
+    h = J/4, n = 5120): the reversed-mask attention of every cached position
+    (MFMA-bound: 2*d*n*(n-1) flops per query head over the upper triangle),
+    then the token-level keep-J selection and the K, V, id gather."""
+    from kvsynth import QWEN7B_REFRESH as cfg, refresh_inputs
+    x = refresh_inputs(cfg, device=dev)
+    b, n = cfg.batch, cfg.n
+    desc = kv.lore_desc(batch=b, n=n, h_q=cfg.h_q, h_kv=cfg.h_kv, d=cfg.d, d_model=cfg.h_q * cfg.d,
+                        w=0, m=1, t=1, n_sink=0, dtype=torch.bfloat16)
+    m = torch.empty(b, cfg.h_q, n, device=dev)
+    l = torch.empty_like(m)
+    O = torch.empty(b, cfg.h_q, n, cfg.d, device=dev)
+    ws = torch.empty(max(kv.kvs_counter_causal_workspace_bytes(desc),
+                         kv.kvs_refresh_workspace_bytes(b, n)), dtype=torch.uint8, device=dev)
+    kept = torch.empty(b, cfg.J, dtype=torch.int32, device=dev)
+    Ko = torch.empty(b, cfg.h_kv, cfg.J, cfg.d, dtype=torch.bfloat16, device=dev)
+    Vo = torch.empty_like(Ko)
+    ido = torch.empty(b, cfg.J, dtype=torch.int32, device=dev)
+
+    def once():
+        kv.kvscore_counter_causal(desc, x["Q"], x["K"], x["V"], m, l, O, ws)
+        kv.kvscore_refresh(x["surprise"], x["K"], x["V"], kept, Ko, Vo, n_sys=cfg.n_sys, J=cfg.J,
+                           ids=x["ids"], ids_out=ido, ws=ws)
+
+    for _ in range(3):
+        once()
+    torch.cuda.synchronize()
+    kv.kvs_timing_reset()
+    kv.kvs_timing_enable(True)
+    for _ in range(reps):
+        once()
+    torch.cuda.synchronize()
+    per = {}
+    for nm, ms in kv.kvs_timing_records():
+        per.setdefault(nm, []).append(ms)
+    kv.kvs_timing_enable(False)
+    kv.kvs_timing_reset()
+    avg = {nm: sum(v) / len(v) for nm, v in per.items()}
+    total = sum(sum(v) for v in per.values()) / reps
+    flops = 2 * cfg.d * n * (n - 1) * cfg.h_q * b
+    tf = flops / (avg["attn_partial"] * 1e-3) / 1e12
+    return {"workload": cfg.name, "n": n, "J": cfg.J, "h": cfg.h, "n_sys": cfg.n_sys,
+            "kernels_ms": round(total, 4), "per_kernel_ms": {k: round(v, 4) for k, v in avg.items()},
+            "roofline": {"kernel": "attn_partial (counter-causal)", "bound": "mfma",
+                         "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -440,6 +489,8 @@ def main():
                      "unit": "TFLOP/s",
                      "frac": round(fflops / (aff * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "traffic": None}}
+    print("[bench] counter-causal refresh", file=sys.stderr, flush=True)
+    out["refresh"] = bench_refresh(kv, torch, dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, data[0])

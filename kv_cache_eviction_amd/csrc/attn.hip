@@ -410,14 +410,10 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
 // the four waves share the split weights: each takes every fourth split for
 // the row maximum and the weighted row sum, combined through LDS, so no
 // thread waits on a serial chain of loads.
-// With nblk > 0 (counter-causal rows) virtual head `head` is block
-// head % nblk of query head head / nblk, and its row q lands at position
-// (head % nblk) * 64 + q of that head's n_rows rows (positions >= n_rows are
-// padding).  A row that saw no key gets row_sum 0 and O = 0.
 template <int D>
 __global__ void __launch_bounds__(256)
 attn_combine_lore_kernel(const float *__restrict__ pm, const float *__restrict__ pl,
-                         const float *__restrict__ pO, int splits, int nq, int nblk, int n_rows,
+                         const float *__restrict__ pO, int splits, int nq,
                          float *__restrict__ row_max, float *__restrict__ row_sum,
                          float *__restrict__ O) {
   constexpr int CH = 32;           // partial-O values held in registers per pass
@@ -459,19 +455,9 @@ attn_combine_lore_kernel(const float *__restrict__ pm, const float *__restrict__
   psum[part * 64 + q] = lloc;
   __syncthreads();
   const float L = (psum[q] + psum[64 + q]) + (psum[128 + q] + psum[192 + q]);
-  long orow;
-  bool valid;
-  if (nblk > 0) {
-    const int pos = (int)(head % nblk) * 64 + q;
-    orow = (head / nblk) * n_rows + pos;
-    valid = pos < n_rows;
-  } else {
-    orow = head * nq + q;
-    valid = q < nq;
-  }
-  if (part == 0 && valid && blockIdx.y == 0) {
-    row_max[orow] = M * kLn2;
-    row_sum[orow] = L;
+  if (part == 0 && q < nq && blockIdx.y == 0) {
+    row_max[head * nq + q] = M * kLn2;
+    row_sum[head * nq + q] = L;
   }
   float o = 0.f;
   for (int s0 = 0; s0 < splits; s0 += CH) {
@@ -483,7 +469,70 @@ attn_combine_lore_kernel(const float *__restrict__ pm, const float *__restrict__
     for (int u = 0; u < CH; ++u)
       if (s0 + u < splits) o += ov[u] * wsh[(s0 + u) * 64 + q];
   }
-  if (valid) O[orow * D + d] = L > 0.f ? o * (1.f / L) : 0.f;
+  if (q < nq) O[(head * nq + q) * D + d] = o * (1.f / L);
+}
+
+// Counter-causal rows: merge the (few) splits of one virtual head, i.e. 64
+// consecutive positions of one query head, and write them as rows of O.
+// Thread (q = tid % 64, part = tid / 64) forms the split weights of row q and
+// the outputs of a quarter of d, reading partial O down the row axis
+// (coalesced); an LDS tile turns them into row-major stores.  A position that
+// saw no key gets row_max -inf, row_sum 0 and O = 0.
+template <int D>
+__global__ void __launch_bounds__(256)
+attn_combine_rev_kernel(const float *__restrict__ pm, const float *__restrict__ pl,
+                        const float *__restrict__ pO, int splits, int nblk, int n,
+                        float *__restrict__ row_max, float *__restrict__ row_sum,
+                        float *__restrict__ O) {
+  __shared__ float tile[64 * (D + 1)];
+  const long head = blockIdx.x;
+  const int q = threadIdx.x & 63, part = threadIdx.x >> 6;
+  const float *hm = pm + head * splits * 64;
+  const float *hl = pl + head * splits * 64;
+  float wgt[kMaxRevSplits];
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxRevSplits; ++s) M = fmaxf(M, s < splits ? hm[s * 64 + q] : -INFINITY);
+  const float muse = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxRevSplits; ++s) {
+    wgt[s] = s < splits ? exp2f(hm[s * 64 + q] - muse) : 0.f;
+    if (s < splits) L += hl[s * 64 + q] * wgt[s];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const float *ho = pO + head * splits * (long)D * 64 + q;
+#pragma unroll 8
+  for (int k = 0; k < D / 4; ++k) {
+    const int d = part * (D / 4) + k;
+    float o = 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxRevSplits; ++s)
+      if (s < splits) o += wgt[s] * ho[((long)s * D + d) * 64];
+    tile[q * (D + 1) + d] = o * inv;
+  }
+  const int pos0 = (int)(head % nblk) * 64;
+  const long obase = (head / nblk) * (long)n;
+  if (part == 0 && pos0 + q < n) {
+    row_max[obase + pos0 + q] = M * kLn2;
+    row_sum[obase + pos0 + q] = L;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * D; i += 256) {
+    const int r = i / D, c = i % D;
+    if (pos0 + r < n) O[(obase + pos0 + r) * D + c] = tile[r * (D + 1) + c];
+  }
+}
+
+SplitPlan rev_split_plan(int n) {
+  // cut the long early-position ranges so no workgroup walks more than about
+  // 2048 keys; the short late ones skip the splits before their first key
+  int splits = (n + 2047) / 2048;
+  if (splits > kMaxRevSplits) splits = kMaxRevSplits;
+  if (splits < 1) splits = 1;
+  int tps = (n + splits - 1) / splits;
+  tps = (tps + 63) / 64 * 64;
+  return SplitPlan{(n + tps - 1) / tps, tps};
 }
 
 // H2O prefill: merge the splits into per-row constants for the column-sum
@@ -598,10 +647,10 @@ hipError_t launch_attn_combine_lore(int d, const float *part_m, const float *par
     TimedLaunch tl_("attn_combine", st);
     if (d == 64)
       hipLaunchKernelGGL(attn_combine_lore_kernel<64>, dim3(heads, 64 / 4), dim3(256), shm, st,
-                         part_m, part_l, part_O, splits, nq, 0, 0, row_max, row_sum, O);
+                         part_m, part_l, part_O, splits, nq, row_max, row_sum, O);
     else
       hipLaunchKernelGGL(attn_combine_lore_kernel<128>, dim3(heads, 128 / 4), dim3(256), shm, st,
-                         part_m, part_l, part_O, splits, nq, 0, 0, row_max, row_sum, O);
+                         part_m, part_l, part_O, splits, nq, row_max, row_sum, O);
   }
   return hipGetLastError();
 }
@@ -610,15 +659,16 @@ hipError_t launch_attn_combine_rev(int d, const float *part_m, const float *part
                                    const float *part_O, int vheads, int splits, int nblk, int n,
                                    float *row_max, float *row_sum, float *O, hipStream_t st) {
   const size_t shm = sizeof(float) * 64 * ((size_t)splits + 8);
-  if (nblk < 1) return hipErrorInvalidValue;
+  (void)shm;
+  if (nblk < 1 || splits < 1 || splits > kMaxRevSplits) return hipErrorInvalidValue;
   {
     TimedLaunch tl_("attn_combine", st);
     if (d == 64)
-      hipLaunchKernelGGL(attn_combine_lore_kernel<64>, dim3(vheads, 64 / 4), dim3(256), shm, st,
-                         part_m, part_l, part_O, splits, 64, nblk, n, row_max, row_sum, O);
+      hipLaunchKernelGGL(attn_combine_rev_kernel<64>, dim3(vheads), dim3(256), 0, st, part_m,
+                         part_l, part_O, splits, nblk, n, row_max, row_sum, O);
     else
-      hipLaunchKernelGGL(attn_combine_lore_kernel<128>, dim3(vheads, 128 / 4), dim3(256), shm, st,
-                         part_m, part_l, part_O, splits, 64, nblk, n, row_max, row_sum, O);
+      hipLaunchKernelGGL(attn_combine_rev_kernel<128>, dim3(vheads), dim3(256), 0, st, part_m,
+                         part_l, part_O, splits, nblk, n, row_max, row_sum, O);
   }
   return hipGetLastError();
 }

@@ -396,8 +396,7 @@ CounterCausalPlan plan_counter_causal(const kvs_lore_desc *d) {
   p.nblk = (d->n + 63) / 64;
   p.geo = kvs::RowGeom{2, d->n, p.nblk, 0, G * p.nblk};
   p.vheads = d->batch * d->h_q * p.nblk;
-  p.split = kvs::attn_split_plan(
-      d->batch * d->h_kv * kvs::attn_head_split(p.geo.group, true).hsplit, d->n);
+  p.split = kvs::rev_split_plan(d->n);
   const size_t S = p.split.splits, V = (size_t)p.vheads;
   p.off_pm = 0;
   p.off_pl = align_up(p.off_pm + V * S * 64 * 4);

@@ -32,6 +32,9 @@ struct SplitPlan {
 constexpr int kMaxRangeTokens = 1 << 22;
 
 SplitPlan attn_split_plan(int units, int n);
+// Counter-causal rows: at most kMaxRevSplits token splits.
+constexpr int kMaxRevSplits = 8;
+SplitPlan rev_split_plan(int n);
 struct HeadSplit { int hsplit, hpw, maxw, qbw; };
 HeadSplit attn_head_split(int group, bool with_o);
 
