@@ -18,6 +18,7 @@ namespace kvs {
 typedef __bf16 bf16;
 typedef _Float16 f16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 struct f32x8 { f32x4 lo, hi; };
@@ -148,6 +149,24 @@ __device__ __forceinline__ void store_converted16(const U128 &v, Tout *dst) {
               (bits16(from_f32<Tout>(to_f32(ve[2 * e + 1]))) << 16);
     *reinterpret_cast<U128 *>(dst) = o;
   }
+}
+
+// Eight 16-bit values (bf16 or fp16) as eight fp8 e5m2 bytes, clamped to the
+// format's largest finite magnitude, 57344; round to nearest even.
+template <typename Tin>
+__device__ __forceinline__ void store_bf8x8(const U128 &v, uint8_t *dst) {
+  const Tin *ve = reinterpret_cast<const Tin *>(&v);
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float f[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __builtin_amdgcn_fmed3f(to_f32(ve[4 * h + e]), -57344.f, 57344.f);
+    int p = __builtin_amdgcn_cvt_pk_bf8_f32(f[0], f[1], 0, false);
+    p = __builtin_amdgcn_cvt_pk_bf8_f32(f[2], f[3], p, true);
+    w[h] = (uint32_t)p;
+  }
+  *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
 }
 
 // ---- raw buffer loads ----------------------------------------------------------

@@ -350,7 +350,7 @@ __global__ void __launch_bounds__(256)
 prep_mfma_kernel(const f16 *__restrict__ Gv, const float *__restrict__ O,
                  const float *__restrict__ row_max, const float *__restrict__ row_sum,
                  const float *__restrict__ omega, int h_q, int n, int nq, int w, int m, int t,
-                 float lambda_l, f16 *__restrict__ Yhi, f16 *__restrict__ Ylo,
+                 float lambda_l, f16 *__restrict__ Yhi, uint8_t *__restrict__ Ylo8,
                  float4 *__restrict__ consts) {
   constexpr int KS = D / 32, NB = D / 16;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -407,6 +407,7 @@ prep_mfma_kernel(const f16 *__restrict__ Gv, const float *__restrict__ O,
     }
   }
   float pij[4] = {0.f, 0.f, 0.f, 0.f};
+  float ylo[NB][4], lmax[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const f16x8 (&bf)[KS] = bfa[nb];
@@ -421,9 +422,28 @@ prep_mfma_kernel(const f16 *__restrict__ Gv, const float *__restrict__ O,
       const float y = r < nq ? acc[j] * unr[j] : 0.f;
       const f16 hi = (f16)y;
       Yhi[(hb * 64 + r) * D + c] = hi;
-      Ylo[(hb * 64 + r) * D + c] = (f16)(y - (float)hi);
+      ylo[nb][j] = y - (float)hi;
+      lmax[j] = fmaxf(lmax[j], fabsf(ylo[nb][j]));
       pij[j] = fmaf(oc[nb][j], y, pij[j]);
     }
+  }
+  // y_lo as fp8 e4m3 with a power-of-two row scale 2^k putting the row's
+  // largest |y_lo| in [128, 256); the score pass's block-scaled MFMA applies
+  // 2^-k through the row's E8M0 scale byte 127 - k.  Per head: 64 rows of D
+  // bytes, then 64 int32 scale bytes.
+  uint8_t *yb = Ylo8 + hb * (64 * D + 256);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float am = row16_max(lmax[j]);
+    const int e = am > 0.f ? ((__float_as_int(am) >> 23) & 0xFF) - 127 : 7;
+    const int k = min(max(7 - e, -120), 120);
+    const float sc = ldexpf(1.f, k);
+    const int r = wv * 16 + 4 * grp + j;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      yb[r * D + nb * 16 + col] =
+          (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(ylo[nb][j] * sc, 0.f, 0, false) & 0xFF);
+    if (col == 0) reinterpret_cast<int *>(yb + 64 * D)[r] = 127 - k;
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) pij[j] = row16_sum(pij[j]);
@@ -638,8 +658,11 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
   constexpr int ITEMS = TN * CPR;
   constexpr int PF = (ITEMS + NT - 1) / NT;
   constexpr float kTiny = 1.17549435e-38f;  // FLT_MIN
+  constexpr int V8ROW = 128 + 16;           // fp8 V row: 128 k-slots (zero past D), padded
   __shared__ __align__(16) Tin Ks[2][TN * KROW];
   __shared__ __align__(16) TV Vs[MODE == 0 ? 2 : 1][MODE == 0 ? TN * VROW : 8];
+  // V as fp8 e5m2 for the y_lo product (one block-scaled 16x16x128 MFMA)
+  __shared__ __align__(16) uint8_t V8s[SPLIT_Y ? 2 : 1][SPLIT_Y ? TN * V8ROW : 16];
   // per-lane partial sums: row (wave, row group) of TN tokens.  Rows are 82
   // floats apart: the reads of the per-tile sum (8 consecutive tokens x 8
   // waves, row stride 4*82 = 8 mod 32 banks) hit 32 distinct banks per half-wave.
@@ -665,7 +688,8 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
   // lane holds query rows 16*qb + 4*grp + j (j = 0..3) for token column col.
   FQ qf[QBW][KS];
   FV yhf[MODE == 0 ? QBW : 1][KS];
-  FV ylf[SPLIT_Y ? QBW : 1][KS];
+  i32x8 yl8[SPLIT_Y ? QBW : 1];  // y_lo row as fp8 e4m3 (k = 32 grp .. 32 grp + 31)
+  int ysc[SPLIT_Y ? QBW : 1];     // its E8M0 scale byte
   float beta[QBW][4], rwr[QBW][4];
   f32x4 xinit[QBW];
   int lim[QBW][4];
@@ -708,8 +732,13 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
       qf[qb][ks] = valid ? load8<Tin>(Q + qrow * D + ks * 32 + 8 * grp) : zero8<Tin>();
       if (MODE == 0)
         yhf[qb][ks] = spare ? zero8<TV>() : load8<TV>(Yhi + (head * 64 + r) * D + ks * 32 + 8 * grp);
-      if (SPLIT_Y)
-        ylf[qb][ks] = spare ? zero8<TV>() : load8<TV>(Ylo + (head * 64 + r) * D + ks * 32 + 8 * grp);
+    }
+    if (SPLIT_Y) {
+      const uint8_t *yb = reinterpret_cast<const uint8_t *>(Ylo) + head * (64 * D + 256);
+      const bool in_d = 32 * grp < D;  // D = 64: the upper k-slots are zero
+      yl8[qb] = (spare || !in_d) ? i32x8{0, 0, 0, 0, 0, 0, 0, 0}
+                                 : *reinterpret_cast<const i32x8 *>(yb + r * D + 32 * grp);
+      ysc[qb] = spare ? 127 : reinterpret_cast<const int *>(yb + 64 * D)[r];
     }
   }
 #pragma unroll
@@ -754,6 +783,7 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
         const int row = idx / CPR, ch = idx % CPR;
         *reinterpret_cast<U128 *>(&Ks[buf][row * KROW + ch * EPC]) = pk[u];
         if (MODE == 0) store_converted16<Tin, TV>(pv[u], &Vs[buf][row * VROW + ch * EPC]);
+        if constexpr (SPLIT_Y) store_bf8x8<Tin>(pv[u], &V8s[buf][row * V8ROW + ch * EPC]);
       }
     }
     if (MODE == 0) Ns[buf][wv][lane] = pn;
@@ -762,15 +792,27 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
   // One 16-token block: this lane's sum over its 4*QBW query rows for token
   // tok0 + col.  The K and V fragments of a block are read from LDS one block
   // ahead, so their latency hides behind the previous block's work.
-  auto load_frags = [&](int cur, int tb, FQ (&kf)[KS], FV (&vf)[MODE == 0 ? KS : 1]) {
+  auto load_frags = [&](int cur, int tb, FQ (&kf)[KS], FV (&vf)[MODE == 0 ? KS : 1],
+                        i32x8 &v8) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       kf[ks] = load8<Tin>(&Ks[cur][(tb * 16 + col) * KROW + ks * 32 + 8 * grp]);
       if (MODE == 0) vf[ks] = load8<TV>(&Vs[cur][(tb * 16 + col) * VROW + ks * 32 + 8 * grp]);
     }
+    if constexpr (SPLIT_Y) {
+      // B fragment of the 16x16x128 product: token tb*16 + col, k = 32 grp .. +31
+      // (with D = 64 the upper lanes hold zeros: their LDS slots are never written)
+      if (32 * grp < D) {
+        const U128 *p8 = reinterpret_cast<const U128 *>(&V8s[cur][(tb * 16 + col) * V8ROW + 32 * grp]);
+        const U128 a = p8[0], b2 = p8[1];
+        v8 = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b2.x, (int)b2.y, (int)b2.z, (int)b2.w};
+      } else {
+        v8 = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
   };
   auto block = [&](auto masked, int tok0, float nv, const FQ (&kf)[KS],
-                   const FV (&vf)[MODE == 0 ? KS : 1]) -> float {
+                   const FV (&vf)[MODE == 0 ? KS : 1], const i32x8 &v8) -> float {
     constexpr bool MASKED = decltype(masked)::value;
     f32x4 sa[QBW], xa[QBW];
 #pragma unroll
@@ -787,10 +829,9 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) x4 = mma(yhf[qb][ks], vf[ks], x4);
       }
-      if (SPLIT_Y) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) x4 = mma(ylf[qb][ks], vf[ks], x4);
-      }
+      if constexpr (SPLIT_Y)  // y_lo (e4m3, row scale 2^-k) times V (e5m2), K = 128
+        x4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(yl8[qb], v8, x4, 0, 1, 0, ysc[qb],
+                                                               0, 127);
       xa[qb] = x4;
     }
     const int tok = tok0 + col;
@@ -838,15 +879,17 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
   auto tile = [&](auto masked, int cur, int t0, bool pending, float part) {
     FQ kb[2][KS];
     FV vb[2][MODE == 0 ? KS : 1];
+    i32x8 v8b[2];
     float nv[TN / 16];
 #pragma unroll
     for (int tb = 0; tb < TN / 16; ++tb) nv[tb] = (MODE == 0) ? Ns[cur][wv][tb * 16 + col] : 0.f;
-    load_frags(cur, 0, kb[0], vb[0]);
+    load_frags(cur, 0, kb[0], vb[0], v8b[0]);
 #pragma unroll
     for (int tb = 0; tb < TN / 16; ++tb) {
-      if (tb + 1 < TN / 16) load_frags(cur, tb + 1, kb[(tb + 1) & 1], vb[(tb + 1) & 1]);
+      if (tb + 1 < TN / 16)
+        load_frags(cur, tb + 1, kb[(tb + 1) & 1], vb[(tb + 1) & 1], v8b[(tb + 1) & 1]);
       sched_fence();
-      const float tsum = block(masked, t0 + tb * 16, nv[tb], kb[tb & 1], vb[tb & 1]);
+      const float tsum = block(masked, t0 + tb * 16, nv[tb], kb[tb & 1], vb[tb & 1], v8b[tb & 1]);
       red[cur][(wv * 4 + grp) * RROW + tb * 16 + col] = tsum;
       if (tb == 0 && pending) reduce_store(part, t0 - TN);
       // a wave further ahead in the tile yields issue priority to the wave
@@ -961,7 +1004,7 @@ static hipError_t run_prep(const float *Gpart, int gsplits, const float *O, cons
     if constexpr (sizeof(TV) == 2)
       hipLaunchKernelGGL((prep_mfma_kernel<D>), dim3(h_q, batch), dim3(256), 0, st,
                          (const f16 *)Gv, O, row_max, row_sum, omega, h_q, n, nq, w, m, t,
-                         lambda_l, (f16 *)Yhi, (f16 *)Ylo, consts);
+                         lambda_l, (f16 *)Yhi, (uint8_t *)Ylo, consts);
     else
       hipLaunchKernelGGL((prep_kernel<D, TV>), dim3(h_q, batch, 4), dim3(256), 0, st, Gr, O,
                          row_max, row_sum, omega, h_q, n, nq, w, m, t, lambda_l, (TV *)Yhi,
