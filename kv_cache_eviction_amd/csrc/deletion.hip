@@ -16,7 +16,8 @@
 // Kernels, in call order:
 //   gram_kernel        G_h partial sums over d_model ranges, upper blocks (MFMA)
 //   gram_reduce_kernel G~_h = G_h rounded to the value type, mirrored (symmetric)
-//   prep_kernel        y_q = G~_h o_q (hi + lo), pi_q, per-row constants
+//   prep_kernel        y_q = G~_h o_q (fp16 hi + lo; lo as scaled fp8 for 16-bit
+//                      inputs), pi_q, per-row constants
 //   vnorm_kernel       N_i for every token and query head (MFMA)
 //   score_kernel<0>    recompute a, form e, aggregate rows and group heads -> S
 //   score_kernel<1>    H2O: column sums of the causal prompt probabilities
@@ -344,7 +345,8 @@ prep_kernel(const float *__restrict__ Gr, const float *__restrict__ O,
 // power of two (largest |o| in [2^14, 2^15)) and split into fp16 hi + lo
 // parts: the products are exact and the sum is an fp32 accumulation, as in
 // a plain fp32 dot product.  G~ is symmetric, so its rows serve as the
-// columns of the B operand.
+// columns of the B operand.  y is stored as fp16 y_hi plus y_lo = y - y_hi as
+// fp8 e4m3 scaled per row by a power of two (see the y_lo block below).
 template <int D>
 __global__ void __launch_bounds__(256)
 prep_mfma_kernel(const f16 *__restrict__ Gv, const float *__restrict__ O,
@@ -630,8 +632,12 @@ vnorm_kernel(const Tin *__restrict__ V, const typename ValueType<Tin>::type *__r
 // plus two cross-lane adds per 16 tokens; the per-wave partial sums are
 // combined across waves in a fixed order.
 //   MODE 0 (LORE): out = out_scale * sum_h sum_q wr_q * a/(1-a+eps) * sqrt(max(0, N - 2x + pi)),
-//                  x = v . (y_hi + y_lo) as two MFMA products whose accumulator
-//                  starts at -pi/2, so N - 2*acc = N - 2x + pi;
+//                  x = v . (y_hi + y_lo) as MFMA products whose accumulator
+//                  starts at -pi/2, so N - 2*acc = N - 2x + pi; for 16-bit
+//                  inputs y_hi . v runs on fp16 MFMA and y_lo . v as one
+//                  block-scaled fp8 MFMA (y_lo e4m3 with its row's power-of-
+//                  two scale, v e5m2): y_lo is about 2^-11 of y, so the fp8
+//                  roundings stay near 2^-15 of x;
 //                  sqrt(q2)/(1+eps-a) is formed as q2 * rsqrt(q2 (1+eps-a)^2)
 //                  with q2 clamped at 1e-30 instead of 0.
 //   MODE 1 (H2O):  out = sum over causal rows of a
