@@ -27,11 +27,12 @@ def dev():
     return torch.device("cuda")
 
 
-def run_attention(cfg, inp, dev):
-    desc = kv.lore_desc(batch=cfg.batch, n=cfg.n, h_q=cfg.h_q, h_kv=cfg.h_kv, d=cfg.d,
+def run_attention(cfg, inp, dev, n=None):
+    n = cfg.n if n is None else n
+    desc = kv.lore_desc(batch=cfg.batch, n=n, h_q=cfg.h_q, h_kv=cfg.h_kv, d=cfg.d,
                         d_model=cfg.h_q * cfg.d, w=0, m=1, t=1, n_sink=0,
                         dtype=TORCH_DTYPES[cfg.dtype])
-    b, hq, n, d = cfg.batch, cfg.h_q, cfg.n, cfg.d
+    b, hq, d = cfg.batch, cfg.h_q, cfg.d
     m = torch.empty(b, hq, n, device=dev)
     l = torch.empty(b, hq, n, device=dev)
     O = torch.full((b, hq, n, d), float("nan"), device=dev)
@@ -42,17 +43,18 @@ def run_attention(cfg, inp, dev):
     return m.cpu().numpy(), l.cpu().numpy(), O.cpu().numpy()
 
 
-def compare_attention(cfg, inp, got, heads, name):
+def compare_attention(cfg, inp, got, heads, name, n=None):
     m, l, O = got
     G = cfg.h_q // cfg.h_kv
     g = heads[0] // G
     mo, lo, Oo = oracle.counter_causal_attention(inp["Q"][:, heads].cpu(), inp["K"][:, g:g + 1].cpu(),
                                                  inp["V"][:, g:g + 1].cpu())
     m, l, O = m[:, heads], l[:, heads], O[:, heads]
-    n = cfg.n
+    n = cfg.n if n is None else n
     # every position but the last sees at least one key
-    check_stats(m[:, :, :n - 1], l[:, :, :n - 1], O[:, :, :n - 1], mo[:, :, :n - 1],
-                lo[:, :, :n - 1], Oo[:, :, :n - 1])
+    if n > 1:
+        check_stats(m[:, :, :n - 1], l[:, :, :n - 1], O[:, :, :n - 1], mo[:, :, :n - 1],
+                    lo[:, :, :n - 1], Oo[:, :, :n - 1])
     assert np.all(m[:, :, n - 1] == -np.inf) and np.all(l[:, :, n - 1] == 0)
     assert np.all(O[:, :, n - 1] == 0)
     print("%s heads %s: counter-causal attention within the bar" % (name, heads))
@@ -74,6 +76,28 @@ def test_attention_small(dev, cfg):
     G = cfg.h_q // cfg.h_kv
     for g in range(cfg.h_kv):
         compare_attention(cfg, inp, got, list(range(g * G, (g + 1) * G)), cfg.name)
+
+
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 129])
+def test_attention_tiny_and_block_edges(dev, n):
+    # one token (sees nothing), two, and caches ending just before, at and
+    # just after a 64-position block boundary
+    cfg = QWEN7B_REFRESH.with_(name="edge", h_q=6, h_kv=2, d=64, J=256, n_sys=0, dtype="f32",
+                               seed=66)
+    x = refresh_inputs(cfg, device="cpu")  # 320 positions, cut to the first n
+    inp = {k: x[k][:, :, :n].contiguous() for k in ("Q", "K", "V")}
+    got = run_attention(cfg, inp, dev, n=n)
+    for g in range(cfg.h_kv):
+        compare_attention(cfg, inp, got, [3 * g, 3 * g + 1, 3 * g + 2], "n=%d" % n, n=n)
+
+
+@pytest.mark.parametrize("n,J,n_sys", [(1, 1, 0), (1, 5, 3), (2, 1, 0), (65, 40, 8)])
+def test_refresh_tiny(dev, n, J, n_sys):
+    cfg = QWEN7B_REFRESH.with_(batch=2, h_kv=2, d=64, dtype="f16", seed=67)
+    x = refresh_inputs(cfg.with_(J=256), device="cpu")
+    inp = {"K": x["K"][:, :, :n].contiguous(), "V": x["V"][:, :, :n].contiguous(),
+           "surprise": x["surprise"][:, :n].contiguous(), "ids": x["ids"][:, :n].contiguous()}
+    check_refresh(inp, run_refresh(inp, 2, J, n_sys, dev), J, n_sys)
 
 
 def test_attention_full_size_sampled_kv_head(dev):
