@@ -280,6 +280,8 @@ def main():
     ap.add_argument("--config", default="llama3.1-8b-128k-32layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-h2o", action="store_true")
+    ap.add_argument("--streams", type=int, default=1,
+                    help="spread the layers of a plain timed step over this many streams")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph of one step instead of eager launches")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -330,9 +332,30 @@ def main():
             x = data[l]
             ev.run(x["Q"], x["K"], x["V"], x["W_O"], x["omega"], outs[l][0], outs[l][1])
 
+    # layers are independent once every layer's K/V is resident, so a plain
+    # step may run layer l on stream l % S, each stream with its own buffers
+    # and workspace (default priority); the main stream joins them at the end
+    n_str = max(1, args.streams)
+    evs = [ev] + [kv.LoreEviction(desc, dev) for _ in range(n_str - 1)]
+    side_streams = [torch.cuda.Stream() for _ in range(n_str - 1)]
+
+    def step_streams():
+        main = torch.cuda.current_stream()
+        for sst in side_streams:
+            sst.wait_stream(main)
+        for l in range(layers):
+            x = data[l]
+            i = l % n_str
+            with torch.cuda.stream(main if i == 0 else side_streams[i - 1]):
+                evs[i].run(x["Q"], x["K"], x["V"], x["W_O"], x["omega"], outs[l][0], outs[l][1])
+        for sst in side_streams:
+            main.wait_stream(sst)
+
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
+        if n_str > 1:
+            step_streams()
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
 
@@ -364,6 +387,8 @@ def main():
         for _ in range(args.steps):
             if graph is not None and not instrumented:
                 graph.replay()
+            elif n_str > 1 and not instrumented:
+                step_streams()
             else:
                 step()
         stop.record(st)
@@ -407,7 +432,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3),
         "ms_per_step_instrumented": round(total_ms_inst / args.steps, 3),
-        "launch": "eager" if graph is None else "hip-graph replay of one step",
+        "launch": ("hip-graph replay of one step" if graph is not None else
+                   "eager, layers over %d streams" % n_str if n_str > 1 else "eager"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
