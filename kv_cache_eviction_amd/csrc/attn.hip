@@ -578,7 +578,10 @@ HeadSplit attn_head_split(int group, bool with_o) {
   HeadSplit h;
   h.qbw = with_o ? 2 : 4;
   const int wph = 4 / h.qbw;
-  h.hsplit = (group * wph + 7) / 8;
+  // without O (H2O prefill rows, causal) groups of at most 4 virtual heads:
+  // the waves of a workgroup then differ less in how many tiles they need
+  // (measured 4% faster than 8 on the OPT-30B prompt, 2 was slower)
+  h.hsplit = with_o ? (group * wph + 7) / 8 : (group + 3) / 4;
   h.hpw = (group + h.hsplit - 1) / h.hsplit;
   h.maxw = 2;
   while (h.maxw < h.hpw * wph) h.maxw *= 2;
