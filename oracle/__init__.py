@@ -33,7 +33,14 @@ only) and take the GQA group mean; the trajectory disagreement D_m is the mean
 (1 - cosine) between its lookahead queries and every other trajectory's, per
 query head, standardized over the trajectories (zero below a spread of 1e-6); output
 fidelity is the mean cosine between per-head attention outputs over the full
-and the retained cache.
+and the retained cache; the memory refresh keeps its survivors in position
+order, protects the system prompt and the last token, and breaks ties toward
+the lower position.
+
+Every function here is pinned by tests to what the pages and the mathematics
+fix (worked examples, closed forms, invariants, brute force on tiny inputs).
+The readings above are conventions no page fixes: parity on those choices is
+unpinned, and they are listed with the design notes.
 """
 
 import ctypes
