@@ -235,15 +235,14 @@ def bench_refresh(kv, torch, dev, reps=10):
     m = torch.empty(b, cfg.h_q, n, device=dev)
     l = torch.empty_like(m)
     O = torch.empty(b, cfg.h_q, n, cfg.d, device=dev)
-    ws = torch.empty(max(kv.kvs_counter_causal_workspace_bytes(desc),
-                         kv.kvs_refresh_workspace_bytes(b, n)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kv.kvs_refresh_workspace_bytes(b, n), dtype=torch.uint8, device=dev)
     kept = torch.empty(b, cfg.J, dtype=torch.int32, device=dev)
     Ko = torch.empty(b, cfg.h_kv, cfg.J, cfg.d, dtype=torch.bfloat16, device=dev)
     Vo = torch.empty_like(Ko)
     ido = torch.empty(b, cfg.J, dtype=torch.int32, device=dev)
 
     def once():
-        kv.kvscore_counter_causal(desc, x["Q"], x["K"], x["V"], m, l, O, ws)
+        kv.kvscore_counter_causal(desc, x["Q"], x["K"], x["V"], m, l, O)
         kv.kvscore_refresh(x["surprise"], x["K"], x["V"], kept, Ko, Vo, n_sys=cfg.n_sys, J=cfg.J,
                            ids=x["ids"], ids_out=ido, ws=ws)
 

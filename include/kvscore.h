@@ -211,14 +211,13 @@ kvs_status kvscore_output_fidelity(const kvs_lore_desc *desc, int32_t n_f, int32
  *  row_max  [batch][h_q][n] fp32    out: max_{j>i} q_i.k_j / sqrt(d).
  *  row_sum  [batch][h_q][n] fp32    out: sum_{j>i} exp(q_i.k_j/sqrt(d) - row_max).
  *  O        [batch][h_q][n][d] fp32 out: the attention output of each position.
- *  ws, ws_bytes                     workspace (>= kvs_counter_causal_workspace_bytes).
- * Cost: about n^2/2 key visits per query head.  h_q * ceil(n/64) above about
- * 262000 (one launch's grid) is KVS_ERR_UNSUPPORTED.
+ * No workspace.  Cost: about n^2/2 key visits per query head.  n above 2^22,
+ * or h_q * ceil(n/64) above about 262000 (one launch's grid), is
+ * KVS_ERR_UNSUPPORTED.
  */
-size_t kvs_counter_causal_workspace_bytes(const kvs_lore_desc *desc);
 kvs_status kvscore_counter_causal(const kvs_lore_desc *desc, const void *Q, const void *K,
                                   const void *V, float *row_max, float *row_sum, float *O,
-                                  void *ws, size_t ws_bytes, void *stream);
+                                  void *stream);
 
 /*
  * Memory refresh (counter-causal review, Alg. 3 "Memory refresh step", design

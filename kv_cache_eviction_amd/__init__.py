@@ -10,7 +10,7 @@ from ._lib import (KvsError, LoreDesc, H2ODesc, load, last_error, lore_desc, h2o
                    kvs_lore_workspace_bytes, kvs_topb_workspace_bytes, kvscore_probs, kvscore_deletion,
                    kvscore_baseline_scores, kvscore_reliability_weights, RELIABILITY_E,
                    kvs_fidelity_workspace_bytes, kvscore_output_fidelity,
-                   kvs_counter_causal_workspace_bytes, kvscore_counter_causal,
+                   kvscore_counter_causal,
                    kvs_refresh_workspace_bytes, kvscore_refresh,
                    RELIABILITY_D, kvscore_topb_select, kv_compact, kvs_h2o_workspace_bytes,
                    kvscore_h2o_accumulate, KVS_F32, KVS_BF16, KVS_F16, KVS_H2O_PREFILL,
@@ -22,7 +22,7 @@ __all__ = ["KvsError", "LoreDesc", "H2ODesc", "load", "last_error", "lore_desc",
            "kvs_lore_workspace_bytes", "kvs_topb_workspace_bytes", "kvscore_probs", "kvscore_deletion",
            "kvscore_baseline_scores", "kvscore_reliability_weights", "RELIABILITY_E",
            "kvs_fidelity_workspace_bytes", "kvscore_output_fidelity",
-           "kvs_counter_causal_workspace_bytes", "kvscore_counter_causal",
+           "kvscore_counter_causal",
            "kvs_refresh_workspace_bytes", "kvscore_refresh",
            "RELIABILITY_D", "KVS_BASELINE_WINDOW", "KVS_BASELINE_TOVA", "kvscore_topb_select", "kv_compact", "kvs_h2o_workspace_bytes",
            "kvscore_h2o_accumulate", "KVS_F32", "KVS_BF16", "KVS_F16", "KVS_H2O_PREFILL",

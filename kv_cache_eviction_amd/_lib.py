@@ -23,7 +23,7 @@ CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
 
 EXPORTS = ("kvs_lore_workspace_bytes", "kvs_topb_workspace_bytes", "kvscore_probs", "kvscore_deletion",
            "kvscore_baseline_scores", "kvscore_reliability_weights", "kvs_fidelity_workspace_bytes",
-           "kvscore_output_fidelity", "kvs_counter_causal_workspace_bytes", "kvscore_counter_causal",
+           "kvscore_output_fidelity", "kvscore_counter_causal",
            "kvs_refresh_workspace_bytes", "kvscore_refresh", "kvscore_topb_select", "kv_compact", "kvs_h2o_workspace_bytes",
            "kvscore_h2o_accumulate", "kvs_timing_enable", "kvs_timing_count", "kvs_timing_read",
            "kvs_timing_reset", "kvs_last_error")
@@ -85,10 +85,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvs_fidelity_workspace_bytes.argtypes = [LP, i32, i32]
     lib.kvscore_output_fidelity.restype = i32
     lib.kvscore_output_fidelity.argtypes = [LP, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.kvs_counter_causal_workspace_bytes.restype = sz
-    lib.kvs_counter_causal_workspace_bytes.argtypes = [LP]
     lib.kvscore_counter_causal.restype = i32
-    lib.kvscore_counter_causal.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kvscore_counter_causal.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp]
     lib.kvs_refresh_workspace_bytes.restype = sz
     lib.kvs_refresh_workspace_bytes.argtypes = [i32, i32]
     lib.kvscore_refresh.restype = i32
@@ -283,14 +281,7 @@ def kvscore_output_fidelity(desc, Qf, K, V, K_keep, V_keep, cos_out, fidelity, w
            "kvscore_output_fidelity")
 
 
-def kvs_counter_causal_workspace_bytes(desc: LoreDesc) -> int:
-    nb = load().kvs_counter_causal_workspace_bytes(ctypes.byref(desc))
-    if nb == 0:
-        raise KvsError("invalid descriptor: " + last_error())
-    return nb
-
-
-def kvscore_counter_causal(desc, Q, K, V, row_max, row_sum, O, ws, stream=None):
+def kvscore_counter_causal(desc, Q, K, V, row_max, row_sum, O, stream=None):
     """Every cached position's fresh query attends to the keys after it."""
     dt = CODE_DTYPE[desc.dtype]
     b, hq, hk, n, d = desc.batch, desc.h_q, desc.h_kv, desc.n, desc.d
@@ -300,10 +291,8 @@ def kvscore_counter_causal(desc, Q, K, V, row_max, row_sum, O, ws, stream=None):
     _need(row_max, "row_max", (b, hq, n), torch.float32)
     _need(row_sum, "row_sum", (b, hq, n), torch.float32)
     _need(O, "O", (b, hq, n, d), torch.float32)
-    _ws_check(ws, kvs_counter_causal_workspace_bytes(desc))
     _check(load().kvscore_counter_causal(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V),
-                                         _ptr(row_max), _ptr(row_sum), _ptr(O), _ptr(ws),
-                                         ws.numel() * ws.element_size(), _stream(stream)),
+                                         _ptr(row_max), _ptr(row_sum), _ptr(O), _stream(stream)),
            "kvscore_counter_causal")
 
 

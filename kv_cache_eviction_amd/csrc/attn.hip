@@ -79,7 +79,8 @@ __device__ __forceinline__ long q_row(const RowGeom &g, int b, int h_kv, int kvh
 // visible key (or the end of the cache).  REV (counter-causal rows, mode 2)
 // adds a first visible key per row: tiles wholly before a wave's rows are
 // skipped, a workgroup starts at the tile of its rows' earliest key, and the
-// tiles that cross a row's first key are masked too.
+// tiles that cross a row's first key are masked too.  Counter-causal rows are
+// launched unsplit and write their final rows from the epilogue.
 template <typename Tin, int D, bool WITH_O, int MAXW, int QBW, bool REV = false>
 __global__ void __launch_bounds__(64 * MAXW)
 attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__restrict__ V,
@@ -380,6 +381,35 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
 
   if (spare) return;
   const long head = ((long)b * h_kv + kvh) * geo.group + hv;
+  if constexpr (REV && WITH_O) {
+    if (splits == 1) {
+      // counter-causal rows run unsplit: this workgroup saw every key of its
+      // rows, so it writes the final row_max (natural units), row_sum and
+      // normalised O rows itself (pm, pl, pO are then row_max [.][n],
+      // row_sum [.][n] and O [.][n][D])
+      const long ohead = (((long)b * h_kv + kvh) * (geo.group / geo.nq) + hv / geo.nq);
+#pragma unroll
+      for (int qb = 0; qb < QBW; ++qb) {
+        const float fix = (mtop[qb] == -INFINITY) ? 1.f : hw_exp2(mref[qb] - mtop[qb]);
+        const float l = group4_sum(lsum[qb] * fix);
+        const int pos = (hv % geo.nq) * 64 + (qb0 + qb) * 16 + col;
+        if (pos < n) {
+          const long orow = ohead * n + pos;
+          if (grp == 0) {
+            pm[orow] = mtop[qb] * kLn2;
+            pl[orow] = l;
+          }
+          const float sc = l > 0.f ? fix / l : 0.f;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            *reinterpret_cast<float4 *>(pO + orow * D + db * 16 + 4 * grp) =
+                make_float4(oacc[db][qb][0] * sc, oacc[db][qb][1] * sc, oacc[db][qb][2] * sc,
+                            oacc[db][qb][3] * sc);
+        }
+      }
+      return;
+    }
+  }
   const long pbase = (head * splits + s) * 64;
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
@@ -470,69 +500,6 @@ attn_combine_lore_kernel(const float *__restrict__ pm, const float *__restrict__
       if (s0 + u < splits) o += ov[u] * wsh[(s0 + u) * 64 + q];
   }
   if (q < nq) O[(head * nq + q) * D + d] = o * (1.f / L);
-}
-
-// Counter-causal rows: merge the (few) splits of one virtual head, i.e. 64
-// consecutive positions of one query head, and write them as rows of O.
-// Thread (q = tid % 64, part = tid / 64) forms the split weights of row q and
-// the outputs of a quarter of d, reading partial O down the row axis
-// (coalesced); an LDS tile turns them into row-major stores.  A position that
-// saw no key gets row_max -inf, row_sum 0 and O = 0.
-template <int D>
-__global__ void __launch_bounds__(256)
-attn_combine_rev_kernel(const float *__restrict__ pm, const float *__restrict__ pl,
-                        const float *__restrict__ pO, int splits, int nblk, int n,
-                        float *__restrict__ row_max, float *__restrict__ row_sum,
-                        float *__restrict__ O) {
-  __shared__ float tile[64 * (D + 1)];
-  const long head = blockIdx.x;
-  const int q = threadIdx.x & 63, part = threadIdx.x >> 6;
-  const float *hm = pm + head * splits * 64;
-  const float *hl = pl + head * splits * 64;
-  float wgt[kMaxRevSplits];
-  float M = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < kMaxRevSplits; ++s) M = fmaxf(M, s < splits ? hm[s * 64 + q] : -INFINITY);
-  const float muse = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f;
-#pragma unroll
-  for (int s = 0; s < kMaxRevSplits; ++s) {
-    wgt[s] = s < splits ? exp2f(hm[s * 64 + q] - muse) : 0.f;
-    if (s < splits) L += hl[s * 64 + q] * wgt[s];
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  const float *ho = pO + head * splits * (long)D * 64 + q;
-#pragma unroll 8
-  for (int k = 0; k < D / 4; ++k) {
-    const int d = part * (D / 4) + k;
-    float o = 0.f;
-#pragma unroll
-    for (int s = 0; s < kMaxRevSplits; ++s)
-      if (s < splits) o += wgt[s] * ho[((long)s * D + d) * 64];
-    tile[q * (D + 1) + d] = o * inv;
-  }
-  const int pos0 = (int)(head % nblk) * 64;
-  const long obase = (head / nblk) * (long)n;
-  if (part == 0 && pos0 + q < n) {
-    row_max[obase + pos0 + q] = M * kLn2;
-    row_sum[obase + pos0 + q] = L;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 64 * D; i += 256) {
-    const int r = i / D, c = i % D;
-    if (pos0 + r < n) O[(obase + pos0 + r) * D + c] = tile[r * (D + 1) + c];
-  }
-}
-
-SplitPlan rev_split_plan(int n) {
-  // cut the long early-position ranges so no workgroup walks more than about
-  // 2048 keys; the short late ones skip the splits before their first key
-  int splits = (n + 2047) / 2048;
-  if (splits > kMaxRevSplits) splits = kMaxRevSplits;
-  if (splits < 1) splits = 1;
-  int tps = (n + splits - 1) / splits;
-  tps = (tps + 63) / 64 * 64;
-  return SplitPlan{(n + tps - 1) / tps, tps};
 }
 
 // H2O prefill: merge the splits into per-row constants for the column-sum
@@ -654,24 +621,6 @@ hipError_t launch_attn_combine_lore(int d, const float *part_m, const float *par
     else
       hipLaunchKernelGGL(attn_combine_lore_kernel<128>, dim3(heads, 128 / 4), dim3(256), shm, st,
                          part_m, part_l, part_O, splits, nq, row_max, row_sum, O);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_combine_rev(int d, const float *part_m, const float *part_l,
-                                   const float *part_O, int vheads, int splits, int nblk, int n,
-                                   float *row_max, float *row_sum, float *O, hipStream_t st) {
-  const size_t shm = sizeof(float) * 64 * ((size_t)splits + 8);
-  (void)shm;
-  if (nblk < 1 || splits < 1 || splits > kMaxRevSplits) return hipErrorInvalidValue;
-  {
-    TimedLaunch tl_("attn_combine", st);
-    if (d == 64)
-      hipLaunchKernelGGL(attn_combine_rev_kernel<64>, dim3(vheads), dim3(256), 0, st, part_m,
-                         part_l, part_O, splits, nblk, n, row_max, row_sum, O);
-    else
-      hipLaunchKernelGGL(attn_combine_rev_kernel<128>, dim3(vheads), dim3(256), 0, st, part_m,
-                         part_l, part_O, splits, nblk, n, row_max, row_sum, O);
   }
   return hipGetLastError();
 }

@@ -383,53 +383,24 @@ kvs_status check_counter_causal(const kvs_lore_desc *d) {
   return ok();
 }
 
-struct CounterCausalPlan {
-  kvs::RowGeom geo;
-  kvs::SplitPlan split;
-  int nblk, vheads;
-  size_t off_pm, off_pl, off_po, bytes;
-};
-
-CounterCausalPlan plan_counter_causal(const kvs_lore_desc *d) {
-  CounterCausalPlan p{};
-  const int G = d->h_q / d->h_kv;
-  p.nblk = (d->n + 63) / 64;
-  p.geo = kvs::RowGeom{2, d->n, p.nblk, 0, G * p.nblk};
-  p.vheads = d->batch * d->h_q * p.nblk;
-  p.split = kvs::rev_split_plan(d->n);
-  const size_t S = p.split.splits, V = (size_t)p.vheads;
-  p.off_pm = 0;
-  p.off_pl = align_up(p.off_pm + V * S * 64 * 4);
-  p.off_po = align_up(p.off_pl + V * S * 64 * 4);
-  p.bytes = align_up(p.off_po + V * S * (size_t)d->d * 64 * 4);
-  return p;
-}
-
-KVS_API size_t kvs_counter_causal_workspace_bytes(const kvs_lore_desc *desc) {
-  if (check_counter_causal(desc) != KVS_OK) return 0;
-  return plan_counter_causal(desc).bytes;
-}
-
 KVS_API kvs_status kvscore_counter_causal(const kvs_lore_desc *desc, const void *Q, const void *K,
                                           const void *V, float *row_max, float *row_sum,
-                                          float *O, void *ws, size_t ws_bytes, void *stream) {
+                                          float *O, void *stream) {
   kvs_status st = check_counter_causal(desc);
   if (st != KVS_OK) return st;
   if (!Q || !K || !V || !row_max || !row_sum || !O)
     return fail(KVS_ERR_INVALID, "kvscore_counter_causal: a required pointer is NULL");
   st = check_aligned("kvscore_counter_causal", {Q, K, V, O});
   if (st != KVS_OK) return st;
-  const CounterCausalPlan p = plan_counter_causal(desc);
-  st = check_ws(ws, ws_bytes, p.bytes);
-  if (st != KVS_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  float *pm = at<float>(ws, p.off_pm), *pl = at<float>(ws, p.off_pl), *po = at<float>(ws, p.off_po);
-  hipError_t e = kvs::launch_attn_partial(desc->dtype, desc->d, true, Q, K, V, p.geo, desc->batch,
-                                          desc->h_kv, p.split, pm, pl, po, s);
-  if (e != hipSuccess) return hip_status(e, "counter-causal attention");
-  e = kvs::launch_attn_combine_rev(desc->d, pm, pl, po, p.vheads, p.split.splits, p.nblk, desc->n,
-                                   row_max, row_sum, O, s);
-  return hip_status(e, "counter-causal combine");
+  // one split over all n keys (a workgroup starts at its rows' earliest key),
+  // so the attention pass writes the final rows and no workspace is needed
+  const int G = desc->h_q / desc->h_kv, nblk = (desc->n + 63) / 64;
+  const kvs::RowGeom geo{2, desc->n, nblk, 0, G * nblk};
+  const int tps = (desc->n + 63) / 64 * 64;
+  hipError_t e = kvs::launch_attn_partial(desc->dtype, desc->d, true, Q, K, V, geo, desc->batch,
+                                          desc->h_kv, kvs::SplitPlan{1, tps}, row_max, row_sum,
+                                          O, static_cast<hipStream_t>(stream));
+  return hip_status(e, "counter-causal attention");
 }
 
 // ---------------------------------------------------------------------------

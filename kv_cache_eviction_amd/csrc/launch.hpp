@@ -32,13 +32,12 @@ struct SplitPlan {
 constexpr int kMaxRangeTokens = 1 << 22;
 
 SplitPlan attn_split_plan(int units, int n);
-// Counter-causal rows: at most kMaxRevSplits token splits.
-constexpr int kMaxRevSplits = 8;
-SplitPlan rev_split_plan(int n);
 struct HeadSplit { int hsplit, hpw, maxw, qbw; };
 HeadSplit attn_head_split(int group, bool with_o);
 
-// Pass 1 partials -> combined statistics.
+// Pass 1 partials -> combined statistics.  Counter-causal rows (RowGeom mode
+// 2, one split covering all n keys) take part_m, part_l, part_O as the final
+// row_max [batch*h_q][n], row_sum and O [batch*h_q][n][d] instead.
 // part_m/part_l: [heads][splits][64]; part_O: [heads][splits][d][64].
 hipError_t launch_attn_partial(int etype, int d, bool with_o, const void *Q, const void *K,
                                const void *V, RowGeom geo, int batch, int h_kv, SplitPlan plan,
@@ -47,11 +46,6 @@ hipError_t launch_attn_partial(int etype, int d, bool with_o, const void *Q, con
 hipError_t launch_attn_combine_lore(int d, const float *part_m, const float *part_l,
                                     const float *part_O, int heads, int splits, int nq,
                                     float *row_max, float *row_sum, float *O, hipStream_t st);
-// Counter-causal rows (RowGeom mode 2): vheads = batch * h_q * nblk virtual
-// heads of 64 rows; writes row_max, row_sum [batch*h_q][n] and O [batch*h_q][n][d].
-hipError_t launch_attn_combine_rev(int d, const float *part_m, const float *part_l,
-                                   const float *part_O, int vheads, int splits, int nblk, int n,
-                                   float *row_max, float *row_sum, float *O, hipStream_t st);
 // H2O: writes per-row constants {beta2, 0, 1, last-visible bits} [heads][64].
 hipError_t launch_attn_combine_rows(const float *part_m, const float *part_l, int heads,
                                     int splits, int group, int P, float4 *consts, hipStream_t st);

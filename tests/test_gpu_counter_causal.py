@@ -36,9 +36,8 @@ def run_attention(cfg, inp, dev, n=None):
     m = torch.empty(b, hq, n, device=dev)
     l = torch.empty(b, hq, n, device=dev)
     O = torch.full((b, hq, n, d), float("nan"), device=dev)
-    ws = torch.empty(kv.kvs_counter_causal_workspace_bytes(desc), dtype=torch.uint8, device=dev)
     Q, K, V = (inp[k].to(dev).contiguous() for k in ("Q", "K", "V"))
-    kv.kvscore_counter_causal(desc, Q, K, V, m, l, O, ws)
+    kv.kvscore_counter_causal(desc, Q, K, V, m, l, O)
     torch.cuda.synchronize()
     return m.cpu().numpy(), l.cpu().numpy(), O.cpu().numpy()
 
