@@ -574,6 +574,33 @@ def main():
                      "traffic": None}}
     print("[bench] counter-causal refresh", file=sys.stderr, flush=True)
     out["refresh"] = bench_refresh(kv, torch, dev)
+    # diagnostic, not timed: recall of layer 0's planted facts in the kept
+    # sets of LORE-KV, of its window-only form (lambda_L = 0) and of the two
+    # prompt-side baselines (the synthetic lookahead queries target the
+    # facts, the window queries do not)
+    print("[bench] planted-fact recall", file=sys.stderr, flush=True)
+    facts = x["marks"].long()  # [b][n_facts] positions, shared by the KV heads
+
+    def recall(kept):
+        hit = (kept.long()[:, :, :, None] == facts[:, None, None, :]).any(dim=2)
+        return round(float(hit.float().mean()), 4)
+
+    Kd = torch.empty_like(outs[0][0])
+    Vd = torch.empty_like(outs[0][1])
+    ev.run(x["Q"], x["K"], x["V"], x["W_O"], x["omega"], Kd, Vd)
+    rec = {"lore_kv": recall(ev.kept)}
+    desc0 = kv.lore_desc(batch=cfg.batch, n=cfg.n, h_q=cfg.h_q, h_kv=cfg.h_kv, d=cfg.d,
+                         d_model=cfg.d_model, w=cfg.w, m=cfg.m, t=cfg.t, n_sink=cfg.n_sink,
+                         chunk=cfg.chunk, budget=cfg.budget, eps=cfg.eps, lambda_l=0.0, dtype=dt)
+    ev0 = kv.LoreEviction(desc0, dev)
+    ev0.run(x["Q"], x["K"], x["V"], x["W_O"], x["omega"], Kd, Vd)
+    rec["lore_kv_window_only"] = recall(ev0.kept)
+    for name, kind in (("window_baseline", kv.KVS_BASELINE_WINDOW), ("tova", kv.KVS_BASELINE_TOVA)):
+        ev0.baseline(kind, x["Q"], x["K"], x["V"])
+        ev0.select()
+        rec[name] = recall(ev0.kept)
+    del ev0
+    out["planted_fact_recall"] = rec
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, data)
