@@ -228,23 +228,23 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
         if (VITEMS % NT != 0 && idx >= VITEMS) continue;
         if constexpr (V16) {
           const int kp = idx % (TN / 2), ch = idx / (TN / 2);
-          const Tin *ae = reinterpret_cast<const Tin *>(&pv[u][0]);
-          const Tin *be = reinterpret_cast<const Tin *>(&pv[u][V16 ? 1 : 0]);
+          const Elems16<Tin> ae = elems16<Tin>(pv[u][0]);
+          const Elems16<Tin> be = elems16<Tin>(pv[u][V16 ? 1 : 0]);
 #pragma unroll
           for (int e = 0; e < EPC; ++e) {
             uint32_t packed;
             if constexpr (__is_same(Tin, bf16) && __is_same(TV, f16))
               // exact in the fp16 normal range: round-toward-zero changes nothing there
-              packed = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(to_f32(ae[e]), to_f32(be[e])));
+              packed = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(to_f32(ae.e[e]), to_f32(be.e[e])));
             else
-              packed = bits16(from_f32<TV>(to_f32(ae[e]))) | (bits16(from_f32<TV>(to_f32(be[e]))) << 16);
+              packed = bits16(from_f32<TV>(to_f32(ae.e[e]))) | (bits16(from_f32<TV>(to_f32(be.e[e]))) << 16);
             *reinterpret_cast<uint32_t *>(&Vt[buf][(ch * EPC + e) * VROW + 2 * kp]) = packed;
           }
         } else {
           const int r = idx % TN, ch = idx / TN;
-          const Tin *ae = reinterpret_cast<const Tin *>(&pv[u][0]);
+          const Elems16<Tin> ae = elems16<Tin>(pv[u][0]);
 #pragma unroll
-          for (int e = 0; e < EPC; ++e) Vt[buf][(ch * EPC + e) * VROW + r] = from_f32<TV>(to_f32(ae[e]));
+          for (int e = 0; e < EPC; ++e) Vt[buf][(ch * EPC + e) * VROW + r] = from_f32<TV>(to_f32(ae.e[e]));
         }
       }
     }

@@ -117,6 +117,17 @@ __device__ __forceinline__ typename FragOf<To>::type convert8(const typename Fra
 // ---- 16-byte vector copies ---------------------------------------------------
 struct alignas(16) U128 { uint32_t x, y, z, w; };
 
+// A 16-byte chunk viewed as its elements.  A bit copy, not a pointer cast:
+// type-based alias analysis may otherwise drop the write of the chunk that a
+// read of its elements through another type depends on.
+template <typename T> struct Elems16 { T e[16 / sizeof(T)]; };
+template <typename T> __device__ __forceinline__ Elems16<T> elems16(const U128 &v) {
+  return __builtin_bit_cast(Elems16<T>, v);
+}
+template <typename T> __device__ __forceinline__ U128 pack16(const Elems16<T> &v) {
+  return __builtin_bit_cast(U128, v);
+}
+
 template <typename T> __device__ __forceinline__ uint32_t bits16(T x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x);
 }
@@ -140,13 +151,13 @@ __device__ __forceinline__ void store_converted16(const U128 &v, Tout *dst) {
                                                                       __uint_as_float(w[e] & 0xFFFF0000u)));
     *reinterpret_cast<U128 *>(dst) = o;
   } else {
-    const Tin *ve = reinterpret_cast<const Tin *>(&v);
+    const Elems16<Tin> ve = elems16<Tin>(v);
     U128 o;
     uint32_t *ow = reinterpret_cast<uint32_t *>(&o);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      ow[e] = bits16(from_f32<Tout>(to_f32(ve[2 * e]))) |
-              (bits16(from_f32<Tout>(to_f32(ve[2 * e + 1]))) << 16);
+      ow[e] = bits16(from_f32<Tout>(to_f32(ve.e[2 * e]))) |
+              (bits16(from_f32<Tout>(to_f32(ve.e[2 * e + 1]))) << 16);
     *reinterpret_cast<U128 *>(dst) = o;
   }
 }
@@ -155,13 +166,13 @@ __device__ __forceinline__ void store_converted16(const U128 &v, Tout *dst) {
 // format's largest finite magnitude, 57344; round to nearest even.
 template <typename Tin>
 __device__ __forceinline__ void store_bf8x8(const U128 &v, uint8_t *dst) {
-  const Tin *ve = reinterpret_cast<const Tin *>(&v);
+  const Elems16<Tin> ve = elems16<Tin>(v);
   uint32_t w[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     float f[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) f[e] = __builtin_amdgcn_fmed3f(to_f32(ve[4 * h + e]), -57344.f, 57344.f);
+    for (int e = 0; e < 4; ++e) f[e] = __builtin_amdgcn_fmed3f(to_f32(ve.e[4 * h + e]), -57344.f, 57344.f);
     int p = __builtin_amdgcn_cvt_pk_bf8_f32(f[0], f[1], 0, false);
     p = __builtin_amdgcn_cvt_pk_bf8_f32(f[2], f[3], p, true);
     w[h] = (uint32_t)p;

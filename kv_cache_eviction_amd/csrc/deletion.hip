@@ -96,19 +96,19 @@ gram_kernel(const Tin *__restrict__ W, int dm, int h_q, int rows_per_split,
       if (ITEMS % 256 != 0 && idx >= ITEMS) continue;
       const int kr = P16 ? idx / CPR : idx % RI, ch = P16 ? idx % CPR : idx / RI;
       if constexpr (P16) {
-        const Tin *ae = reinterpret_cast<const Tin *>(&pw[u][0]);
-        const Tin *be = reinterpret_cast<const Tin *>(&pw[u][P16 ? 1 : 0]);
+        const Elems16<Tin> ae = elems16<Tin>(pw[u][0]);
+        const Elems16<Tin> be = elems16<Tin>(pw[u][P16 ? 1 : 0]);
         // row pair kr lands at dword kr ^ 4*((row >> 3) & 7) of LDS row
         // ch*8 + e: the 16 lanes of a row pair then hit distinct banks
         const int kd = kr ^ (4 * (ch & 7));
 #pragma unroll
         for (int e = 0; e < EPC; ++e)
           *reinterpret_cast<uint32_t *>(&Wt[buf][(ch * EPC + e) * WROW + 2 * kd]) =
-              bits16(ae[e]) | (bits16(be[e]) << 16);
+              bits16(ae.e[e]) | (bits16(be.e[e]) << 16);
       } else {
-        const Tin *ae = reinterpret_cast<const Tin *>(&pw[u][0]);
+        const Elems16<Tin> ae = elems16<Tin>(pw[u][0]);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) Wt[buf][(ch * EPC + e) * WROW + kr] = ae[e];
+        for (int e = 0; e < EPC; ++e) Wt[buf][(ch * EPC + e) * WROW + kr] = ae.e[e];
       }
     }
   };

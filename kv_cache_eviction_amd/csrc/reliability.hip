@@ -60,10 +60,10 @@ traj_cosine_kernel(const T *__restrict__ Q, int h_q, int nq, int d, int w, int m
   for (int u = 0; u < kPerThread; ++u) {
     const int i = threadIdx.x + u * kRelThreads;
     if (i < nchunks) {
-      const T *e = reinterpret_cast<const T *>(&v[u]);
+      const Elems16<T> e = elems16<T>(v[u]);
       float *dst = &rows[(i / cpr) * kStride + (i % cpr) * kEpc];
 #pragma unroll
-      for (int k = 0; k < kEpc; ++k) dst[k] = to_f32(e[k]);
+      for (int k = 0; k < kEpc; ++k) dst[k] = to_f32(e.e[k]);
     }
   }
   __syncthreads();
