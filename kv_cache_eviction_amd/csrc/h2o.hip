@@ -11,12 +11,13 @@
 // (Def. 2.1).  Rows (sequence, head) are independent, one wavefront each.
 //
 // A row's slots are read as 16-byte lane chunks, D/EPC lanes per slot, so one
-// wave instruction covers 64*16 contiguous-per-slot bytes, and eight such
-// instructions are in flight before any is used; invalid slots (and slots
-// whose probability is 0 in the P.V pass) are never read: their loads take an
-// offset past the buffer resource's range, which returns zeros without a
-// memory access.  The slot map and the logits sit in LDS for the softmax; the
-// updated accumulators are read back (same lane) for the arg-min.
+// wave instruction covers 64*16 contiguous-per-slot bytes.  Loads go in
+// batches of eight such instructions, all in flight before the first is used
+// (the first value batch is in flight while the softmax runs); free
+// slots are never read: their loads take an offset past the buffer
+// resource's range, which returns zeros without a memory access.  The slot
+// map and accumulators are loaded once into LDS beside the logits, so the
+// softmax, the accumulation and the arg-min touch global memory only to write.
 #include "common.hpp"
 #include "launch.hpp"
 #include "timing.hpp"
@@ -48,6 +49,46 @@ template <int LPR> __device__ __forceinline__ float across_groups_sum(float v) {
   return v;
 }
 
+// c + a * b for one 16-byte chunk of fp16 in each of a and b (the new query
+// and a key row), elementwise in order, or c + a * b[e] for a scalar a and
+// each element of b (a probability and a value row).  fp16 chunks feed the
+// mixed-precision FMA straight from their packed registers: the product and
+// sum are those of fp32, and no unpacked copies are held.
+template <typename T>
+__device__ __forceinline__ float dot16(const U128 &a, const float (&af)[16 / sizeof(T)],
+                                       const U128 &b, float c) {
+  if constexpr (__is_same(T, f16)) {
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel_hi:[1,1,0]" : "+v"(c) : "v"(aw[p]), "v"(bw[p]));
+      asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "+v"(c)
+          : "v"(aw[p]), "v"(bw[p]));
+    }
+  } else {
+    const Elems16<T> be = elems16<T>(b);
+#pragma unroll
+    for (int e = 0; e < 16 / (int)sizeof(T); ++e) c += af[e] * to_f32(be.e[e]);
+  }
+  return c;
+}
+template <typename T>
+__device__ __forceinline__ void axpy16(float a, const U128 &b, float (&o)[16 / sizeof(T)]) {
+  if constexpr (__is_same(T, f16)) {
+    const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel_hi:[0,1,0]" : "+v"(o[2 * p]) : "v"(a), "v"(bw[p]));
+      asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(o[2 * p + 1])
+          : "v"(a), "v"(bw[p]));
+    }
+  } else {
+    const Elems16<T> be = elems16<T>(b);
+#pragma unroll
+    for (int e = 0; e < 16 / (int)sizeof(T); ++e) o[e] += a * to_f32(be.e[e]);
+  }
+}
+
 __device__ __forceinline__ uint32_t order_key_pos(float x) {
   const uint32_t u = __float_as_uint(x + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -63,13 +104,16 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
   constexpr int EPC = 16 / (int)sizeof(T);
   constexpr int LPR = D / EPC;  // lanes per slot row
   constexpr int RPI = 64 / LPR; // slot rows per wave step
-  constexpr int U = 8;          // wave steps whose loads are in flight together
+  constexpr int U = 8;          // wave steps per batch of loads
+  constexpr int STEP = RPI * U; // slots per batch
   extern __shared__ float dsh[];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const long row = (long)blockIdx.x * 4 + wv;
+  const int wpb = blockDim.x >> 6;
+  const long row = (long)blockIdx.x * wpb + wv;
   if (row >= rows) return;
-  float *prob = dsh + (long)wv * 2 * cap;
-  int32_t *pos_s = reinterpret_cast<int32_t *>(prob + cap);
+  float *prob = dsh + (long)wv * 3 * cap;
+  float *acc_s = prob + cap;
+  int32_t *pos_s = reinterpret_cast<int32_t *>(prob + 2 * cap);
   int32_t *pos = slot_pos + row * cap;
   float *ac = acc + row * cap;
   T *Kr = K + row * cap * D;
@@ -77,70 +121,84 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
   const uint32_t row_bytes = (uint32_t)cap * (uint32_t)(D * sizeof(T));
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kr, row_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vr, row_bytes);
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(pos, (uint32_t)cap * 4u);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(ac, (uint32_t)cap * 4u);
+  const int newpos = cur_len - 1;
+  const int sub = lane % LPR, rr = lane / LPR;
 
-  // slot map into LDS; lowest free slot, and how many slots hold a token
+  // the new token's query, key and value, loaded before the slot map
+  const U128 qq = *reinterpret_cast<const U128 *>(q + row * D + sub * EPC);
+  const U128 kq = *reinterpret_cast<const U128 *>(k_new + row * D + sub * EPC);
+  const U128 vq = *reinterpret_cast<const U128 *>(v_new + row * D + sub * EPC);
+
+  // slot map and accumulators into LDS, eight 64-slot blocks per lane loaded
+  // together; lowest free slot, and how many slots hold a token
   int ws = -1, nvalid = 0;
-  for (int base = 0; base < cap; base += 64) {
-    const int s = base + lane;
-    const int p = s < cap ? pos[s] : 0;
-    if (s < cap) pos_s[s] = p;
-    const unsigned long long fb = __ballot(s < cap && p < 0);
-    const unsigned long long vb = __ballot(s < cap && p >= 0);
-    nvalid += __popcll(vb);
-    if (ws < 0 && fb) ws = base + __ffsll((long long)fb) - 1;
+  for (int base = 0; base < cap; base += 64 * 8) {
+    int pv[8];
+    float av[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = base + 64 * u + lane;
+      const uint32_t off = s < cap ? (uint32_t)s * 4u : kNoLoad;
+      pv[u] = __float_as_int(buf_load_f32(rp, off));
+      av[u] = buf_load_f32(ra, off);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = base + 64 * u + lane;
+      if (s < cap) {
+        pos_s[s] = pv[u];
+        acc_s[s] = av[u];
+      }
+      const unsigned long long fb = __ballot(s < cap && pv[u] < 0);
+      const unsigned long long vb = __ballot(s < cap && pv[u] >= 0);
+      nvalid += __popcll(vb);
+      if (ws < 0 && fb) ws = base + 64 * u + __ffsll((long long)fb) - 1;
+    }
   }
   if (ws < 0) {
     if (lane == 0 && evict_slot) evict_slot[row] = -2;
     return;
   }
   wave_lds_sync();
-  const int newpos = cur_len - 1;
-  const int sub = lane % LPR, rr = lane / LPR;
 
-  float qv[EPC], kn[EPC], vn[EPC];
+  // the query unpacked (unused for fp16, whose FMAs read the packed chunk)
+  float qv[EPC];
   {
-    const U128 qq = *reinterpret_cast<const U128 *>(q + row * D + sub * EPC);
-    const U128 kk = *reinterpret_cast<const U128 *>(k_new + row * D + sub * EPC);
-    const U128 vv = *reinterpret_cast<const U128 *>(v_new + row * D + sub * EPC);
-    const T *qe = reinterpret_cast<const T *>(&qq);
-    const T *ke = reinterpret_cast<const T *>(&kk);
-    const T *ve = reinterpret_cast<const T *>(&vv);
+    const Elems16<T> qe = elems16<T>(qq);
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      qv[e] = to_f32(qe[e]);
-      kn[e] = to_f32(ke[e]);
-      vn[e] = to_f32(ve[e]);
-    }
+    for (int e = 0; e < EPC; ++e) qv[e] = to_f32(qe.e[e]);
   }
 
-  // logits of every valid slot (the new token's from registers); U wave steps
-  // of K rows are loaded before any is used
-  for (int base = 0; base < cap; base += RPI * U) {
-    U128 kk[U];
+  // A batch is U wave steps of slot rows; a slot row is read only if it holds
+  // a token other than the one in the new token's slot.
+  auto load_batch = [&](U128 *buf, __amdgpu_buffer_rsrc_t r, int base) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = base + u * RPI + rr;
       const bool ld = s < cap && s != ws && pos_s[s] >= 0;
-      kk[u] = buf_load16(rk, ld ? (uint32_t)(s * D + sub * EPC) * (uint32_t)sizeof(T) : kNoLoad);
+      buf[u] = buf_load16(r, ld ? (uint32_t)(s * D + sub * EPC) * (uint32_t)sizeof(T) : kNoLoad);
     }
+  };
+
+  // logits of every valid slot; the new token's slot, whose load is skipped,
+  // takes its key from registers
+  U128 cur[U];
+  for (int base = 0; base < cap; base += STEP) {
+    load_batch(cur, rk, base);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = base + u * RPI + rr;
       const bool inb = s < cap;
       const bool valid = inb && (s == ws || pos_s[s] >= 0);
-      const T *ke = reinterpret_cast<const T *>(&kk[u]);
-      float part = 0.f;
-      if (inb && s == ws) {
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) part += qv[e] * kn[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) part += qv[e] * to_f32(ke[e]);
-      }
+      float part = dot16<T>(qq, qv, s == ws ? kq : cur[u], 0.f);
       part = lane_group_sum<LPR>(part);
       if (sub == 0 && inb) prob[s] = valid ? part * c : -INFINITY;
     }
   }
+  // the first batch of value rows is in flight during the softmax
+  if (O) load_batch(cur, rv, 0);
   wave_lds_sync();
 
   float mx = -INFINITY;
@@ -155,7 +213,9 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
     float a = 0.f;
     if (valid) {
       a = hw_exp2(prob[s] - mx) * inv;
-      ac[s] = ((s == ws) ? 0.f : ac[s]) + a;  // read back by this same lane below
+      const float na = ((s == ws) ? 0.f : acc_s[s]) + a;
+      acc_s[s] = na;
+      ac[s] = na;
     }
     prob[s] = a;
   }
@@ -165,46 +225,29 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
     float ov[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) ov[e] = 0.f;
-    for (int base = 0; base < cap; base += RPI * U) {
-      U128 vv[U];
-      float av[U];
+    for (int base = 0; base < cap; base += STEP) {
+      if (base > 0) load_batch(cur, rv, base);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int s = base + u * RPI + rr;
-        av[u] = s < cap ? prob[s] : 0.f;
-        const bool ld = av[u] != 0.f && s != ws;
-        vv[u] = buf_load16(rv, ld ? (uint32_t)(s * D + sub * EPC) * (uint32_t)sizeof(T) : kNoLoad);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int s = base + u * RPI + rr;
-        const T *ve = reinterpret_cast<const T *>(&vv[u]);
-        if (s == ws) {
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) ov[e] += av[u] * vn[e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) ov[e] += av[u] * to_f32(ve[e]);
-        }
+        const float a = s < cap ? prob[s] : 0.f;
+        axpy16<T>(a, s == ws ? vq : cur[u], ov);
       }
     }
 #pragma unroll
     for (int e = 0; e < EPC; ++e) ov[e] = across_groups_sum<LPR>(ov[e]);
     if (rr == 0) {
-      U128 out;
-      T *oe = reinterpret_cast<T *>(&out);
+      Elems16<T> oe;
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) oe[e] = from_f32<T>(ov[e]);
-      *reinterpret_cast<U128 *>(O + row * D + sub * EPC) = out;
+      for (int e = 0; e < EPC; ++e) oe.e[e] = from_f32<T>(ov[e]);
+      *reinterpret_cast<U128 *>(O + row * D + sub * EPC) = pack16(oe);
     }
   }
 
   // the new token takes its slot
   if (rr == 0) {
-    *reinterpret_cast<U128 *>(Kr + (long)ws * D + sub * EPC) =
-        *reinterpret_cast<const U128 *>(k_new + row * D + sub * EPC);
-    *reinterpret_cast<U128 *>(Vr + (long)ws * D + sub * EPC) =
-        *reinterpret_cast<const U128 *>(v_new + row * D + sub * EPC);
+    *reinterpret_cast<U128 *>(Kr + (long)ws * D + sub * EPC) = kq;
+    *reinterpret_cast<U128 *>(Vr + (long)ws * D + sub * EPC) = vq;
   }
   if (lane == 0) pos[ws] = newpos;
 
@@ -216,7 +259,7 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
       const int p = (s == ws) ? newpos : pos_s[s];
       if (p >= 0 && p < recent_from) {
         const unsigned long long key =
-            ((unsigned long long)order_key_pos(ac[s]) << 32) | (uint32_t)(0x7FFFFFFF - p);
+            ((unsigned long long)order_key_pos(acc_s[s]) << 32) | (uint32_t)(0x7FFFFFFF - p);
         best = key < best ? key : best;
       }
     }
@@ -243,16 +286,22 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
   }
 }
 
+// Waves (rows) per workgroup: four while their probabilities, accumulators
+// and slot maps fit 64 KB of LDS, else two (up to 2730 slots).
+static inline int decode_waves_per_block(int cap) { return 3 * 4 * cap * 4 <= 65536 ? 4 : 2; }
+
 template <typename T, int D>
 static hipError_t run_decode(int rows, int cap, int cur_len, int k_heavy, int k_recent,
                              const void *q, void *K, void *V, const void *k_new,
                              const void *v_new, int32_t *slot_pos, float *acc, void *O,
                              int32_t *evict_slot, hipStream_t st) {
   const float c = kLog2e / sqrtf((float)D);
-  const size_t shm = sizeof(float) * 2 * (size_t)cap * 4;  // probabilities and slot map per wave
+  const int wpb = decode_waves_per_block(cap);
+  // probabilities, accumulators and slot map per wave
+  const size_t shm = sizeof(float) * 3 * (size_t)cap * wpb;
   {
     TimedLaunch tl_("h2o_decode", st);
-    hipLaunchKernelGGL((h2o_decode_kernel<T, D>), dim3((rows + 3) / 4), dim3(256), shm, st,
+    hipLaunchKernelGGL((h2o_decode_kernel<T, D>), dim3((rows + wpb - 1) / wpb), dim3(64 * wpb), shm, st,
                        (const T *)q, (T *)K, (T *)V, (const T *)k_new, (const T *)v_new, slot_pos,
                        acc, (T *)O, evict_slot, rows, cap, cur_len, k_heavy, k_recent, c);
   }
