@@ -134,3 +134,14 @@ def test_opt30b_full_sampled_rows(dev):
     rows = [0, 57, 1000, 2047, 3000, 3583]
     ties = run_lockstep(cfg, dev, rows, cfg.steps, gen_device=dev)
     print("opt30b sampled rows: near-tie evictions %d" % ties)
+
+
+def test_wide_cache_two_rows_per_group(dev):
+    """A slot cache wider than 1365 slots (budget 95% of the length): the
+    decode groups two rows per workgroup instead of four, to keep each row's
+    probabilities, accumulators and slot map in LDS; three rows leave the
+    second group half empty."""
+    cfg = OPT30B_H2O.with_(name="wide", batch=1, heads=3, d=64, prompt=1024, steps=440,
+                           heavy_frac=0.60, recent_frac=0.35, seed=33)
+    assert cfg.cap > 1365
+    run_lockstep(cfg, dev, list(range(3)), cfg.steps)
