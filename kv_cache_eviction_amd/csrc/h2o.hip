@@ -173,11 +173,11 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
 
   // A batch is U wave steps of slot rows; a slot row is read only if it holds
   // a token other than the one in the new token's slot.
-  auto load_batch = [&](U128 *buf, __amdgpu_buffer_rsrc_t r, int base) {
+  auto load_batch = [&](U128 *buf, __amdgpu_buffer_rsrc_t r, int base, bool want) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = base + u * RPI + rr;
-      const bool ld = s < cap && s != ws && pos_s[s] >= 0;
+      const bool ld = want && s < cap && s != ws && pos_s[s] >= 0;
       buf[u] = buf_load16(r, ld ? (uint32_t)(s * D + sub * EPC) * (uint32_t)sizeof(T) : kNoLoad);
     }
   };
@@ -186,7 +186,7 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
   // takes its key from registers
   U128 cur[U];
   for (int base = 0; base < cap; base += STEP) {
-    load_batch(cur, rk, base);
+    load_batch(cur, rk, base, true);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = base + u * RPI + rr;
@@ -197,9 +197,11 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
       if (sub == 0 && inb) prob[s] = valid ? part * c : -INFINITY;
     }
   }
-  // the first batch of value rows is in flight during the softmax
-  if (O) load_batch(cur, rv, 0);
   wave_lds_sync();
+  // the first batch of value rows is in flight during the softmax: issued
+  // after the LDS fence, and without a branch on O (no output: nothing is
+  // read), so no wait for it is placed before the softmax
+  load_batch(cur, rv, 0, O != nullptr);
 
   float mx = -INFINITY;
   for (int s = lane; s < cap; s += 64) mx = fmaxf(mx, prob[s]);
@@ -226,7 +228,7 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
 #pragma unroll
     for (int e = 0; e < EPC; ++e) ov[e] = 0.f;
     for (int base = 0; base < cap; base += STEP) {
-      if (base > 0) load_batch(cur, rv, base);
+      if (base > 0) load_batch(cur, rv, base, true);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int s = base + u * RPI + rr;
