@@ -320,7 +320,10 @@ typedef enum {
 /*
  *  batch, heads, d   rows are (sequence, head) pairs, each independent (MHA).
  *  d                 64 or 128.
- *  cap               PREFILL: the prompt length P.  DECODE: slots per row.
+ *  cap               PREFILL: the prompt length P, at most 1024.  DECODE: slots
+ *                    per row, at most 2048 (each row keeps its slot map,
+ *                    accumulators and probabilities in LDS).  Larger values
+ *                    return KVS_ERR_UNSUPPORTED before any launch.
  *  cur_len           DECODE: sequence length after appending this step's token
  *                    (the new token's position is cur_len - 1).
  *  k_heavy, k_recent DECODE: budget for this step; a token is recent if its
