@@ -145,3 +145,28 @@ def test_wide_cache_two_rows_per_group(dev):
                            heavy_frac=0.60, recent_frac=0.35, seed=33)
     assert cfg.cap > 1365
     run_lockstep(cfg, dev, list(range(3)), cfg.steps)
+
+
+@pytest.mark.parametrize("dtype,d", [("f16", 128), ("bf16", 64), ("f32", 128)])
+def test_decode_without_output_keeps_the_same_cache(dev, dtype, d):
+    """O is optional: a step without it must leave the slot cache, the slot
+    map, the accumulators and the evictions exactly as a step with it."""
+    cfg = OPT30B_H2O.with_(name="no-o", batch=2, heads=3, d=d, prompt=200, steps=40,
+                           dtype=dtype, seed=34)
+    inp = h2o_inputs(cfg, device="cpu")
+    dt = TORCH_DTYPES[cfg.dtype]
+    caches = [kv.H2OCache(cfg.batch, cfg.heads, cfg.d, cfg.cap, dt, cfg.heavy_frac,
+                          cfg.recent_frac, dev) for _ in range(2)]
+    Qp, Kp, Vp = (inp[k].to(dev) for k in ("Qp", "Kp", "Vp"))
+    for c in caches:
+        c.prefill(Qp, Kp, Vp)
+    caches[1].O.fill_(7)  # never written without the output
+    for s in range(cfg.steps):
+        q, k, v = (inp[x][s].to(dev) for x in ("q", "k", "v"))
+        caches[0].step(q, k, v, with_output=True)
+        caches[1].step(q, k, v, with_output=False)
+        torch.cuda.synchronize()
+        for name in ("K", "V", "slot_pos", "acc", "evict_slot"):
+            a, b = getattr(caches[0], name), getattr(caches[1], name)
+            assert torch.equal(a, b), "step %d: %s differs without the output" % (s, name)
+    assert bool((caches[1].O == 7).all())
