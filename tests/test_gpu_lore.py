@@ -53,7 +53,20 @@ def compare(cfg, g, o, o_rtol=1e-3):
     st = check_stats(g["row_max"], g["row_sum"], g["O"], o["row_max"], o["row_sum"], o["O"], o_rtol)
     worst = check_scores(g["S"], o["S"], cfg.n_sink, cfg.w)
     nd = check_kept(g["kept"], o["kept"], o["pooled"], cfg.n_sink, cfg.w, cfg.budget)
+    check_pooled(cfg, g)
     print("%s: stats %s, worst score rel err %.3g, kept diffs at ties %d" % (cfg.name, st, worst, nd))
+
+
+def check_pooled(cfg, g):
+    """The selector's pooled scores against the oracle's pooling of the same
+    (GPU) scores: NaN on exactly the protected tokens, and each candidate's
+    chunk mean to fp32 rounding of a sum of at most `chunk` terms."""
+    Pg = g["pooled"].astype(np.float64)
+    Po = oracle.pooled_scores(g["S"].astype(np.float64), cfg.n_sink, cfg.w, cfg.chunk)
+    assert np.array_equal(np.isnan(Pg), np.isnan(Po)), "pooled NaNs differ from the protected set"
+    fin = ~np.isnan(Po)
+    err = np.abs(Pg[fin] - Po[fin])
+    assert np.all(err <= 1e-6 * np.abs(Po[fin]) + 1e-37), "pooled score error %g" % err.max()
 
 
 def test_tiny_fp32(dev):
@@ -113,7 +126,8 @@ def test_full_size_sampled_head(dev, cfg, b, g):
     gs = {"row_max": gr["row_max"][b:b + 1, g * G:(g + 1) * G],
           "row_sum": gr["row_sum"][b:b + 1, g * G:(g + 1) * G],
           "O": gr["O"][b:b + 1, g * G:(g + 1) * G],
-          "S": gr["S"][b:b + 1, g:g + 1], "kept": gr["kept"][b:b + 1, g:g + 1]}
+          "S": gr["S"][b:b + 1, g:g + 1], "kept": gr["kept"][b:b + 1, g:g + 1],
+          "pooled": gr["pooled"][b:b + 1, g:g + 1]}
     compare(one.with_(name=cfg.name), gs, o)
 
 
