@@ -1080,8 +1080,10 @@ static hipError_t run_score_w(const void *Q, const void *K, const void *V, const
   // LORE (MODE 0): about one workgroup per CU (256 on MI355X; its LDS admits
   // one per CU), each over a long token range, so each workgroup's set-up
   // (query and y fragments, row constants) is paid once per CU: 11% faster
-  // than ~1024 shorter workgroups.  MODE 1 keeps ~1024.
-  const long target = MODE == 0 ? 256 : 1024;
+  // than ~1024 shorter workgroups.  MODE 1 (no value tiles, two workgroups
+  // per CU fit) takes ~512: 5% faster than 1024 on the window score, while
+  // 256 left half of each CU's slots empty (22% slower).
+  const long target = MODE == 0 ? 256 : 512;
   long tpw = ((long)geo.n * units + target - 1) / target;
   tpw = (tpw + 63) / 64 * 64;
   if (tpw < 64) tpw = 64;
