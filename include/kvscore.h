@@ -122,13 +122,22 @@ kvs_status kvscore_probs(const kvs_lore_desc *desc, const void *Q, const void *K
  *  Q, K, V                  as for kvscore_probs.
  *  W_O      [d_model][h_q*d] the attention output projection (linear-layer layout).
  *  omega    [batch][m] fp32  trajectory reliability weights (Eq. 10 output, a
- *           softmax, so >= 0; an entry <= 0 gives its trajectory no weight).
+ *           softmax).  The domain is omega >= 0.  A row whose weight
+ *           lambda_l * omega_j / t is below FLT_MIN (1.2e-38) -- in particular
+ *           any omega_j <= 0, which lies outside the domain -- contributes
+ *           nothing to S: the kernel folds log2 of the row weight into the
+ *           exponent of a, so it cannot carry a negative or subnormal weight.
+ *           For omega_j < 0 this differs from Eq. 7 read literally (which
+ *           would subtract that trajectory's term); no error is raised, since
+ *           omega lives in device memory and is not read on the host.
  *  row_max, row_sum, O      kvscore_probs outputs for the same inputs.
  *  S        [batch][h_kv][n] fp32 out: the KV head's score of every token
  *           (protected tokens are scored too; selection ignores them).
  *
  * For bf16 input the value-side products (V.G_h, V.y, P.V) run in fp16 after
- * an exact bf16->fp16 conversion of V; |V| must stay below 65504.
+ * a bf16->fp16 conversion of V.  That conversion is exact in fp16's normal
+ * range (2^-14 <= |v| < 65504); smaller magnitudes become fp16 subnormals,
+ * truncated (absolute error below 2^-24); |V| must stay below 65504.
  */
 kvs_status kvscore_deletion(const kvs_lore_desc *desc, const void *Q, const void *K, const void *V,
                             const void *W_O, const float *omega,

@@ -631,15 +631,20 @@ vnorm_kernel(const Tin *__restrict__ V, const typename ValueType<Tin>::type *__r
 // query rows of each 16-row block, so the sum over query rows is in-lane
 // plus two cross-lane adds per 16 tokens; the per-wave partial sums are
 // combined across waves in a fixed order.
-//   MODE 0 (LORE): out = out_scale * sum_h sum_q wr_q * a/(1-a+eps) * sqrt(max(0, N - 2x + pi)),
+//   MODE 0 (LORE): out = out_scale * sum_h sum_q wr_q * a/(1-a+eps) * sqrt(|N - 2x + pi|),
 //                  x = v . (y_hi + y_lo) as MFMA products whose accumulator
 //                  starts at -pi/2, so N - 2*acc = N - 2x + pi; for 16-bit
 //                  inputs y_hi . v runs on fp16 MFMA and y_lo . v as one
 //                  block-scaled fp8 MFMA (y_lo e4m3 with its row's power-of-
 //                  two scale, v e5m2): y_lo is about 2^-11 of y, so the fp8
 //                  roundings stay near 2^-15 of x;
-//                  sqrt(q2)/(1+eps-a) is formed as q2 * rsqrt(q2 (1+eps-a)^2)
-//                  with q2 clamped at 1e-30 instead of 0.
+//                  sqrt(q2)/(1+eps-a) is formed as |q2| * rsqrt(|q2| (1+eps-a)^2
+//                  + FLT_MIN).  N - 2x + pi = (v-o)^T G~ (v-o) >= 0 in exact
+//                  arithmetic; it goes negative only by rounding when v ~ o,
+//                  where |q2| and max(0, q2) give the same magnitude to the
+//                  score's accuracy, and the absolute value is a free source
+//                  modifier where a clamp would cost an instruction.  Rows of
+//                  weight below FLT_MIN contribute nothing.
 //   MODE 1 (H2O):  out = sum over causal rows of a
 template <typename Tin, int D, int MODE, int MAXW, int QBW>
 __global__ void __launch_bounds__(64 * MAXW)
@@ -713,10 +718,12 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
       rwr[qb][j] = 0.f;
       if (MODE == 0) {
         // a * w_r = 2^(e - beta + log2 w_r): the exponent carries the row
-        // weight; rows of weight <= 0 contribute nothing (the weights are a
-        // softmax times a nonnegative lambda)
+        // weight and 1/w_r recovers a for the denominator.  Rows of weight
+        // below FLT_MIN contribute nothing: the weights are a softmax times a
+        // nonnegative lambda, and below FLT_MIN 1/w_r would overflow to inf
+        // and turn 0 * inf into NaN for every token whose a*w_r underflows
         const float w_r = cs.z;
-        if (w_r > 0.f) {
+        if (w_r >= kTiny) {
           beta[qb][j] -= log2f(w_r);
           rwr[qb][j] = 1.f / w_r;
         } else {
