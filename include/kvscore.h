@@ -301,6 +301,29 @@ kvs_status kvscore_topb_select(const kvs_lore_desc *desc, const float *S, int32_
                                float *pooled, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * kvscore_topb_select without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, outputs and results as
+ * kvscore_topb_select; its scratch is a fixed array the library owns on each
+ * GPU it runs on, KVS_TOPB_NOALLOC_MAX_BYTES bytes, held until the process
+ * ends.  Nothing is allocated or freed by the call.
+ *
+ * Limit: kvs_topb_workspace_bytes(desc) must not exceed
+ * KVS_TOPB_NOALLOC_MAX_BYTES (e.g. 1 x 8 KV heads x 131072 tokens with chunk
+ * 4 needs 2 MiB; 3584 rows x 1024 tokens with chunk 1 needs 29 MiB); larger
+ * inputs return KVS_ERR_UNSUPPORTED before anything is enqueued.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (other streams, other threads) race and must be serialised by the
+ * caller.  A call rewrites everything of the scratch it reads, so the
+ * contents left by an earlier call never matter.
+ * Errors: as kvscore_topb_select; KVS_ERR_HIP if the scratch's device address
+ * cannot be looked up on the current device.
+ */
+#define KVS_TOPB_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+kvs_status kvscore_topb_select_noalloc(const kvs_lore_desc *desc, const float *S, int32_t *kept,
+                                       float *pooled, void *stream);
+
+/*
  * Gather kept rows into a compact cache (LORE-KV: decoding then runs on the
  * compressed cache).  Also used to load the H2O slot cache after the prompt
  * reduction.

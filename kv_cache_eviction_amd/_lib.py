@@ -24,7 +24,7 @@ CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
 EXPORTS = ("kvs_lore_workspace_bytes", "kvs_topb_workspace_bytes", "kvscore_probs", "kvscore_deletion",
            "kvscore_baseline_scores", "kvscore_reliability_weights", "kvs_fidelity_workspace_bytes",
            "kvscore_output_fidelity", "kvscore_counter_causal",
-           "kvs_refresh_workspace_bytes", "kvscore_refresh", "kvscore_topb_select", "kv_compact", "kvs_h2o_workspace_bytes",
+           "kvs_refresh_workspace_bytes", "kvscore_refresh", "kvscore_topb_select", "kvscore_topb_select_noalloc", "kv_compact", "kvs_h2o_workspace_bytes",
            "kvscore_h2o_accumulate", "kvs_timing_enable", "kvs_timing_count", "kvs_timing_read",
            "kvs_timing_reset", "kvs_last_error")
 
@@ -96,6 +96,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvs_topb_workspace_bytes.argtypes = [LP]
     lib.kvscore_topb_select.restype = i32
     lib.kvscore_topb_select.argtypes = [LP, vp, vp, vp, vp, sz, vp]
+    lib.kvscore_topb_select_noalloc.restype = i32
+    lib.kvscore_topb_select_noalloc.argtypes = [LP, vp, vp, vp, vp]
     lib.kv_compact.restype = i32
     lib.kv_compact.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kvs_h2o_workspace_bytes.restype = sz
@@ -343,6 +345,19 @@ def kvscore_topb_select(desc, S, kept, pooled, ws, stream=None):
     _check(load().kvscore_topb_select(ctypes.byref(desc), _ptr(S), _ptr(kept), _ptr(pooled),
                                       _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "kvscore_topb_select")
+
+
+def kvscore_topb_select_noalloc(desc, S, kept, pooled=None, stream=None):
+    """kvscore_topb_select on the library's own scratch (no workspace, no
+    allocation); rejects inputs whose selection needs more than
+    KVS_TOPB_NOALLOC_MAX_BYTES of scratch."""
+    b, hk, n = desc.batch, desc.h_kv, desc.n
+    _need(S, "S", (b, hk, n), torch.float32)
+    _need(kept, "kept", (b, hk, desc.n_keep), torch.int32)
+    _need(pooled, "pooled", (b, hk, n), torch.float32, optional=True)
+    _check(load().kvscore_topb_select_noalloc(ctypes.byref(desc), _ptr(S), _ptr(kept),
+                                              _ptr(pooled), _stream(stream)),
+           "kvscore_topb_select_noalloc")
 
 
 def kv_compact(K, V, kept, K_out, V_out, pos_out=None, score_in=None, score_out=None,

@@ -472,6 +472,35 @@ KVS_API kvs_status kvscore_topb_select(const kvs_lore_desc *desc, const float *S
   return hip_status(e, "top-B select");
 }
 
+static_assert(kvs::kTopbScratchBytes == KVS_TOPB_NOALLOC_MAX_BYTES,
+              "the header states the library's scratch size");
+
+KVS_API kvs_status kvscore_topb_select_noalloc(const kvs_lore_desc *desc, const float *S,
+                                               int32_t *kept, float *pooled, void *stream) {
+  kvs_status st = check_select(desc);
+  if (st != KVS_OK) return st;
+  if (!S || !kept) return fail(KVS_ERR_INVALID, "kvscore_topb_select_noalloc: S or kept is NULL");
+  const size_t need = topb_bytes_of(desc);
+  if (need > kvs::kTopbScratchBytes) {
+    char buf[200];
+    snprintf(buf, sizeof buf,
+             "kvscore_topb_select_noalloc: needs %zu bytes of scratch, above the library's "
+             "%zu-byte maximum (use kvscore_topb_select with a workspace)",
+             need, kvs::kTopbScratchBytes);
+    return fail(KVS_ERR_UNSUPPORTED, buf);
+  }
+  void *scratch = nullptr;
+  hipError_t e = kvs::topb_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "kvscore_topb_select_noalloc: scratch address");
+  const int n_cand = desc->n - desc->n_sink - desc->w;
+  const int B = desc->budget < n_cand ? desc->budget : n_cand;
+  const int n_keep = desc->n_sink + B + desc->w;
+  e = kvs::launch_topb(S, desc->batch * desc->h_kv, desc->n, desc->n_sink, desc->w, desc->chunk,
+                       desc->budget, n_keep, scratch, kept, pooled,
+                       static_cast<hipStream_t>(stream));
+  return hip_status(e, "top-B select (library scratch)");
+}
+
 KVS_API kvs_status kv_compact(int32_t batch, int32_t heads, int32_t n_src, int32_t n_keep,
                               int32_t cap_dst, int32_t d, int32_t dtype, const void *K,
                               const void *V, const int32_t *kept, void *K_out, void *V_out,

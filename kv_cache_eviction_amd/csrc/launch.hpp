@@ -86,6 +86,10 @@ hipError_t launch_score(int etype, int d, int mode, const void *Q, const void *K
 
 // Selection and compaction.
 size_t topb_workspace_bytes(int rows, int n, int chunk);
+// The library-owned scratch of the allocation-free selection: its size, and
+// its device address on the current device (looked up once per device).
+constexpr size_t kTopbScratchBytes = (size_t)32 << 20;
+hipError_t topb_scratch(void **ptr);
 hipError_t launch_topb(const float *S, int rows, int n, int n_sink, int w, int chunk, int budget,
                        int n_keep, void *ws, int32_t *kept, float *pooled, hipStream_t st);
 // kept [rows / kept_div][n_keep]: rows share lists in groups of kept_div;

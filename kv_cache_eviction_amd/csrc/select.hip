@@ -16,6 +16,9 @@
 // to find the threshold key tau and how many tokens of the tau-chunks are
 // still needed, and writes the selection in ascending index order with
 // block-wide scans.
+#include <atomic>
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "timing.hpp"
@@ -367,6 +370,42 @@ hipError_t launch_topb(const float *S, int rows, int n, int n_sink, int w, int c
                        budget, n_keep, nchunks, nseg, keys_ws, cand, cand_n, kept);
   }
   return hipGetLastError();
+}
+
+// Scratch of the allocation-free selection (kvscore_topb_select_noalloc): the
+// level-1 chunk keys, candidate lists and counts that kvscore_topb_select
+// otherwise takes from the caller's workspace.  A file-scope device array, so
+// every GPU the library runs on holds its own copy from the code object's
+// load until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is taken once per device
+// with hipGetSymbolAddress (that device current) and only that address is
+// ever passed to a kernel.  Every launch writes each scratch entry it reads
+// earlier in the same call (keys of every chunk, the lists up to their
+// counts, the counts of every segment), so nothing needs clearing between
+// calls; calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) uint8_t scratch[kTopbScratchBytes];
+
+hipError_t topb_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void *> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 // Compaction: K'[row][r] = K[row][kept[r]] (and V), 16 bytes per thread.
