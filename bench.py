@@ -86,20 +86,55 @@ def measured_traffic(kernel):
     return int(round((k["fetch_kib"] * rec["fetch_scale"] + k["write_kib"] * rec["write_scale"]) * 1024))
 
 
+# measured ceilings (kvs_measure_peaks), filled in by main(): reported beside
+# the published peaks, which stay the roofline denominators
+MEASURED = {}
+
+
+def with_measured(roof):
+    """Add the achieved rate's fraction of the measured ceiling of the same
+    resource (dense bf16 MFMA loop, or streaming HBM read)."""
+    if roof is None:
+        return None
+    key = "mfma_bf16_tflops" if roof["bound"] == "mfma" else "hbm_read_gbs"
+    if key in MEASURED:
+        roof["measured_peak"] = MEASURED[key]
+        roof["frac_of_measured"] = round(roof["achieved"] / MEASURED[key], 4)
+    return roof
+
+
 def roofline_of(name, work, avg_ms):
     w = work.get(name)
     if w is None:
         return None
     if w["bound"] == "mfma":
         achieved = w["flops"] / (avg_ms * 1e-3) / 1e12
-        return {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(name),
-                "algorithmic_per_launch": w["flops"], "avg_launch_ms": round(avg_ms, 4)}
+        return with_measured({"kernel": name, "bound": "mfma", "achieved": round(achieved, 2),
+                              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                              "traffic": measured_traffic(name),
+                              "algorithmic_per_launch": w["flops"], "avg_launch_ms": round(avg_ms, 4)})
     achieved = w["bytes"] / (avg_ms * 1e-3) / 1e9
-    return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
-            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(name),
-            "algorithmic_per_launch": w["bytes"], "avg_launch_ms": round(avg_ms, 4)}
+    return with_measured({"kernel": name, "bound": "hbm", "achieved": round(achieved, 2),
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(name),
+                          "algorithmic_per_launch": w["bytes"], "avg_launch_ms": round(avg_ms, 4)})
+
+
+def measure_peaks(kv, torch, dev):
+    """Dense bf16 MFMA and streaming HBM read ceilings on this GPU (1 GiB
+    buffer, so the read exceeds the 256 MB last-level cache)."""
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    tf, gb = kv.kvs_measure_peaks(buf)
+    del buf
+    torch.cuda.empty_cache()
+    MEASURED["mfma_bf16_tflops"] = round(tf, 1)
+    MEASURED["hbm_read_gbs"] = round(gb, 1)
+    return {"mfma_bf16_tflops": round(tf, 1), "mfma_frac_of_spec": round(tf / PEAK_BF16_TFLOPS, 4),
+            "hbm_read_gbs": round(gb, 1), "hbm_frac_of_spec": round(gb / PEAK_HBM_GBS, 4),
+            "method": "kvs_measure_peaks: back-to-back v_mfma_f32_16x16x32_bf16 on four "
+                      "accumulators per wave (2048 x 4 waves); waves streaming 64 KiB each "
+                      "with eight 16-byte-per-lane loads in flight over 1 GiB; best of 3"}
 
 
 def cpu_baseline(cfg, layers_data, min_seconds=10.0, max_layers=4):
@@ -198,9 +233,10 @@ def bench_h2o(kv, torch, dev, layers=4):
             "decode_ms_total": round(total, 3),
             "decode_step_kernel_ms": round(dec_ms, 4),
             "slots_attended_per_s": round(layers * rows * slots / (total * 1e-3), 1),
-            "roofline": {"kernel": "h2o_decode", "bound": "hbm", "achieved": round(hbm, 1),
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(hbm / PEAK_HBM_GBS, 4),
-                         "traffic": measured_traffic("h2o_decode")},
+            "roofline": with_measured({"kernel": "h2o_decode", "bound": "hbm",
+                                       "achieved": round(hbm, 1), "peak": PEAK_HBM_GBS,
+                                       "unit": "GB/s", "frac": round(hbm / PEAK_HBM_GBS, 4),
+                                       "traffic": measured_traffic("h2o_decode")}),
             "prefill_compact": {"kernel_ms": round(pc[0], 4), "bytes": pc_bytes,
                                 "achieved_gbs": round(pc_bytes / (pc[0] * 1e-3) / 1e9, 1),
                                 "frac": round(pc_bytes / (pc[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
@@ -210,24 +246,33 @@ def bench_h2o(kv, torch, dev, layers=4):
 def bench_compact_qwen(kv, torch, dev, reps=20):
     """kv_compact on the Qwen2.5-14B batch shape (8 sequences x 8 KV heads of
     32K tokens, bf16, keep 1 + 512 + 32 per head): the HBM-bound gather at a
-    size where it is not launch-bound.  Each of the reps gathers a different
-    random kept set into its own output, so the 20 x 17.9 MB of rows read
-    (K/V 1.07 GB) do not stay in the 256 MB MALL between reps; the launches
-    run back to back between one event pair (per-launch events would add
-    about 2 us to a 6 us kernel)."""
+    size where it is not launch-bound.  The kept sets have the selector's
+    structure: the sink, the window, and B/chunk = 128 whole aligned chunks
+    of 4 candidates (chunk pooling ranks whole chunks), drawn at random per
+    row.  Each of the reps gathers a different set into its own output, so
+    the rows read (K/V 1.07 GB) do not stay in the 256 MB MALL between reps;
+    the launches run back to back between one event pair (per-launch events
+    would add about 2 us to a few-us kernel)."""
     from kvsynth import QWEN_14B_BATCH as cfg
     b, hk, n, d = cfg.batch, cfg.h_kv, cfg.n, cfg.d
-    n_keep = 1 + cfg.budget + cfg.w
+    n_keep = cfg.n_sink + cfg.budget + cfg.w
     g = torch.Generator(device=dev)
     g.manual_seed(4040)
     K = torch.randn(b, hk, n, d, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
     V = torch.randn(b, hk, n, d, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
     rows = b * hk
+    ch = cfg.chunk
+    # whole chunks inside the candidates [n_sink, n - w)
+    c_lo = (cfg.n_sink + ch - 1) // ch
+    c_hi = (n - cfg.w) // ch
+    per = cfg.budget // ch
     tail = torch.arange(n - cfg.w, n, device=dev).expand(rows, cfg.w)
+    sink = torch.arange(cfg.n_sink, device=dev).expand(rows, cfg.n_sink)
     sets = []
     for _ in range(reps):
-        mid = torch.rand(rows, n - 1 - cfg.w, generator=g, device=dev).argsort(dim=1)[:, :cfg.budget] + 1
-        kept = torch.cat([torch.zeros(rows, 1, dtype=torch.long, device=dev), mid, tail], dim=1)
+        chunks = torch.rand(rows, c_hi - c_lo, generator=g, device=dev).argsort(dim=1)[:, :per] + c_lo
+        mid = (chunks[:, :, None] * ch + torch.arange(ch, device=dev)).reshape(rows, per * ch)
+        kept = torch.cat([sink, mid, tail], dim=1)
         kept = kept.sort(dim=1).values.to(torch.int32).reshape(b, hk, n_keep).contiguous()
         Ko = torch.empty(b, hk, n_keep, d, dtype=torch.bfloat16, device=dev)
         sets.append((kept, Ko, torch.empty_like(Ko)))
@@ -251,10 +296,12 @@ def bench_compact_qwen(kv, torch, dev, reps=20):
     del K, V, sets, scrub
     torch.cuda.empty_cache()
     return {"workload": cfg.name + "-compact", "kernel_ms": round(ms, 4), "bytes": nbytes,
+            "kept_sets": "sink + %d random whole chunks of %d + window, a different set per rep"
+                         % (per, ch),
             "timing": "%d back-to-back launches, distinct kept sets and outputs" % reps,
-            "roofline": {"kernel": "compact", "bound": "hbm", "achieved": round(gbs, 1),
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": None}}
+            "roofline": with_measured({"kernel": "compact", "bound": "hbm", "achieved": round(gbs, 1),
+                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                       "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None})}
 
 
 def bench_refresh(kv, torch, dev, reps=10):
@@ -343,6 +390,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
+    print("[bench] measured peaks", file=sys.stderr, flush=True)
+    peaks = measure_peaks(kv, torch, dev)
     cfg = LORE_CONFIGS[args.config]
     layers = args.layers or cfg.layers
     dt = TORCH_DTYPES[cfg.dtype]
@@ -477,6 +526,7 @@ def main():
                    "h_q": cfg.h_q, "h_kv": cfg.h_kv, "d": cfg.d, "d_model": cfg.d_model,
                    "w": cfg.w, "m": cfg.m, "t": cfg.t, "budget": cfg.budget, "chunk": cfg.chunk},
         "roofline": roof,
+        "measured_peaks": peaks,
         "layer_ms": round(layer_ms, 4),
         "layer_mfma_frac": round(credited / (layer_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernels": kernels,

@@ -403,6 +403,25 @@ kvs_status kvscore_h2o_accumulate(const kvs_h2o_desc *desc, int32_t mode,
                                   void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Measured ceilings, reported beside the published peaks (a diagnostic, not
+ * part of the path): the dense bf16 MFMA rate of v_mfma_f32_16x16x32_bf16
+ * issued back to back on four independent accumulators per wave (2048
+ * workgroups of four waves), and the streaming HBM read rate of waves that
+ * each read one contiguous 64 KiB range with eight 16-byte-per-lane loads in
+ * flight (the row-read pattern of the H2O decode and the compaction).
+ *
+ *  buf, bytes  caller-owned device buffer, >= 66 MiB (use >= 1 GiB so the
+ *              read exceeds the 256 MB last-level cache); its contents are
+ *              read and partly overwritten.
+ *  mfma_bf16_tflops, hbm_read_gbs  host outputs: best of three timed runs
+ *              after a warm-up (HIP events on `stream`).
+ * Unlike every other entry point this one waits for its own work.
+ * Errors: KVS_ERR_INVALID for NULL pointers, a small or misaligned buffer.
+ */
+kvs_status kvs_measure_peaks(void *buf, size_t bytes, float *mfma_bf16_tflops,
+                             float *hbm_read_gbs, void *stream);
+
+/*
  * Per-launch kernel timing, for benchmarks and profiling.  While enabled,
  * every kernel the library launches is bracketed by two HIP events recorded
  * on its launch stream (process-wide).  kvs_timing_read synchronises on the

@@ -25,7 +25,7 @@ EXPORTS = ("kvs_lore_workspace_bytes", "kvs_topb_workspace_bytes", "kvscore_prob
            "kvscore_baseline_scores", "kvscore_reliability_weights", "kvs_fidelity_workspace_bytes",
            "kvscore_output_fidelity", "kvscore_counter_causal",
            "kvs_refresh_workspace_bytes", "kvscore_refresh", "kvscore_topb_select", "kvscore_topb_select_noalloc", "kv_compact", "kvs_h2o_workspace_bytes",
-           "kvscore_h2o_accumulate", "kvs_timing_enable", "kvs_timing_count", "kvs_timing_read",
+           "kvscore_h2o_accumulate", "kvs_measure_peaks", "kvs_timing_enable", "kvs_timing_count", "kvs_timing_read",
            "kvs_timing_reset", "kvs_last_error")
 
 
@@ -96,6 +96,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvs_topb_workspace_bytes.argtypes = [LP]
     lib.kvscore_topb_select.restype = i32
     lib.kvscore_topb_select.argtypes = [LP, vp, vp, vp, vp, sz, vp]
+    lib.kvs_measure_peaks.restype = i32
+    lib.kvs_measure_peaks.argtypes = [vp, sz, ctypes.POINTER(ctypes.c_float),
+                                      ctypes.POINTER(ctypes.c_float), vp]
     lib.kvscore_topb_select_noalloc.restype = i32
     lib.kvscore_topb_select_noalloc.argtypes = [LP, vp, vp, vp, vp]
     lib.kv_compact.restype = i32
@@ -421,6 +424,17 @@ def kvscore_h2o_accumulate(desc, mode, q, K, V=None, k_new=None, v_new=None, slo
                                          _ptr(k_new), _ptr(v_new), _ptr(slot_pos), _ptr(acc),
                                          _ptr(O), _ptr(evict_slot), _ptr(ws), nb, _stream(stream)),
            "kvscore_h2o_accumulate")
+
+
+def kvs_measure_peaks(buf, stream=None):
+    """Measured dense bf16 MFMA TFLOP/s and streaming HBM read GB/s on a
+    caller-owned device buffer (uint8, >= 66 MiB; 1 GiB recommended)."""
+    if buf is None or not buf.is_cuda or not buf.is_contiguous():
+        raise KvsError("kvs_measure_peaks: buf must be a contiguous device tensor")
+    tf, gb = ctypes.c_float(), ctypes.c_float()
+    _check(load().kvs_measure_peaks(_ptr(buf), buf.numel() * buf.element_size(), ctypes.byref(tf),
+                                    ctypes.byref(gb), _stream(stream)), "kvs_measure_peaks")
+    return tf.value, gb.value
 
 
 def kvs_timing_enable(on: bool = True):

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvscore.so")
-SOURCES = ["attn.hip", "deletion.hip", "select.hip", "h2o.hip", "reliability.hip", "fidelity.hip",
+SOURCES = ["attn.hip", "deletion.hip", "select.hip", "h2o.hip", "reliability.hip", "fidelity.hip", "peaks.hip",
            "timing.cpp",
            "capi.cpp"]
 ARCH = "gfx950"

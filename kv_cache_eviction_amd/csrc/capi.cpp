@@ -612,6 +612,18 @@ KVS_API kvs_status kvscore_h2o_accumulate(const kvs_h2o_desc *desc, int32_t mode
   return hip_status(e, "decode step");
 }
 
+KVS_API kvs_status kvs_measure_peaks(void *buf, size_t bytes, float *mfma_bf16_tflops,
+                                     float *hbm_read_gbs, void *stream) {
+  if (!buf || !mfma_bf16_tflops || !hbm_read_gbs)
+    return fail(KVS_ERR_INVALID, "kvs_measure_peaks: a required pointer is NULL");
+  if (bytes < ((size_t)66 << 20))
+    return fail(KVS_ERR_INVALID, "kvs_measure_peaks: the buffer must hold at least 66 MiB");
+  if (check_aligned("kvs_measure_peaks", {buf}) != KVS_OK) return KVS_ERR_INVALID;
+  const hipError_t e = kvs::measure_peaks(buf, bytes, mfma_bf16_tflops, hbm_read_gbs,
+                                          static_cast<hipStream_t>(stream));
+  return hip_status(e, "kvs_measure_peaks");
+}
+
 KVS_API kvs_status kvs_timing_enable(int32_t on) {
   kvs::timing_enable(on);
   return ok();

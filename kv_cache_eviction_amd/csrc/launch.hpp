@@ -99,6 +99,11 @@ hipError_t launch_compact(int rows, int n_src, int n_keep, int cap_dst, int row_
                           void *V_out, int32_t *pos_out, const void *payload_in,
                           void *payload_out, hipStream_t st, int kept_div = 1);
 
+// Measured ceilings: dense bf16 MFMA TFLOP/s and streaming HBM read GB/s,
+// on the caller's buffer (>= 64 MiB + 2 MiB); waits for its own work.
+hipError_t measure_peaks(void *buf, size_t bytes, float *mfma_tflops, float *read_gbs,
+                         hipStream_t st);
+
 // H2O decode step.
 hipError_t launch_h2o_decode(int etype, int d, int rows, int cap, int cur_len, int k_heavy,
                              int k_recent, const void *q, void *K, void *V, const void *k_new,
