@@ -352,7 +352,8 @@ typedef enum {
 /*
  *  batch, heads, d   rows are (sequence, head) pairs, each independent (MHA).
  *  d                 64 or 128.
- *  cap               PREFILL: the prompt length P, at most 1024.  DECODE: slots
+ *  cap               PREFILL: the prompt length P, at most 16384 (and
+ *                    heads * ceil(P/256) at most 65535).  DECODE: slots
  *                    per row, at most 2048 (each row keeps its slot map,
  *                    accumulators and probabilities in LDS).  Larger values
  *                    return KVS_ERR_UNSUPPORTED before any launch.

@@ -261,11 +261,19 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
     }
     if (wg_lo > t_begin) it0 = min(nt, (wg_lo - t_begin) / TN);
   }
+  // causal prompt rows (mode 1): no row of this workgroup sees a key after
+  // its last head's last row, so the tiles past it are neither loaded nor
+  // stepped through (their rows' statistics come out empty for this split)
+  int it_end = nt;
+  if (!REV && geo.mode == 1) {
+    const int wg_last = min(n - 1, min(geo.group, hs * hpw + hpw) * 64 - 1);
+    it_end = wg_last < t_begin ? 0 : min(nt, (wg_last - t_begin) / TN + 1);
+  }
   wait_vmem_all();
   prefetch(t_begin + it0 * TN);
   stash(it0 & 1);
   __syncthreads();
-  for (int it = it0; it < nt; ++it) {
+  for (int it = it0; it < it_end; ++it) {
     const int t0 = t_begin + it * TN;
     const int cur = it & 1;
     prefetch(t0 + TN);  // past the split end this reads nothing

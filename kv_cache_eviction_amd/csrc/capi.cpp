@@ -527,6 +527,10 @@ KVS_API kvs_status kv_compact(int32_t batch, int32_t heads, int32_t n_src, int32
 
 namespace {
 
+// Longest prompt the prefill takes: its column-sum pass runs one launch per
+// eight 64-row blocks of the prompt (32 launches at 16384 tokens).
+constexpr int kMaxPrefill = 16384;
+
 kvs_status check_h2o(const kvs_h2o_desc *d, int mode) {
   if (!d) return fail(KVS_ERR_INVALID, "descriptor is NULL");
   if (d->batch < 1 || d->heads < 1 || d->cap < 1)
@@ -535,7 +539,11 @@ kvs_status check_h2o(const kvs_h2o_desc *d, int mode) {
   if (d->dtype != KVS_F32 && d->dtype != KVS_BF16 && d->dtype != KVS_F16)
     return fail(KVS_ERR_INVALID, "unknown dtype");
   if (mode == KVS_H2O_PREFILL) {
-    if (d->cap > 1024) return fail(KVS_ERR_UNSUPPORTED, "prefill prompt longer than 1024");
+    if (d->cap > kMaxPrefill)
+      return fail(KVS_ERR_UNSUPPORTED, "prefill prompt longer than 16384");
+    // the attention pass launches heads * ceil(cap/64 / 4) workgroups along grid y
+    if ((long)d->heads * (((d->cap + 63) / 64 + 3) / 4) > 65535)
+      return fail(KVS_ERR_UNSUPPORTED, "prefill: heads * ceil(cap / 256) above 65535");
   } else if (mode == KVS_H2O_DECODE) {
     if (d->cap > 2048) return fail(KVS_ERR_UNSUPPORTED, "decode slot count above 2048");
     if (d->cur_len < 1 || d->k_heavy < 0 || d->k_recent < 0)

@@ -761,7 +761,13 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
   }
 
   const int t_begin = blockIdx.x * tpw;
-  const int t_end = min(n, t_begin + tpw);
+  int t_end = min(n, t_begin + tpw);
+  if (MODE == 1 && geo.mode == 1 && accumulate) {
+    // causal prompt rows: no row of this head subset sees a token after its
+    // last row, so an accumulating launch leaves those tokens untouched
+    t_end = min(t_end, min(n, (hv0 + hcount) * 64));
+    if (t_end <= t_begin) return;  // (workgroup-uniform)
+  }
   const float *Nh = Nn + head * (long)n_pad;
   float *Sout = S + ((long)b * h_kv + kvh) * n;
   const int nt = (t_end - t_begin + TN - 1) / TN;
@@ -1096,15 +1102,20 @@ static hipError_t run_score_w(const void *Q, const void *K, const void *V, const
   if (tpw < 64) tpw = 64;
   if (tpw > kMaxRangeTokens) tpw = kMaxRangeTokens;
   const int blocks = (int)((geo.n + tpw - 1) / tpw);
-  // head subsets in stream order; the later ones add to S
-  for (int hv0 = 0; hv0 < geo.group; hv0 += hpw) {
+  // head subsets in stream order, the later ones adding to S.  Causal prompt
+  // rows (geo.mode 1) go from the last subset to the first: the first launch
+  // covers (and writes) every token, and each later one only the tokens up
+  // to its own last row.
+  const int nsub = (geo.group + hpw - 1) / hpw;
+  for (int k = 0; k < nsub; ++k) {
+    const int hv0 = (geo.mode == 1 ? nsub - 1 - k : k) * hpw;
     const int hcount = std::min(hpw, geo.group - hv0);
     {
       TimedLaunch tl_((MODE == 0 ? "score_lore" : "score_h2o_colsum"), st);
       hipLaunchKernelGGL((score_kernel<Tin, D, MODE, MAXW, QBW>), dim3(blocks, h_kv, batch),
                          dim3(64 * MAXW), 0, st, (const Tin *)Q, (const Tin *)K, (const Tin *)V,
                          (const TV *)Yhi, (const TV *)Ylo, consts, Nn, n_pad, geo, h_kv, hv0,
-                         hcount, hv0 > 0 ? 1 : 0, (int)tpw, eps, out_scale, S);
+                         hcount, k > 0 ? 1 : 0, (int)tpw, eps, out_scale, S);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -152,6 +152,18 @@ def test_ragged_prompt_lockstep(dev):
     run_lockstep(cfg, dev, list(range(4)), cfg.steps)
 
 
+@pytest.mark.parametrize("prompt,heavy,recent", [(2048, 0.1, 0.1), (3000, 0.2, 0.1)],
+                         ids=["p2048", "p3000-ragged"])
+def test_long_prompt_lockstep(dev, prompt, heavy, recent):
+    """Prompts beyond 1024 tokens (the H2O page's long-sequence runs use 2048
+    and more): the column-sum pass then runs several head-subset launches
+    from the last rows to the first, and the attention pass's workgroups stop
+    at their rows' last key.  P = 3000 is not a multiple of 64."""
+    cfg = OPT30B_H2O.with_(name="long", batch=2, heads=3, prompt=prompt, steps=48,
+                           heavy_frac=heavy, recent_frac=recent, seed=35)
+    run_lockstep(cfg, dev, list(range(cfg.batch * cfg.heads)), cfg.steps)
+
+
 def test_opt30b_full_sampled_rows(dev):
     """The full 64 x 56 decode (the bench's launch shape), all 512 steps; the
     oracle follows 65 of the 3584 (sequence, head) rows in lockstep: one row
