@@ -217,6 +217,19 @@ def bench_h2o(kv, torch, dev, layers=4):
     kv.kvs_timing_enable(False)
     kv.kvs_timing_reset()
     dec = [ms for nm, ms in recs if nm == "h2o_decode"]
+    # the prefill's kernels (recorded before the decode steps): the causal
+    # attention statistics and column sums (the accumulate), then the top-B
+    # reduction and the load into slots
+    pre = {}
+    for nm, ms in recs:
+        if nm == "h2o_decode":
+            break
+        pre[nm] = pre.get(nm, 0.0) + ms
+    acc_ms = sum(pre.get(k, 0.0) for k in ("attn_partial", "attn_combine_rows", "score_h2o_colsum"))
+    # causal QK^T counted once (the statistics and the column sums each form it)
+    P = cfg.prompt
+    pre_flops = 2 * cfg.d * (P * (P + 1) // 2) * cfg.batch * cfg.heads
+    pre_bytes = 2 * cfg.batch * cfg.heads * P * cfg.d * 2  # Q and K of the prompt, read once
     # the prefill's reduction ends with one compact of the kept prompt rows
     pc = [ms for nm, ms in recs if nm == "compact"]
     k_h, k_r = cache.budget(cfg.prompt)
@@ -228,7 +241,18 @@ def bench_h2o(kv, torch, dev, layers=4):
     dec_ms = sum(dec) / len(dec)
     hbm = step_bytes / (dec_ms * 1e-3) / 1e9
     total = e1b.elapsed_time(e2)
+    pre_tf = pre_flops / (acc_ms * 1e-3) / 1e12 if acc_ms > 0 else 0.0
+    pre_gb = pre_bytes / (acc_ms * 1e-3) / 1e9 if acc_ms > 0 else 0.0
     return {"workload": cfg.name, "prefill_ms": round(e0.elapsed_time(e1), 3),
+            "prefill_kernels_ms": {k: round(v, 4) for k, v in pre.items()},
+            "prefill_roofline": with_measured({
+                "kernel": "attn_partial + score_h2o_colsum (causal prompt accumulate)",
+                "bound": "mfma", "achieved": round(pre_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(pre_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "algorithmic_per_launch": pre_flops, "avg_launch_ms": round(acc_ms, 4),
+                "hbm_gbs_on_q_and_k": round(pre_gb, 1),
+                "note": "the causal QK^T is formed twice (row statistics, then column sums) "
+                        "and credited once"}),
             "decode_layers": layers,
             "decode_ms_total": round(total, 3),
             "decode_step_kernel_ms": round(dec_ms, 4),
@@ -649,8 +673,21 @@ def main():
         ev0.baseline(kind, x["Q"], x["K"], x["V"])
         ev0.select()
         rec[name] = recall(ev0.kept)
+    # retention-order shift (LORE-KV page, "More analyses"): the share of
+    # LORE-KV's kept candidates that its window-only form, and the window
+    # baseline, do not keep (mean over KV heads; layer 0, B = 128)
+    sh = torch.empty(cfg.batch, cfg.h_kv, device=dev)
+    kept_lore = ev.kept.clone()
+    ev0.run(x["Q"], x["K"], x["V"], x["W_O"], x["omega"], Kd, Vd)
+    kv.kvscore_retention_shift(kept_lore, ev0.kept, sh, n=cfg.n, n_sink=cfg.n_sink, w=cfg.w)
+    shift = {"budget": cfg.budget, "lore_vs_window_only": round(float(sh.mean()), 4)}
+    ev0.baseline(kv.KVS_BASELINE_WINDOW, x["Q"], x["K"], x["V"])
+    ev0.select()
+    kv.kvscore_retention_shift(kept_lore, ev0.kept, sh, n=cfg.n, n_sink=cfg.n_sink, w=cfg.w)
+    shift["lore_vs_window_baseline"] = round(float(sh.mean()), 4)
     del ev0
     out["planted_fact_recall"] = rec
+    out["retention_shift"] = shift
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, data)

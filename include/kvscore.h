@@ -301,6 +301,25 @@ kvs_status kvscore_topb_select(const kvs_lore_desc *desc, const float *S, int32_
                                float *pooled, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Retention-order shift between two selections of the same budget (LORE-KV
+ * page, "More analyses", "Retention-order shift"): per row, the share of
+ * selection A's kept candidates -- indices in [n_sink, n - w) -- that
+ * selection B does not keep; the protected tokens, kept by both, are left
+ * out.  0 when A keeps no candidate.  With equal budgets the measure is
+ * symmetric.
+ *
+ *  rows          number of kept lists (e.g. batch * h_kv).
+ *  kept_a, kept_b [rows][n_keep] int32: kvscore_topb_select outputs.  kept_b
+ *                must be ascending (as kvscore_topb_select writes it; an
+ *                unsorted kept_b gives a wrong count, never an invalid read).
+ *  shift         [rows] fp32 out.
+ * Errors: KVS_ERR_INVALID for sizes out of range or NULL pointers.
+ */
+kvs_status kvscore_retention_shift(int32_t rows, int32_t n_keep, int32_t n, int32_t n_sink,
+                                   int32_t w, const int32_t *kept_a, const int32_t *kept_b,
+                                   float *shift, void *stream);
+
+/*
  * kvscore_topb_select without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, outputs and results as

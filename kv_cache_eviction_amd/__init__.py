@@ -12,7 +12,8 @@ from ._lib import (KvsError, LoreDesc, H2ODesc, load, last_error, lore_desc, h2o
                    kvs_fidelity_workspace_bytes, kvscore_output_fidelity,
                    kvscore_counter_causal,
                    kvs_refresh_workspace_bytes, kvscore_refresh,
-                   RELIABILITY_D, kvscore_topb_select, kvscore_topb_select_noalloc, kv_compact,
+                   RELIABILITY_D, kvscore_topb_select, kvscore_topb_select_noalloc, kvscore_retention_shift,
+                   kv_compact,
                    kvs_h2o_workspace_bytes,
                    kvscore_h2o_accumulate, KVS_F32, KVS_BF16, KVS_F16, KVS_H2O_PREFILL,
                    KVS_H2O_DECODE, KVS_BASELINE_WINDOW, KVS_BASELINE_TOVA, DTYPE_CODE, EXPORTS, LIB_PATH, kvs_timing_enable,
@@ -26,7 +27,7 @@ __all__ = ["KvsError", "LoreDesc", "H2ODesc", "load", "last_error", "lore_desc",
            "kvs_fidelity_workspace_bytes", "kvscore_output_fidelity",
            "kvscore_counter_causal",
            "kvs_refresh_workspace_bytes", "kvscore_refresh",
-           "RELIABILITY_D", "KVS_BASELINE_WINDOW", "KVS_BASELINE_TOVA", "kvscore_topb_select", "kvscore_topb_select_noalloc", "kv_compact", "kvs_h2o_workspace_bytes",
+           "RELIABILITY_D", "KVS_BASELINE_WINDOW", "KVS_BASELINE_TOVA", "kvscore_topb_select", "kvscore_topb_select_noalloc", "kvscore_retention_shift", "kv_compact", "kvs_h2o_workspace_bytes",
            "kvscore_h2o_accumulate", "KVS_F32", "KVS_BF16", "KVS_F16", "KVS_H2O_PREFILL",
            "KVS_H2O_DECODE", "DTYPE_CODE", "EXPORTS", "LIB_PATH", "LoreEviction", "H2OCache",
            "kvs_timing_enable", "kvs_timing_reset", "kvs_timing_records", "kvs_measure_peaks"]

@@ -24,7 +24,7 @@ CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
 EXPORTS = ("kvs_lore_workspace_bytes", "kvs_topb_workspace_bytes", "kvscore_probs", "kvscore_deletion",
            "kvscore_baseline_scores", "kvscore_reliability_weights", "kvs_fidelity_workspace_bytes",
            "kvscore_output_fidelity", "kvscore_counter_causal",
-           "kvs_refresh_workspace_bytes", "kvscore_refresh", "kvscore_topb_select", "kvscore_topb_select_noalloc", "kv_compact", "kvs_h2o_workspace_bytes",
+           "kvs_refresh_workspace_bytes", "kvscore_refresh", "kvscore_topb_select", "kvscore_topb_select_noalloc", "kvscore_retention_shift", "kv_compact", "kvs_h2o_workspace_bytes",
            "kvscore_h2o_accumulate", "kvs_measure_peaks", "kvs_timing_enable", "kvs_timing_count", "kvs_timing_read",
            "kvs_timing_reset", "kvs_last_error")
 
@@ -96,6 +96,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvs_topb_workspace_bytes.argtypes = [LP]
     lib.kvscore_topb_select.restype = i32
     lib.kvscore_topb_select.argtypes = [LP, vp, vp, vp, vp, sz, vp]
+    lib.kvscore_retention_shift.restype = i32
+    lib.kvscore_retention_shift.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.kvs_measure_peaks.restype = i32
     lib.kvs_measure_peaks.argtypes = [vp, sz, ctypes.POINTER(ctypes.c_float),
                                       ctypes.POINTER(ctypes.c_float), vp]
@@ -361,6 +363,23 @@ def kvscore_topb_select_noalloc(desc, S, kept, pooled=None, stream=None):
     _check(load().kvscore_topb_select_noalloc(ctypes.byref(desc), _ptr(S), _ptr(kept),
                                               _ptr(pooled), _stream(stream)),
            "kvscore_topb_select_noalloc")
+
+
+def kvscore_retention_shift(kept_a, kept_b, shift, *, n, n_sink, w, stream=None):
+    """Per kept list, the share of kept_a's candidates [n_sink, n - w) absent
+    from kept_b (ascending); kept_a, kept_b [..][n_keep] int32, shift [..] fp32."""
+    if kept_a is None or kept_b is None:
+        raise KvsError("kept_a and kept_b are required")
+    lead, n_keep = tuple(kept_a.shape[:-1]), kept_a.shape[-1]
+    _need(kept_a, "kept_a", lead + (n_keep,), torch.int32)
+    _need(kept_b, "kept_b", lead + (n_keep,), torch.int32)
+    _need(shift, "shift", lead, torch.float32)
+    rows = 1
+    for x in lead:
+        rows *= x
+    _check(load().kvscore_retention_shift(rows, n_keep, int(n), int(n_sink), int(w), _ptr(kept_a),
+                                          _ptr(kept_b), _ptr(shift), _stream(stream)),
+           "kvscore_retention_shift")
 
 
 def kv_compact(K, V, kept, K_out, V_out, pos_out=None, score_in=None, score_out=None,

@@ -472,6 +472,20 @@ KVS_API kvs_status kvscore_topb_select(const kvs_lore_desc *desc, const float *S
   return hip_status(e, "top-B select");
 }
 
+KVS_API kvs_status kvscore_retention_shift(int32_t rows, int32_t n_keep, int32_t n,
+                                          int32_t n_sink, int32_t w, const int32_t *kept_a,
+                                          const int32_t *kept_b, float *shift, void *stream) {
+  if (rows < 1 || n_keep < 1 || n < 1)
+    return fail(KVS_ERR_INVALID, "kvscore_retention_shift: rows, n_keep and n must be >= 1");
+  if (n_sink < 0 || w < 0 || (long)n_sink + w > n || n_keep > n)
+    return fail(KVS_ERR_INVALID, "kvscore_retention_shift: need n_sink, w >= 0, n_sink + w <= n, n_keep <= n");
+  if (!kept_a || !kept_b || !shift)
+    return fail(KVS_ERR_INVALID, "kvscore_retention_shift: a required pointer is NULL");
+  const hipError_t e = kvs::launch_retention_shift(rows, n_keep, n_sink, w, n, kept_a, kept_b,
+                                                   shift, static_cast<hipStream_t>(stream));
+  return hip_status(e, "retention shift");
+}
+
 static_assert(kvs::kTopbScratchBytes == KVS_TOPB_NOALLOC_MAX_BYTES,
               "the header states the library's scratch size");
 

@@ -86,6 +86,10 @@ hipError_t launch_score(int etype, int d, int mode, const void *Q, const void *K
 
 // Selection and compaction.
 size_t topb_workspace_bytes(int rows, int n, int chunk);
+// Retention-order shift between two ascending kept lists per row.
+hipError_t launch_retention_shift(int rows, int n_keep, int n_sink, int w, int n,
+                                  const int32_t *kept_a, const int32_t *kept_b, float *shift,
+                                  hipStream_t st);
 // The library-owned scratch of the allocation-free selection: its size, and
 // its device address on the current device (looked up once per device).
 constexpr size_t kTopbScratchBytes = (size_t)32 << 20;

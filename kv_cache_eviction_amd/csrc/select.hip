@@ -372,6 +372,49 @@ hipError_t launch_topb(const float *S, int rows, int n, int n_sink, int w, int c
   return hipGetLastError();
 }
 
+// Retention-order shift (LORE-KV page, "More analyses"): per row, the
+// candidates [n_sink, n - w) that kept list A holds and kept list B does
+// not, as a fraction of A's candidates (0 when A has none).  One workgroup
+// per row; B is ascending (as kvscore_topb_select writes it), so each of A's
+// candidates is looked up by a binary search over B (bounded by n_keep
+// steps whatever B holds).
+__global__ void __launch_bounds__(256)
+retention_shift_kernel(const int32_t *__restrict__ ka, const int32_t *__restrict__ kb,
+                       int n_keep, int n_sink, int w, int n, float *__restrict__ shift) {
+  __shared__ int scan_sh[5];
+  const long row = blockIdx.x;
+  const int32_t *a = ka + row * n_keep;
+  const int32_t *b = kb + row * n_keep;
+  int miss = 0, cnt = 0;
+  for (int i = threadIdx.x; i < n_keep; i += blockDim.x) {
+    const int x = a[i];
+    if (x < n_sink || x >= n - w) continue;
+    ++cnt;
+    int lo = 0, hi = n_keep;  // first position of B holding a value >= x
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (b[mid] < x) lo = mid + 1;
+      else hi = mid;
+    }
+    miss += (lo < n_keep && b[lo] == x) ? 0 : 1;
+  }
+  int miss_total, cnt_total;
+  block_exclusive_scan(miss, scan_sh, &miss_total);
+  block_exclusive_scan(cnt, scan_sh, &cnt_total);
+  if (threadIdx.x == 0) shift[row] = cnt_total > 0 ? (float)miss_total / (float)cnt_total : 0.f;
+}
+
+hipError_t launch_retention_shift(int rows, int n_keep, int n_sink, int w, int n,
+                                  const int32_t *kept_a, const int32_t *kept_b, float *shift,
+                                  hipStream_t st) {
+  {
+    TimedLaunch tl_("retention_shift", st);
+    hipLaunchKernelGGL(retention_shift_kernel, dim3(rows), dim3(256), 0, st, kept_a, kept_b,
+                       n_keep, n_sink, w, n, shift);
+  }
+  return hipGetLastError();
+}
+
 // Scratch of the allocation-free selection (kvscore_topb_select_noalloc): the
 // level-1 chunk keys, candidate lists and counts that kvscore_topb_select
 // otherwise takes from the caller's workspace.  A file-scope device array, so

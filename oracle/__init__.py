@@ -35,7 +35,9 @@ query head, standardized over the trajectories (zero below a spread of 1e-6); ou
 fidelity is the mean cosine between per-head attention outputs over the full
 and the retained cache; the memory refresh keeps its survivors in position
 order, protects the system prompt and the last token, and breaks ties toward
-the lower position.
+the lower position; the retention-order shift is the share of one
+selection's kept candidates (protected tokens left out) that the other
+selection does not keep.
 
 Every function here is pinned by tests to what the pages and the mathematics
 fix (worked examples, closed forms, invariants, brute force on tiny inputs).
@@ -416,6 +418,27 @@ def topb_select(S, *, n_sink, w, chunk, budget):
         out.append(np.sort(np.concatenate([protected, chosen])))
     kept = np.stack(out).reshape(S.shape[:-1] + (len(out[0]),))
     return kept.astype(np.int64), P
+
+
+def retention_shift(kept_a, kept_b, *, n_sink, w, n):
+    """Share of the retained candidates that change between two selections.
+
+    LORE-KV page, "More analyses", "Retention-order shift" (about 20% of the
+    retained tokens change at B = 128).  Reading: for each KV head, the
+    candidates [n_sink, n - w) that selection A keeps and selection B does
+    not, as a fraction of A's kept candidates; the protected tokens are kept
+    by both and are left out.  With equal budgets the measure is symmetric.
+    kept_a, kept_b [..][n_keep] (any order); returns [..] fp64 (0 when A keeps
+    no candidate).
+    """
+    a = np.asarray(kept_a).reshape(-1, np.asarray(kept_a).shape[-1])
+    b = np.asarray(kept_b).reshape(-1, np.asarray(kept_b).shape[-1])
+    out = np.empty(a.shape[0])
+    for row in range(a.shape[0]):
+        ca = {int(i) for i in a[row] if n_sink <= i < n - w}
+        cb = {int(i) for i in b[row] if n_sink <= i < n - w}
+        out[row] = len(ca - cb) / len(ca) if ca else 0.0
+    return out.reshape(np.asarray(kept_a).shape[:-1])
 
 
 def compact(K, V, kept):

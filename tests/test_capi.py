@@ -175,8 +175,12 @@ def test_selection_descriptor_needs_only_selection_fields():
 
 def test_h2o_descriptor_checks():
     kv, lib = _lib()
-    d = kv.h2o_desc(batch=2, heads=3, d=128, cap=1025)
+    d = kv.h2o_desc(batch=2, heads=3, d=128, cap=16385)      # prompt above 16384
     assert lib.kvs_h2o_workspace_bytes(ctypes.byref(d), kv.KVS_H2O_PREFILL) == 0
+    d = kv.h2o_desc(batch=1, heads=1100, d=128, cap=16384)   # grid: 1100 * 64 workgroups
+    assert lib.kvs_h2o_workspace_bytes(ctypes.byref(d), kv.KVS_H2O_PREFILL) == 0
+    d = kv.h2o_desc(batch=2, heads=3, d=128, cap=16384)
+    assert lib.kvs_h2o_workspace_bytes(ctypes.byref(d), kv.KVS_H2O_PREFILL) > 0
     d = kv.h2o_desc(batch=2, heads=3, d=128, cap=1024)
     assert lib.kvs_h2o_workspace_bytes(ctypes.byref(d), kv.KVS_H2O_PREFILL) > 0
     rc = lib.kvscore_h2o_accumulate(ctypes.byref(d), 7, None, None, None, None, None, None,
@@ -194,3 +198,17 @@ def test_binding_checks_shapes_before_calling():
     d = _desc(kv)
     with pytest.raises(kv.KvsError):
         kv.kvscore_probs(d, torch.zeros(1), None, None, None, None, None, None)
+
+
+def test_retention_shift_and_noalloc_host_checks():
+    """Bad sizes and NULL pointers are refused on the host (no device touched)."""
+    kv, lib = _lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: a host check fails first
+    assert lib.kvscore_retention_shift(0, 5, 10, 1, 2, fake, fake, fake, None) == 1
+    assert lib.kvscore_retention_shift(2, 11, 10, 1, 2, fake, fake, fake, None) == 1   # n_keep > n
+    assert lib.kvscore_retention_shift(2, 5, 10, 6, 5, fake, fake, fake, None) == 1    # n_sink + w > n
+    assert lib.kvscore_retention_shift(2, 5, 10, 1, 2, None, fake, fake, None) == 1
+    d = kv.lore_desc(batch=64, n=1 << 20, h_q=8, h_kv=8, d=128, d_model=1, w=32, m=0, t=0,
+                     n_sink=1, chunk=1, budget=128)
+    assert lib.kvscore_topb_select_noalloc(ctypes.byref(d), fake, fake, None, None) == 2
+    assert "maximum" in kv.last_error()

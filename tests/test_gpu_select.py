@@ -101,3 +101,28 @@ def test_quantized_scores_many_ties(dev):
     kept = run_select(dev, S, 4, 32, 4, 2000)
     o, _ = oracle.topb_select(S.double().numpy(), n_sink=4, w=32, chunk=4, budget=2000)
     assert np.array_equal(kept, o)
+
+
+@pytest.mark.parametrize("budget", [128, 0, 5000])
+def test_retention_shift_matches_oracle(dev, budget):
+    """The retention-order shift between two GPU selections over correlated
+    scores (a perturbed copy), against the oracle's count on the same kept
+    lists: an exact ratio of integers, so the fp32 result is the correctly
+    rounded fp64 one.  budget 0 keeps no candidate (shift 0); 5000 keeps
+    every candidate of both (shift 0)."""
+    g = torch.Generator().manual_seed(75 + budget)
+    n, n_sink, w = 4099, 1, 32
+    S1 = torch.rand(2, 3, n, generator=g)
+    S2 = S1 + 0.3 * torch.rand(2, 3, n, generator=g)
+    k1 = run_select(dev, S1, n_sink, w, 4, budget)
+    k2 = run_select(dev, S2, n_sink, w, 4, budget)
+    shift = torch.empty(2, 3, device=dev)
+    kv.kvscore_retention_shift(torch.from_numpy(k1).to(dev), torch.from_numpy(k2).to(dev), shift,
+                               n=n, n_sink=n_sink, w=w)
+    torch.cuda.synchronize()
+    ref = oracle.retention_shift(k1, k2, n_sink=n_sink, w=w, n=n)
+    assert np.array_equal(shift.cpu().numpy(), ref.astype(np.float32))
+    if budget in (0, 5000):
+        assert np.all(ref == 0)
+    else:
+        assert np.all(ref > 0)

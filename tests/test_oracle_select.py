@@ -67,3 +67,32 @@ def test_compact_is_exact_gather():
             for r in range(11):
                 assert np.array_equal(Kc[b, g, r], K[b, g, kept[b, g, r]])
                 assert np.array_equal(Vc[b, g, r], V[b, g, kept[b, g, r]])
+
+
+def test_retention_shift_golden():
+    """Hand-worked retention-order shifts (tests/golden/retention_shift_n16.json)."""
+    from conftest import golden
+    g = golden("retention_shift_n16.json")
+    got = oracle.retention_shift(np.array(g["kept_a"]), np.array(g["kept_b"]), n_sink=g["n_sink"],
+                                 w=g["w"], n=g["n"])
+    assert np.array_equal(got, np.array(g["expected_shift"]))
+
+
+def test_retention_shift_properties():
+    """Symmetric at equal budgets, zero against itself, blind to the protected
+    tokens and to list order; a one-swap change moves it by 1/B."""
+    rng = np.random.default_rng(7)
+    n, n_sink, w, B = 500, 2, 16, 40
+    cand = np.arange(n_sink, n - w)
+    prot = np.concatenate([np.arange(n_sink), np.arange(n - w, n)])
+    a = np.stack([np.sort(np.concatenate([prot, rng.choice(cand, B, replace=False)])) for _ in range(6)])
+    b = np.stack([np.sort(np.concatenate([prot, rng.choice(cand, B, replace=False)])) for _ in range(6)])
+    s_ab = oracle.retention_shift(a, b, n_sink=n_sink, w=w, n=n)
+    assert np.allclose(s_ab, oracle.retention_shift(b, a, n_sink=n_sink, w=w, n=n))
+    assert np.all(oracle.retention_shift(a, a, n_sink=n_sink, w=w, n=n) == 0)
+    assert np.allclose(s_ab, oracle.retention_shift(a[:, ::-1], b, n_sink=n_sink, w=w, n=n))
+    c = a.copy()
+    row_cand = [i for i in range(c.shape[1]) if n_sink <= c[0, i] < n - w]
+    free = np.setdiff1d(cand, c[0])
+    c[0, row_cand[0]] = free[0]
+    assert oracle.retention_shift(a[:1], c[:1], n_sink=n_sink, w=w, n=n)[0] == 1.0 / B
