@@ -99,19 +99,35 @@ typedef struct {
  * serve all of them in turn on one stream. */
 size_t kvs_lore_workspace_bytes(const kvs_lore_desc *desc);
 
+/* Visibility of the cached tokens to the query rows. */
+typedef enum {
+  KVS_MASK_NONE = 0,           /* every row sees all n tokens */
+  KVS_MASK_WINDOW_CAUSAL = 1,  /* LORE-KV scoring rows: window row r < w sees tokens
+                                  0..n-w+r (causal at its own position), lookahead rows all n */
+  KVS_MASK_CAUSAL = 2,         /* prompt row r sees 0..r (H2O prefill: KVS_H2O_PREFILL) */
+  KVS_MASK_SLOTS = 3           /* the occupied slots of a slot cache (H2O decode: KVS_H2O_DECODE) */
+} kvs_mask;
+
 /*
  * Pass 1: softmax statistics and attention outputs of the scoring rows.
  * (LORE-KV Method: a_{q,i} and o_q of Eq. 5.)
  *
+ *  mask     KVS_MASK_WINDOW_CAUSAL (the LORE-KV scoring rows; the statistics
+ *           kvscore_deletion needs) or KVS_MASK_NONE (every row sees every
+ *           token, e.g. held-out queries).  The causal and slot masks are
+ *           the H2O modes of kvscore_h2o_accumulate: KVS_ERR_UNSUPPORTED here.
  *  Q        [batch][h_q][n_q][d]      scoring queries (window rows first).
  *  K, V     [batch][h_kv][n][d]       the cache.
  *  row_max  [batch][h_q][n_q] fp32    out: max_i q.k_i / sqrt(d) over visible i.
  *  row_sum  [batch][h_q][n_q] fp32    out: sum_i exp(q.k_i/sqrt(d) - row_max).
  *  O        [batch][h_q][n_q][d] fp32 out: o_q = sum_i a_{q,i} v_i.
  *  ws, ws_bytes                       workspace (>= kvs_lore_workspace_bytes).
+ * The dense probability matrix a [n_q][n] is not an output: the path never
+ * forms it (the score pass recomputes each probability from q.k and the row
+ * statistics), and at the 128K workload it would be 1 GiB per layer.
  */
-kvs_status kvscore_probs(const kvs_lore_desc *desc, const void *Q, const void *K, const void *V,
-                         float *row_max, float *row_sum, float *O,
+kvs_status kvscore_probs(const kvs_lore_desc *desc, int32_t mask, const void *Q, const void *K,
+                         const void *V, float *row_max, float *row_sum, float *O,
                          void *ws, size_t ws_bytes, void *stream);
 
 /*
@@ -130,7 +146,9 @@ kvs_status kvscore_probs(const kvs_lore_desc *desc, const void *Q, const void *K
  *           For omega_j < 0 this differs from Eq. 7 read literally (which
  *           would subtract that trajectory's term); no error is raised, since
  *           omega lives in device memory and is not read on the host.
- *  row_max, row_sum, O      kvscore_probs outputs for the same inputs.
+ *  row_max, row_sum, O      kvscore_probs outputs for the same inputs, under
+ *                           KVS_MASK_WINDOW_CAUSAL (the score recomputes the
+ *                           probabilities with that mask).
  *  S        [batch][h_kv][n] fp32 out: the KV head's score of every token
  *           (protected tokens are scored too; selection ignores them).
  *
@@ -362,7 +380,8 @@ kvs_status kv_compact(int32_t batch, int32_t heads, int32_t n_src, int32_t n_kee
                       void *K_out, void *V_out, int32_t *pos_out,
                       const float *score_in, float *score_out, void *stream);
 
-/* H2O modes. */
+/* H2O modes: the mode fixes the mask (prefill: KVS_MASK_CAUSAL over the
+ * prompt; decode: KVS_MASK_SLOTS over the occupied slots plus the new token). */
 typedef enum {
   KVS_H2O_PREFILL = 0, /* accumulated attention of a causal prompt */
   KVS_H2O_DECODE = 1   /* one decode step on the slot cache */
@@ -398,20 +417,26 @@ typedef struct {
  * KVS_H2O_PREFILL:
  *   q, K    [batch][heads][cap][d]  prompt queries and keys (row r attends to keys 0..r).
  *   acc     [batch][heads][cap] fp32 out: acc_i = sum_{r >= i} a_{r,i}.
- *   V, k_new, v_new, slot_pos, O, evict_slot: unused (may be NULL).
+ *   V, k_new, v_new, write_slot, slot_pos, O, evict_slot: unused (may be NULL).
  *   ws, ws_bytes: workspace of at least kvs_h2o_workspace_bytes(desc, mode).
  *
  * KVS_H2O_DECODE (one step; rows independent):
  *   q, k_new, v_new [batch][heads][d]   this step's query, key and value.
- *   K, V            [batch][heads][cap][d]  slot cache, in/out (the new token is
- *                   written into the lowest-index free slot).
+ *   K, V            [batch][heads][cap][d]  slot cache, in/out: the new token is
+ *                   written into slot write_slot[row], or, with write_slot NULL,
+ *                   into the lowest-index free slot.
+ *   write_slot      [batch][heads] int32, nullable: the slot each row's new token
+ *                   goes into; it must be free (slot_pos -1) and in [0, cap).  A
+ *                   row whose write_slot is occupied or out of range is left
+ *                   unchanged and reports evict_slot -2 (checked on the device).
  *   slot_pos        [batch][heads][cap] int32, in/out: position held by each slot,
  *                   -1 = free.  At least one slot must be free on entry.
  *   acc             [batch][heads][cap] fp32, in/out: accumulated attention per slot.
  *   O               [batch][heads][d] (dtype), nullable: out, attention output.
  *   evict_slot      [batch][heads] int32, nullable: out, slot evicted this step
  *                   (its slot_pos becomes -1) or -1 if the row is within
- *                   budget; -2 if the row had no free slot (nothing changed).
+ *                   budget; -2 if the row had no free slot, or its write_slot
+ *                   was not a free slot in range (nothing changed).
  *   ws, ws_bytes: unused.
  */
 size_t kvs_h2o_workspace_bytes(const kvs_h2o_desc *desc, int32_t mode);
@@ -419,7 +444,8 @@ size_t kvs_h2o_workspace_bytes(const kvs_h2o_desc *desc, int32_t mode);
 kvs_status kvscore_h2o_accumulate(const kvs_h2o_desc *desc, int32_t mode,
                                   const void *q, void *K, void *V,
                                   const void *k_new, const void *v_new,
-                                  int32_t *slot_pos, float *acc, void *O, int32_t *evict_slot,
+                                  const int32_t *write_slot, int32_t *slot_pos, float *acc,
+                                  void *O, int32_t *evict_slot,
                                   void *ws, size_t ws_bytes, void *stream);
 
 /*

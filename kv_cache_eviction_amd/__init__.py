@@ -16,7 +16,8 @@ from ._lib import (KvsError, LoreDesc, H2ODesc, load, last_error, lore_desc, h2o
                    kv_compact,
                    kvs_h2o_workspace_bytes,
                    kvscore_h2o_accumulate, KVS_F32, KVS_BF16, KVS_F16, KVS_H2O_PREFILL,
-                   KVS_H2O_DECODE, KVS_BASELINE_WINDOW, KVS_BASELINE_TOVA, DTYPE_CODE, EXPORTS, LIB_PATH, kvs_timing_enable,
+                   KVS_H2O_DECODE, KVS_BASELINE_WINDOW, KVS_BASELINE_TOVA, KVS_MASK_NONE,
+                   KVS_MASK_WINDOW_CAUSAL, KVS_MASK_CAUSAL, KVS_MASK_SLOTS, DTYPE_CODE, EXPORTS, LIB_PATH, kvs_timing_enable,
                    kvs_measure_peaks,
                    kvs_timing_reset, kvs_timing_records)
 from .evict import LoreEviction, H2OCache
@@ -29,5 +30,6 @@ __all__ = ["KvsError", "LoreDesc", "H2ODesc", "load", "last_error", "lore_desc",
            "kvs_refresh_workspace_bytes", "kvscore_refresh",
            "RELIABILITY_D", "KVS_BASELINE_WINDOW", "KVS_BASELINE_TOVA", "kvscore_topb_select", "kvscore_topb_select_noalloc", "kvscore_retention_shift", "kv_compact", "kvs_h2o_workspace_bytes",
            "kvscore_h2o_accumulate", "KVS_F32", "KVS_BF16", "KVS_F16", "KVS_H2O_PREFILL",
-           "KVS_H2O_DECODE", "DTYPE_CODE", "EXPORTS", "LIB_PATH", "LoreEviction", "H2OCache",
+           "KVS_H2O_DECODE", "KVS_MASK_NONE", "KVS_MASK_WINDOW_CAUSAL", "KVS_MASK_CAUSAL",
+           "KVS_MASK_SLOTS", "DTYPE_CODE", "EXPORTS", "LIB_PATH", "LoreEviction", "H2OCache",
            "kvs_timing_enable", "kvs_timing_reset", "kvs_timing_records", "kvs_measure_peaks"]

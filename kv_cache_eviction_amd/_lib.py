@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libkvscore.so")
 KVS_F32, KVS_BF16, KVS_F16 = 0, 1, 2
 KVS_H2O_PREFILL, KVS_H2O_DECODE = 0, 1
 KVS_BASELINE_WINDOW, KVS_BASELINE_TOVA = 0, 1
+KVS_MASK_NONE, KVS_MASK_WINDOW_CAUSAL, KVS_MASK_CAUSAL, KVS_MASK_SLOTS = 0, 1, 2, 3
 DTYPE_CODE = {torch.float32: KVS_F32, torch.bfloat16: KVS_BF16, torch.float16: KVS_F16}
 CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
 
@@ -73,7 +74,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvs_lore_workspace_bytes.restype = sz
     lib.kvs_lore_workspace_bytes.argtypes = [LP]
     lib.kvscore_probs.restype = i32
-    lib.kvscore_probs.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kvscore_probs.argtypes = [LP, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kvscore_deletion.restype = i32
     lib.kvscore_deletion.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kvscore_baseline_scores.restype = i32
@@ -108,7 +109,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvs_h2o_workspace_bytes.restype = sz
     lib.kvs_h2o_workspace_bytes.argtypes = [HP, i32]
     lib.kvscore_h2o_accumulate.restype = i32
-    lib.kvscore_h2o_accumulate.argtypes = [HP, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kvscore_h2o_accumulate.argtypes = [HP, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                           vp]
     lib.kvs_timing_enable.restype = i32
     lib.kvs_timing_enable.argtypes = [i32]
     lib.kvs_timing_count.restype = i32
@@ -178,7 +180,8 @@ def _ws_check(ws, need):
         raise KvsError("workspace must be a device tensor of at least %d bytes" % need)
 
 
-def kvscore_probs(desc, Q, K, V, row_max, row_sum, O, ws, stream=None):
+def kvscore_probs(desc, Q, K, V, row_max, row_sum, O, ws, stream=None,
+                  mask=KVS_MASK_WINDOW_CAUSAL):
     dt = CODE_DTYPE[desc.dtype]
     b, hq, hk, n, d, nq = desc.batch, desc.h_q, desc.h_kv, desc.n, desc.d, desc.n_q
     _need(Q, "Q", (b, hq, nq, d), dt)
@@ -189,7 +192,7 @@ def kvscore_probs(desc, Q, K, V, row_max, row_sum, O, ws, stream=None):
     _need(O, "O", (b, hq, nq, d), torch.float32)
     need = kvs_lore_workspace_bytes(desc)
     _ws_check(ws, need)
-    _check(load().kvscore_probs(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), _ptr(row_max),
+    _check(load().kvscore_probs(ctypes.byref(desc), int(mask), _ptr(Q), _ptr(K), _ptr(V), _ptr(row_max),
                                 _ptr(row_sum), _ptr(O), _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream(stream)), "kvscore_probs")
 
@@ -414,7 +417,8 @@ def kvs_h2o_workspace_bytes(desc: H2ODesc, mode: int) -> int:
 
 
 def kvscore_h2o_accumulate(desc, mode, q, K, V=None, k_new=None, v_new=None, slot_pos=None,
-                           acc=None, O=None, evict_slot=None, ws=None, stream=None):
+                           acc=None, O=None, evict_slot=None, ws=None, stream=None,
+                           write_slot=None):
     dt = CODE_DTYPE[desc.dtype]
     b, h, d, cap = desc.batch, desc.heads, desc.d, desc.cap
     if mode == KVS_H2O_PREFILL:
@@ -436,11 +440,13 @@ def kvscore_h2o_accumulate(desc, mode, q, K, V=None, k_new=None, v_new=None, slo
         _need(acc, "acc", (b, h, cap), torch.float32)
         _need(O, "O", (b, h, d), dt, optional=True)
         _need(evict_slot, "evict_slot", (b, h), torch.int32, optional=True)
+        _need(write_slot, "write_slot", (b, h), torch.int32, optional=True)
         nb = 0
     else:
         raise KvsError("unknown H2O mode %r" % (mode,))
     _check(load().kvscore_h2o_accumulate(ctypes.byref(desc), mode, _ptr(q), _ptr(K), _ptr(V),
-                                         _ptr(k_new), _ptr(v_new), _ptr(slot_pos), _ptr(acc),
+                                         _ptr(k_new), _ptr(v_new), _ptr(write_slot),
+                                         _ptr(slot_pos), _ptr(acc),
                                          _ptr(O), _ptr(evict_slot), _ptr(ws), nb, _stream(stream)),
            "kvscore_h2o_accumulate")
 

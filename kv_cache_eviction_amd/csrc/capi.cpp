@@ -162,11 +162,16 @@ KVS_API size_t kvs_lore_workspace_bytes(const kvs_lore_desc *desc) {
   return m;
 }
 
-KVS_API kvs_status kvscore_probs(const kvs_lore_desc *desc, const void *Q, const void *K,
-                                 const void *V, float *row_max, float *row_sum, float *O,
-                                 void *ws, size_t ws_bytes, void *stream) {
+KVS_API kvs_status kvscore_probs(const kvs_lore_desc *desc, int32_t mask, const void *Q,
+                                 const void *K, const void *V, float *row_max, float *row_sum,
+                                 float *O, void *ws, size_t ws_bytes, void *stream) {
   kvs_status st = check_lore(desc);
   if (st != KVS_OK) return st;
+  if (mask == KVS_MASK_CAUSAL || mask == KVS_MASK_SLOTS)
+    return fail(KVS_ERR_UNSUPPORTED, "kvscore_probs: the causal and slot masks are the H2O modes "
+                                     "of kvscore_h2o_accumulate");
+  if (mask != KVS_MASK_NONE && mask != KVS_MASK_WINDOW_CAUSAL)
+    return fail(KVS_ERR_INVALID, "kvscore_probs: unknown mask");
   if (!Q || !K || !V || !row_max || !row_sum || !O)
     return fail(KVS_ERR_INVALID, "kvscore_probs: a required pointer is NULL");
   st = check_aligned("kvscore_probs", {Q, K, V, O});
@@ -175,7 +180,8 @@ KVS_API kvs_status kvscore_probs(const kvs_lore_desc *desc, const void *Q, const
   st = check_ws(ws, ws_bytes, p.probs_bytes);
   if (st != KVS_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const kvs::RowGeom geo = lore_geom(desc);
+  kvs::RowGeom geo = lore_geom(desc);
+  if (mask == KVS_MASK_NONE) geo.w = 0;  // no row is causal: every row sees all n tokens
   float *pm = at<float>(ws, p.off_pm), *pl = at<float>(ws, p.off_pl), *po = at<float>(ws, p.off_po);
   hipError_t e = kvs::launch_attn_partial(desc->dtype, desc->d, true, Q, K, V, geo, desc->batch,
                                           desc->h_kv, p.split, pm, pl, po, s);
@@ -597,8 +603,9 @@ KVS_API size_t kvs_h2o_workspace_bytes(const kvs_h2o_desc *desc, int32_t mode) {
 
 KVS_API kvs_status kvscore_h2o_accumulate(const kvs_h2o_desc *desc, int32_t mode, const void *q,
                                           void *K, void *V, const void *k_new,
-                                          const void *v_new, int32_t *slot_pos, float *acc,
-                                          void *O, int32_t *evict_slot, void *ws, size_t ws_bytes,
+                                          const void *v_new, const int32_t *write_slot,
+                                          int32_t *slot_pos, float *acc, void *O,
+                                          int32_t *evict_slot, void *ws, size_t ws_bytes,
                                           void *stream) {
   kvs_status st = check_h2o(desc, mode);
   if (st != KVS_OK) return st;
@@ -629,7 +636,7 @@ KVS_API kvs_status kvscore_h2o_accumulate(const kvs_h2o_desc *desc, int32_t mode
   if (st != KVS_OK) return st;
   hipError_t e = kvs::launch_h2o_decode(desc->dtype, desc->d, desc->batch * desc->heads, desc->cap,
                                         desc->cur_len, desc->k_heavy, desc->k_recent, q, K, V,
-                                        k_new, v_new,
+                                        k_new, v_new, write_slot,
                                         slot_pos, acc, O, evict_slot, s);
   return hip_status(e, "decode step");
 }

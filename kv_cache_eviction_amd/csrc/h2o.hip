@@ -98,6 +98,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256)
 h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
                   const T *__restrict__ k_new, const T *__restrict__ v_new,
+                  const int32_t *__restrict__ write_slot,
                   int32_t *__restrict__ slot_pos, float *__restrict__ acc, T *__restrict__ O,
                   int32_t *__restrict__ evict_slot, int rows, int cap, int cur_len, int k_heavy,
                   int k_recent, float c) {
@@ -157,11 +158,16 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
       if (ws < 0 && fb) ws = base + 64 * u + __ffsll((long long)fb) - 1;
     }
   }
+  wave_lds_sync();
+  if (write_slot) {
+    // the caller's slot: used only if it is in range and free
+    const int w = write_slot[row];
+    ws = (w >= 0 && w < cap && pos_s[w] < 0) ? w : -1;
+  }
   if (ws < 0) {
     if (lane == 0 && evict_slot) evict_slot[row] = -2;
     return;
   }
-  wave_lds_sync();
 
   // the query unpacked (unused for fp16, whose FMAs read the packed chunk)
   float qv[EPC];
@@ -295,8 +301,8 @@ static inline int decode_waves_per_block(int cap) { return 3 * 4 * cap * 4 <= 65
 template <typename T, int D>
 static hipError_t run_decode(int rows, int cap, int cur_len, int k_heavy, int k_recent,
                              const void *q, void *K, void *V, const void *k_new,
-                             const void *v_new, int32_t *slot_pos, float *acc, void *O,
-                             int32_t *evict_slot, hipStream_t st) {
+                             const void *v_new, const int32_t *write_slot, int32_t *slot_pos,
+                             float *acc, void *O, int32_t *evict_slot, hipStream_t st) {
   const float c = kLog2e / sqrtf((float)D);
   const int wpb = decode_waves_per_block(cap);
   // probabilities, accumulators and slot map per wave
@@ -304,19 +310,19 @@ static hipError_t run_decode(int rows, int cap, int cur_len, int k_heavy, int k_
   {
     TimedLaunch tl_("h2o_decode", st);
     hipLaunchKernelGGL((h2o_decode_kernel<T, D>), dim3((rows + wpb - 1) / wpb), dim3(64 * wpb), shm, st,
-                       (const T *)q, (T *)K, (T *)V, (const T *)k_new, (const T *)v_new, slot_pos,
-                       acc, (T *)O, evict_slot, rows, cap, cur_len, k_heavy, k_recent, c);
+                       (const T *)q, (T *)K, (T *)V, (const T *)k_new, (const T *)v_new, write_slot,
+                       slot_pos, acc, (T *)O, evict_slot, rows, cap, cur_len, k_heavy, k_recent, c);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_h2o_decode(int etype, int d, int rows, int cap, int cur_len, int k_heavy,
                              int k_recent, const void *q, void *K, void *V, const void *k_new,
-                             const void *v_new, int32_t *slot_pos, float *acc, void *O,
-                             int32_t *evict_slot, hipStream_t st) {
+                             const void *v_new, const int32_t *write_slot, int32_t *slot_pos,
+                             float *acc, void *O, int32_t *evict_slot, hipStream_t st) {
 #define KVS_D(T, DD)                                                                          \
   return run_decode<T, DD>(rows, cap, cur_len, k_heavy, k_recent, q, K, V, k_new, v_new,     \
-                           slot_pos, acc, O, evict_slot, st)
+                           write_slot, slot_pos, acc, O, evict_slot, st)
   if (etype == E_F32) { if (d == 64) KVS_D(float, 64); KVS_D(float, 128); }
   if (etype == E_BF16) { if (d == 64) KVS_D(bf16, 64); KVS_D(bf16, 128); }
   if (d == 64) KVS_D(f16, 64);

@@ -109,9 +109,11 @@ hipError_t measure_peaks(void *buf, size_t bytes, float *mfma_tflops, float *rea
                          hipStream_t st);
 
 // H2O decode step.
+// write_slot (nullable): the slot each row's new token goes into (else the
+// lowest free one).
 hipError_t launch_h2o_decode(int etype, int d, int rows, int cap, int cur_len, int k_heavy,
                              int k_recent, const void *q, void *K, void *V, const void *k_new,
-                             const void *v_new, int32_t *slot_pos, float *acc, void *O,
-                             int32_t *evict_slot, hipStream_t st);
+                             const void *v_new, const int32_t *write_slot, int32_t *slot_pos,
+                             float *acc, void *O, int32_t *evict_slot, hipStream_t st);
 
 }  // namespace kvs

@@ -112,13 +112,15 @@ class H2OCache:
                      self.acc, stream)
         self.cur_len = P
 
-    def step(self, q, k, v, stream=None, with_output=True):
-        """One decode step: append, attend, accumulate, evict at most one."""
+    def step(self, q, k, v, stream=None, with_output=True, write_slot=None):
+        """One decode step: append, attend, accumulate, evict at most one.
+        write_slot [batch][heads] int32 (optional): the free slot each row's new
+        token goes into (else the lowest free slot)."""
         self.cur_len += 1
         k_h, k_r = self.budget(self.cur_len)
         desc = L.h2o_desc(batch=self.batch, heads=self.heads, d=self.d, cap=self.cap,
                           cur_len=self.cur_len, k_heavy=k_h, k_recent=k_r, dtype=self.dtype)
         L.kvscore_h2o_accumulate(desc, L.KVS_H2O_DECODE, q, self.K, self.V, k, v, self.slot_pos,
                                  self.acc, self.O if with_output else None, self.evict_slot,
-                                 stream=stream)
+                                 stream=stream, write_slot=write_slot)
         return self.O, self.evict_slot

@@ -62,7 +62,7 @@ def test_bad_descriptor_rejected_before_launch(kw, status):
     kv, lib = _lib()
     d = _desc(kv, **kw)
     assert lib.kvs_lore_workspace_bytes(ctypes.byref(d)) == 0
-    rc = lib.kvscore_probs(ctypes.byref(d), None, None, None, None, None, None, None, 0, None)
+    rc = lib.kvscore_probs(ctypes.byref(d), 1, None, None, None, None, None, None, None, 0, None)
     assert rc == status, kv.last_error()
     assert kv.last_error()
 
@@ -72,10 +72,10 @@ def test_null_pointers_and_workspace():
     d = _desc(kv)
     need = lib.kvs_lore_workspace_bytes(ctypes.byref(d))
     assert need > 0
-    assert lib.kvscore_probs(ctypes.byref(d), None, None, None, None, None, None, None, 0,
+    assert lib.kvscore_probs(ctypes.byref(d), 1, None, None, None, None, None, None, None, 0,
                              None) == 1
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: a host check fails first
-    rc = lib.kvscore_probs(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, 16, None)
+    rc = lib.kvscore_probs(ctypes.byref(d), 1, fake, fake, fake, fake, fake, fake, fake, 16, None)
     assert rc == 3 and "workspace" in kv.last_error()
     rc = lib.kvscore_deletion(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake, fake,
                               fake, fake, 16, None)
@@ -109,7 +109,7 @@ def test_reliability_weights_host_checks():
     rc = lib.kvscore_reliability_weights(ctypes.byref(d), odd, fake, fake, f(1), f(1), f(0.3),
                                          fake, None, fake, big, None)
     assert rc == 1 and "aligned" in kv.last_error()
-    rc = lib.kvscore_probs(ctypes.byref(d), fake, odd, fake, fake, fake, fake, fake, big, None)
+    rc = lib.kvscore_probs(ctypes.byref(d), 1, fake, odd, fake, fake, fake, fake, fake, big, None)
     assert rc == 1 and "aligned" in kv.last_error()
     assert lib.kv_compact(1, 1, 10, 5, 5, 128, 1, fake, fake, fake, odd, fake, None, None,
                           None, None) == 1
@@ -184,11 +184,11 @@ def test_h2o_descriptor_checks():
     d = kv.h2o_desc(batch=2, heads=3, d=128, cap=1024)
     assert lib.kvs_h2o_workspace_bytes(ctypes.byref(d), kv.KVS_H2O_PREFILL) > 0
     rc = lib.kvscore_h2o_accumulate(ctypes.byref(d), 7, None, None, None, None, None, None,
-                                    None, None, None, None, 0, None)
+                                    None, None, None, None, None, 0, None)
     assert rc == 1
     d = kv.h2o_desc(batch=2, heads=3, d=128, cap=300, cur_len=0)
     rc = lib.kvscore_h2o_accumulate(ctypes.byref(d), kv.KVS_H2O_DECODE, None, None, None, None,
-                                    None, None, None, None, None, None, 0, None)
+                                    None, None, None, None, None, None, None, 0, None)
     assert rc == 1
 
 
@@ -212,3 +212,15 @@ def test_retention_shift_and_noalloc_host_checks():
                      n_sink=1, chunk=1, budget=128)
     assert lib.kvscore_topb_select_noalloc(ctypes.byref(d), fake, fake, None, None) == 2
     assert "maximum" in kv.last_error()
+
+
+def test_probs_mask_checks():
+    """kvscore_probs takes the window-causal or no mask; the causal and slot
+    masks belong to kvscore_h2o_accumulate (unsupported here), others are invalid."""
+    kv, lib = _lib()
+    d = _desc(kv)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: the mask check fails first
+    for mask, status in ((kv.KVS_MASK_CAUSAL, 2), (kv.KVS_MASK_SLOTS, 2), (9, 1), (-1, 1)):
+        rc = lib.kvscore_probs(ctypes.byref(d), mask, fake, fake, fake, fake, fake, fake, fake, 0,
+                               None)
+        assert rc == status, (mask, kv.last_error())

@@ -59,13 +59,15 @@ def _sorted_by_pos(pos, vals):
     return np.take_along_axis(key, order, 1), np.take_along_axis(vals, order, 1)
 
 
-def run_lockstep(cfg, dev, rows, steps, gen_device="cpu"):
+def run_lockstep(cfg, dev, rows, steps, gen_device="cpu", write_last_free=False):
     """Prefill, prompt reduction and `steps` decode steps on the GPU for every
     row of cfg; the oracle follows `rows` in lockstep.  Per step: O within
     1e-3 of the row's largest component plus the rounding of O's storage type
     (a half ulp of |o|), the accumulated score of every retained token within
     1e-3 relative, the evicted position equal to the oracle's (or at a near
-    tie, which the oracle then adopts) and the retained sets equal."""
+    tie, which the oracle then adopts) and the retained sets equal.  With
+    write_last_free each new token goes into the highest free slot through
+    write_slot (the default is the lowest)."""
     inp = h2o_inputs(cfg, device=gen_device)
     dt = TORCH_DTYPES[cfg.dtype]
     cache = kv.H2OCache(cfg.batch, cfg.heads, cfg.d, cfg.cap, dt, cfg.heavy_frac,
@@ -90,7 +92,11 @@ def run_lockstep(cfg, dev, rows, steps, gen_device="cpu"):
     for s in range(steps):
         pos_before = _rows(cache.slot_pos, rows).cpu().numpy().astype(np.int64)
         q, k, v = (inp[x][s].to(dev) for x in ("q", "k", "v"))
-        O, ev = cache.step(q, k, v)
+        wslot = None
+        if write_last_free:
+            slot_idx = torch.arange(cfg.cap, device=dev, dtype=torch.int32).expand_as(cache.slot_pos)
+            wslot = torch.where(cache.slot_pos < 0, slot_idx, -1).amax(dim=-1).to(torch.int32)
+        O, ev = cache.step(q, k, v, write_slot=wslot)
         o_ref, _ = ora.attend(_rows(inp["q"][s], rows).cpu(), _rows(inp["k"][s], rows).cpu(),
                               _rows(inp["v"][s], rows).cpu())
         O = _rows(O, rows).cpu().double().numpy()
@@ -101,10 +107,11 @@ def run_lockstep(cfg, dev, rows, steps, gen_device="cpu"):
         bound = 1e-3 * scale + o_round * np.abs(o_ref)
         assert np.all(np.abs(O - o_ref) <= bound), \
             "step %d: O err %g of the row max" % (s, (np.abs(O - o_ref) / scale).max())
-        # the GPU wrote the new token into the lowest slot that was free
+        # the GPU wrote the new token into the lowest slot that was free (or the
+        # highest, through write_slot)
         free = pos_before < 0
         assert free.any(axis=1).all(), "step %d: a row had no free slot" % s
-        ws = free.argmax(axis=1)
+        ws = (cfg.cap - 1 - free[:, ::-1].argmax(axis=1)) if write_last_free else free.argmax(axis=1)
         gpos_slots = pos_before.copy()
         gpos_slots[ar, ws] = cache.cur_len - 1
         # retained set and accumulated scores before the eviction
@@ -143,6 +150,38 @@ def test_small_lockstep(dev, dtype, d):
     rows = list(range(cfg.batch * cfg.heads))
     ties = run_lockstep(cfg, dev, rows, cfg.steps)
     print("small %s d=%d: near-tie evictions %d" % (dtype, d, ties))
+
+
+def test_write_slot_lockstep(dev):
+    """The caller picks each row's slot (here the highest free one instead of
+    the default lowest): the same retained sets, accumulators and evictions
+    by position, in lockstep with the oracle."""
+    cfg = OPT30B_H2O.with_(name="write-slot", batch=2, heads=3, prompt=200, steps=60, seed=36)
+    run_lockstep(cfg, dev, list(range(cfg.batch * cfg.heads)), cfg.steps, write_last_free=True)
+
+
+def test_write_slot_not_free_leaves_row_unchanged(dev):
+    """A write_slot that is occupied, or outside [0, cap), leaves its row's
+    cache, slot map and accumulators exactly as they were and reports -2;
+    the other rows step normally."""
+    cfg = OPT30B_H2O.with_(name="bad-slot", batch=1, heads=4, prompt=200, steps=2, seed=37)
+    inp = h2o_inputs(cfg, device="cpu")
+    cache = kv.H2OCache(cfg.batch, cfg.heads, cfg.d, cfg.cap, torch.float16, cfg.heavy_frac,
+                        cfg.recent_frac, dev)
+    cache.prefill(*(inp[k].to(dev) for k in ("Qp", "Kp", "Vp")))
+    torch.cuda.synchronize()
+    before = {n: getattr(cache, n).clone() for n in ("K", "V", "slot_pos", "acc")}
+    # rows: occupied slot 0, slot cap (out of range), slot -1, a free slot
+    free0 = int((before["slot_pos"][0, 3] < 0).nonzero()[0, 0])
+    wslot = torch.tensor([[0, cfg.cap, -1, free0]], dtype=torch.int32, device=dev)
+    q, k, v = (inp[x][0].to(dev) for x in ("q", "k", "v"))
+    _, ev = cache.step(q, k, v, write_slot=wslot)
+    torch.cuda.synchronize()
+    assert ev[0, :3].tolist() == [-2, -2, -2]
+    for n in ("K", "V", "slot_pos", "acc"):
+        assert torch.equal(getattr(cache, n)[0, :3], before[n][0, :3]), n
+    assert int(cache.slot_pos[0, 3, free0]) == cache.cur_len - 1
+    assert int(ev[0, 3]) != -2
 
 
 def test_ragged_prompt_lockstep(dev):

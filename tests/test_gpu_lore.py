@@ -117,6 +117,31 @@ def test_subnormal_row_weights(dev, lam, omega_1):
     compare(cfg, g, run_oracle(cfg, inp))
 
 
+def test_probs_without_mask(dev):
+    """KVS_MASK_NONE: every scoring row sees all n tokens, so the statistics
+    are the oracle's with no causal window rows (w = 0 in its visibility);
+    the window rows' statistics differ from the window-causal ones."""
+    cfg = TINY.with_(name="mask-none", dtype="bf16", d=128, h_q=8, h_kv=2, n=1000, d_model=512,
+                     seed=18)
+    inp = lore_inputs(cfg)
+    desc = kv.lore_desc(dtype=TORCH_DTYPES[cfg.dtype], **lore_desc_kwargs(cfg))
+    Q, K, V = (inp[k].to(dev).contiguous() for k in ("Q", "K", "V"))
+    b, hq, nq, d = Q.shape
+    outs = {}
+    for mask in (kv.KVS_MASK_NONE, kv.KVS_MASK_WINDOW_CAUSAL):
+        m = torch.empty(b, hq, nq, device=dev)
+        l = torch.empty_like(m)
+        O = torch.empty(b, hq, nq, d, device=dev)
+        ws = torch.empty(kv.kvs_lore_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+        kv.kvscore_probs(desc, Q, K, V, m, l, O, ws, mask=mask)
+        torch.cuda.synchronize()
+        outs[mask] = (m.cpu().numpy(), l.cpu().numpy(), O.cpu().numpy())
+    m_o, l_o, O_o = oracle.lore_attention(inp["Q"], inp["K"], inp["V"], 0)
+    check_stats(*outs[kv.KVS_MASK_NONE], m_o, l_o, O_o)
+    assert not np.allclose(outs[kv.KVS_MASK_NONE][1][..., :cfg.w],
+                           outs[kv.KVS_MASK_WINDOW_CAUSAL][1][..., :cfg.w])
+
+
 def test_mistral_16k_full(dev):
     inp = lore_inputs(MISTRAL_16K)
     compare(MISTRAL_16K, run_gpu(MISTRAL_16K, inp, dev), run_oracle(MISTRAL_16K, inp))
