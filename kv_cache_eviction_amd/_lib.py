@@ -13,7 +13,10 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvscore.so")
+# KVS_SANITIZED_BUILD=1 selects the host-sanitized debug build (build.py
+# --sanitize; its runtime must be preloaded)
+LIB_PATH = os.path.join(_PKG, "_build_san" if os.environ.get("KVS_SANITIZED_BUILD") == "1" else "",
+                        "libkvscore.so")
 
 KVS_F32, KVS_BF16, KVS_F16 = 0, 1, 2
 KVS_H2O_PREFILL, KVS_H2O_DECODE = 0, 1

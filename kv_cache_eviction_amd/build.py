@@ -1,8 +1,14 @@
 """Build libkvscore.so (the HIP kernels + C ABI) for gfx950, in-tree.
 
-Usage: python -m kv_cache_eviction_amd.build [-v]
+Usage: python -m kv_cache_eviction_amd.build [-v] [--sanitize]
 Each source compiles to an object under kv_cache_eviction_amd/_build/, then
 they link into kv_cache_eviction_amd/libkvscore.so.  Always rebuilds.
+
+--sanitize builds kv_cache_eviction_amd/_build_san/libkvscore.so with the
+host code (argument checks, workspace planning, dispatch) instrumented by
+AddressSanitizer and UndefinedBehaviorSanitizer; the device code is built as
+usual.  The sanitizer runtime is not linked in: load it first with
+LD_PRELOAD (see README), and select this library with KVS_SANITIZED_BUILD=1.
 """
 
 import concurrent.futures as cf
@@ -16,6 +22,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvscore.so")
+BUILD_SAN = os.path.join(PKG, "_build_san")
+LIB_SAN = os.path.join(BUILD_SAN, "libkvscore.so")
+# host-only sanitizer flags: each -fsanitize= right after -Xarch_host, so the
+# device code is compiled exactly as in the normal build
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
 SOURCES = ["attn.hip", "deletion.hip", "select.hip", "h2o.hip", "reliability.hip", "fidelity.hip", "peaks.hip",
            "timing.cpp",
            "capi.cpp"]
@@ -38,9 +50,10 @@ def _flags():
             "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wno-unused-command-line-argument"]
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc()] + _flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, verbose, sanitize=False):
+    obj = os.path.join(BUILD_SAN if sanitize else BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc()] + _flags() + (SAN_FLAGS if sanitize else []) + [
+        "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,20 +66,21 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    os.makedirs(BUILD_SAN if sanitize else BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, verbose, sanitize), SOURCES))
+    lib = LIB_SAN if sanitize else LIB
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("linking libkvscore.so failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -54,7 +54,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lore_oracle.c")
-_BUILD = os.path.join(_HERE, "_build")
+# KVS_SANITIZED_BUILD=1 selects the AddressSanitizer + UBSan build (clang,
+# the same sanitizer runtime as the library's sanitized build)
+_SANITIZED = os.environ.get("KVS_SANITIZED_BUILD") == "1"
+_BUILD = os.path.join(_HERE, "_build_san" if _SANITIZED else "_build")
 _SO = os.path.join(_BUILD, "liboracle.so")
 _lib_handle = None
 
@@ -62,12 +65,22 @@ _DP = ctypes.POINTER(ctypes.c_double)
 
 
 def build(force: bool = False) -> str:
-    """Compile the C part of the oracle with gcc (IEEE fp64: no fast-math)."""
+    """Compile the C part of the oracle with gcc (IEEE fp64: no fast-math).
+    With KVS_SANITIZED_BUILD=1: ROCm's clang with AddressSanitizer and
+    UndefinedBehaviorSanitizer and its OpenMP runtime, into _build_san/."""
     os.makedirs(_BUILD, exist_ok=True)
     if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
         tmp = _SO + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-                               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
+        if _SANITIZED:
+            llvm = "/opt/rocm/llvm"
+            cmd = [llvm + "/bin/clang", "-O1", "-g", "-fno-omit-frame-pointer",
+                   "-fsanitize=address,undefined", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                   "-ffp-contract=off", _SRC, "-o", tmp, "-L" + llvm + "/lib",
+                   "-Wl,-rpath," + llvm + "/lib", "-lm"]
+        else:
+            cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                   "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
         os.replace(tmp, _SO)
     return _SO
 
