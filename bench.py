@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (the tiny fp32 workload's matrix ops)
 
 
 def kernel_work(cfg):
@@ -40,7 +41,7 @@ def kernel_work(cfg):
     Bytes count one read of the operands and one write of the results.
     """
     b, n, hq, hk, d, D, nq = cfg.batch, cfg.n, cfg.h_q, cfg.h_kv, cfg.d, cfg.d_model, cfg.n_q
-    s = 2  # bytes per bf16 element
+    s = 4 if cfg.dtype == "f32" else 2  # bytes per element
     kv_bytes = 2 * b * hk * n * d * s
     n_keep = cfg.n_keep
     return {
@@ -177,6 +178,97 @@ def _cpu_layer(oracle, cfg, inp, G, d, heads, threads):
         oracle.compact(K, V, kept)
         dt += time.perf_counter() - t0
     return dt
+
+
+def bench_config_row(kv, torch, dev, cfg, reps=10, copies=4):
+    """One whole LORE-KV eviction (probs -> deletion -> top-B -> compaction)
+    on another workload shape, timed on the device (config_row_cpu times the
+    fp64 oracle on the same inputs).  `copies` input sets are cycled so a
+    layer that fits the 256 MB MALL (the Mistral 16K layer, 67 MB of K/V) is
+    not re-read from it between reps."""
+    from kvsynth import lore_inputs, TORCH_DTYPES
+    dt = TORCH_DTYPES[cfg.dtype]
+    sets = []
+    for c in range(copies):
+        inp = lore_inputs(cfg, layer=0, device=dev)
+        sets.append({k: inp[k].contiguous() for k in ("Q", "K", "V", "W_O", "omega")})
+    desc = kv.lore_desc(batch=cfg.batch, n=cfg.n, h_q=cfg.h_q, h_kv=cfg.h_kv, d=cfg.d,
+                        d_model=cfg.d_model, w=cfg.w, m=cfg.m, t=cfg.t, n_sink=cfg.n_sink,
+                        chunk=cfg.chunk, budget=cfg.budget, eps=cfg.eps,
+                        lambda_l=cfg.lambda_l, dtype=dt)
+    ev = kv.LoreEviction(desc, dev)
+    Ko = torch.empty(cfg.batch, cfg.h_kv, desc.n_keep, cfg.d, dtype=dt, device=dev)
+    Vo = torch.empty_like(Ko)
+
+    def once(i):
+        x = sets[i % copies]
+        ev.run(x["Q"], x["K"], x["V"], x["W_O"], x["omega"], Ko, Vo)
+
+    for i in range(copies):
+        once(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(reps):
+        once(i)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    kv.kvs_timing_reset()
+    kv.kvs_timing_enable(True)
+    for i in range(copies):
+        once(i)
+    torch.cuda.synchronize()
+    per = {}
+    for nm, t in kv.kvs_timing_records():
+        per.setdefault(nm, []).append(t)
+    kv.kvs_timing_enable(False)
+    kv.kvs_timing_reset()
+    work = kernel_work(cfg)
+    credited = sum(w["flops"] for w in work.values())
+    tokens = cfg.batch * cfg.n * cfg.h_kv
+    # per launch averages (head-subset launches of one call are summed per call)
+    kms = {nm: sum(v) / copies for nm, v in per.items()}
+    roofs = {nm: roofline_of(nm, work, kms[nm]) for nm in kms if nm in work}
+    peak = PEAK_FP32_TFLOPS if cfg.dtype == "f32" else PEAK_BF16_TFLOPS
+    row = {"workload": cfg.name, "dtype": cfg.dtype, "batch": cfg.batch, "n": cfg.n,
+           "h_q": cfg.h_q, "h_kv": cfg.h_kv, "budget": cfg.budget, "ms_per_call": round(ms, 4),
+           "value": round(tokens / (ms * 1e-3), 1), "unit": "KV tokens/s",
+           "mfma_frac": round(credited / (ms * 1e-3) / 1e12 / peak, 4), "mfma_peak_tflops": peak,
+           "credited_gflop": round(credited / 1e9, 1),
+           "kernels_ms_per_call": {k: round(v, 4) for k, v in kms.items()},
+           "score_roofline": roofs.get("score_lore"),
+           "timing": "%d calls cycling %d input sets, between one event pair" % (reps, copies)}
+    del sets, ev
+    torch.cuda.empty_cache()
+    return row
+
+
+def config_row_cpu(cfg, oracle_threads):
+    """The fp64 oracle on the whole of a workload (the device rows' first input
+    set), its inputs widened to fp64 outside the timer; once per thread count
+    (0 = every host core)."""
+    import oracle
+    from kvsynth import lore_inputs
+    tokens = cfg.batch * cfg.n * cfg.h_kv
+    inp = lore_inputs(cfg, layer=0)
+    x64 = {k: inp[k].double().numpy() for k in ("Q", "K", "V", "W_O", "omega")}
+    cpu = []
+    for nt in oracle_threads:
+        t0 = time.perf_counter()
+        r = oracle.lore_scores(x64["Q"], x64["K"], x64["V"], x64["W_O"], x64["omega"], w=cfg.w,
+                               m=cfg.m, t=cfg.t, eps=cfg.eps, lambda_l=cfg.lambda_l, nthreads=nt)
+        kept, _ = oracle.topb_select(r["S"], n_sink=cfg.n_sink, w=cfg.w, chunk=cfg.chunk,
+                                     budget=cfg.budget)
+        oracle.compact(x64["K"], x64["V"], kept)
+        dt_s = time.perf_counter() - t0
+        cores = len(os.sched_getaffinity(0)) if nt == 0 else nt
+        cpu.append({"value": round(tokens / dt_s, 1), "unit": "KV tokens/s", "cores": cores,
+                    "kind": "oracle", "seconds": round(dt_s, 3),
+                    "sample": "the whole workload: scores (fp64, incl. the Cholesky factors), "
+                              "top-B and compaction"})
+    return cpu
 
 
 def bench_h2o(kv, torch, dev, layers=4):
@@ -385,6 +477,8 @@ def main():
     ap.add_argument("--config", default="llama3.1-8b-128k-32layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-h2o", action="store_true")
+    ap.add_argument("--no-config-rows", action="store_true",
+                    help="skip the Mistral 16K / Qwen batch / tiny workload rows")
     ap.add_argument("--streams", type=int, default=1,
                     help="spread the layers of a plain timed step over this many streams")
     ap.add_argument("--graph", action="store_true",
@@ -688,16 +782,30 @@ def main():
     del ev0
     out["planted_fact_recall"] = rec
     out["retention_shift"] = shift
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg, data)
+    # every device measurement first, then the host-side oracle timings, so the
+    # GPU never sits idle (and clocks down) between two device measurements
+    from kvsynth import MISTRAL_16K, QWEN_14B_BATCH, TINY
+    plan = ((MISTRAL_16K, 4, (0, 1)), (QWEN_14B_BATCH, 4, (0,)), (TINY, 1, (0, 1)))
+    rows = {}
+    if not args.no_config_rows:
+        # the other LORE-KV workloads: the Mistral-7B 16K layer, the Qwen2.5-14B
+        # batch and the tiny fp32 layer (launch-bound), each beside the oracle
+        for c, copies, _ in plan:
+            print("[bench] workload row %s" % c.name, file=sys.stderr, flush=True)
+            rows[c.name] = bench_config_row(kv, torch, dev, c, copies=copies)
+        out["workload_rows"] = rows
     if not args.no_h2o:
         print("[bench] H2O decode", file=sys.stderr, flush=True)
-        del data
-        torch.cuda.empty_cache()
         out["h2o"] = bench_h2o(kv, torch, dev)
         print("[bench] compact on the Qwen batch shape", file=sys.stderr, flush=True)
         out["compact_qwen"] = bench_compact_qwen(kv, torch, dev)
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, data)
+        for c, _, threads in plan:
+            if c.name in rows:
+                print("[bench] workload row %s: oracle" % c.name, file=sys.stderr, flush=True)
+                rows[c.name]["cpu_baseline"] = config_row_cpu(c, threads)
     print(json.dumps(out), flush=True)
 
 

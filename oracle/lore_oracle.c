@@ -64,10 +64,12 @@ int ora_lore_attention(int batch, int n, int h_q, int h_kv, int d, int n_q, int 
     const int G = h_q / h_kv;
     const double scale = 1.0 / sqrt((double)d);
     const long rows = (long)batch * h_q * n_q;
+    /* threads for this call only (a num_threads clause, not the process-wide
+     * setting, so a call with nthreads = 1 leaves later calls on all cores) */
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
+    const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
 #endif
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
     for (long row = 0; row < rows; ++row) {
         const int r = (int)(row % n_q);
         const int h = (int)((row / n_q) % h_q);
@@ -112,7 +114,7 @@ int ora_lore_scores(int batch, int n, int h_q, int h_kv, int d, int w, int m_tra
     const int n_q = w + m_traj * t_len;
     const double scale = 1.0 / sqrt((double)d);
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
+    const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
 #endif
     double *ot = (double *)malloc(sizeof(double) * (size_t)n_q * d);
     if (!ot) return 2;
@@ -135,7 +137,7 @@ int ora_lore_scores(int batch, int n, int h_q, int h_kv, int d, int w, int m_tra
                     for (int j = k; j < d; ++j) s += Rh[k * d + j] * Oh[r * d + j];
                     ot[r * d + k] = s;
                 }
-#pragma omp parallel
+#pragma omp parallel num_threads(nt)
             {
                 double *vt = (double *)malloc(sizeof(double) * (size_t)d);
                 double *psi_m = (double *)malloc(sizeof(double) * (size_t)(m_traj > 0 ? m_traj : 1));
