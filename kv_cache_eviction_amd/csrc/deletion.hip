@@ -892,7 +892,12 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
     const int tok = t0p + wv * TPW + lane % TPW;
     if (lane < TPW && tok < t_end) {
       sum *= out_scale;
-      Sout[tok] = accumulate ? Sout[tok] + sum : sum;
+      // a later head-subset launch adds to S with a non-returning atomic:
+      // no wait on a load of S (which would also wait for the tile loads in
+      // flight), and one add per element per launch in stream order is the
+      // same sum as a load-add-store
+      if (accumulate) unsafeAtomicAdd(&Sout[tok], sum);
+      else Sout[tok] = sum;
     }
   };
   auto tile = [&](auto masked, int cur, int t0, bool pending, float part) {

@@ -195,8 +195,12 @@ def test_exact_ties_keep_lower_indices(dev):
         assert np.array_equal(row, expect)
 
 
-def test_deterministic(dev):
-    cfg = MISTRAL_16K.with_(name="det", n=4096)
+@pytest.mark.parametrize("cfg", [MISTRAL_16K.with_(name="det", n=4096),
+                                 QWEN_14B_BATCH.with_(name="det-g5", n=4096, batch=2)],
+                         ids=["g4", "g5-two-launches"])
+def test_deterministic(dev, cfg):
+    """Bitwise identical results over three runs, also for a query-head group
+    of 5, whose score pass runs as two launches (the second adding to S)."""
     inp = lore_inputs(cfg)
     runs = [run_gpu(cfg, inp, dev) for _ in range(3)]
     for r in runs[1:]:
