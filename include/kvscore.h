@@ -121,13 +121,16 @@ typedef enum {
  *  row_max  [batch][h_q][n_q] fp32    out: max_i q.k_i / sqrt(d) over visible i.
  *  row_sum  [batch][h_q][n_q] fp32    out: sum_i exp(q.k_i/sqrt(d) - row_max).
  *  O        [batch][h_q][n_q][d] fp32 out: o_q = sum_i a_{q,i} v_i.
+ *  P        [batch][h_q][n_q][n] fp32 out, nullable: the probabilities a_{q,i}
+ *           themselves, 0 where the mask hides token i from row q.  The path
+ *           does not need them (the score pass recomputes each probability
+ *           from q.k and the row statistics), so they are formed only when P
+ *           is given, by an extra pass over K after the statistics
+ *           (1 GiB per layer of the 128K workload).
  *  ws, ws_bytes                       workspace (>= kvs_lore_workspace_bytes).
- * The dense probability matrix a [n_q][n] is not an output: the path never
- * forms it (the score pass recomputes each probability from q.k and the row
- * statistics), and at the 128K workload it would be 1 GiB per layer.
  */
 kvs_status kvscore_probs(const kvs_lore_desc *desc, int32_t mask, const void *Q, const void *K,
-                         const void *V, float *row_max, float *row_sum, float *O,
+                         const void *V, float *row_max, float *row_sum, float *O, float *P,
                          void *ws, size_t ws_bytes, void *stream);
 
 /*

@@ -77,7 +77,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvs_lore_workspace_bytes.restype = sz
     lib.kvs_lore_workspace_bytes.argtypes = [LP]
     lib.kvscore_probs.restype = i32
-    lib.kvscore_probs.argtypes = [LP, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kvscore_probs.argtypes = [LP, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kvscore_deletion.restype = i32
     lib.kvscore_deletion.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kvscore_baseline_scores.restype = i32
@@ -184,7 +184,7 @@ def _ws_check(ws, need):
 
 
 def kvscore_probs(desc, Q, K, V, row_max, row_sum, O, ws, stream=None,
-                  mask=KVS_MASK_WINDOW_CAUSAL):
+                  mask=KVS_MASK_WINDOW_CAUSAL, P=None):
     dt = CODE_DTYPE[desc.dtype]
     b, hq, hk, n, d, nq = desc.batch, desc.h_q, desc.h_kv, desc.n, desc.d, desc.n_q
     _need(Q, "Q", (b, hq, nq, d), dt)
@@ -193,10 +193,11 @@ def kvscore_probs(desc, Q, K, V, row_max, row_sum, O, ws, stream=None,
     _need(row_max, "row_max", (b, hq, nq), torch.float32)
     _need(row_sum, "row_sum", (b, hq, nq), torch.float32)
     _need(O, "O", (b, hq, nq, d), torch.float32)
+    _need(P, "P", (b, hq, nq, n), torch.float32, optional=True)
     need = kvs_lore_workspace_bytes(desc)
     _ws_check(ws, need)
     _check(load().kvscore_probs(ctypes.byref(desc), int(mask), _ptr(Q), _ptr(K), _ptr(V), _ptr(row_max),
-                                _ptr(row_sum), _ptr(O), _ptr(ws), ws.numel() * ws.element_size(),
+                                _ptr(row_sum), _ptr(O), _ptr(P), _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream(stream)), "kvscore_probs")
 
 

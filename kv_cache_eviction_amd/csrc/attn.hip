@@ -530,6 +530,94 @@ attn_combine_rows_kernel(const float *__restrict__ pm, const float *__restrict__
   consts[head * 64 + q] = make_float4(beta2, 0.f, 1.f, __int_as_float(last));
 }
 
+// The dense probabilities a_{q,i} of the scoring rows (an optional output of
+// kvscore_probs): P[b][h][r][i] = 2^(s c - beta2_r) for the tokens row r sees
+// and exactly 0 for the others, beta2_r = row_max_r log2(e) + log2(row_sum_r)
+// from the combined statistics.  One workgroup per (64-token tile, query head,
+// sequence), one wave per 16-row block: the K tile is staged in LDS, S = Q K^T
+// runs on the matrix cores with the tokens across the columns, and each store
+// instruction writes 16 consecutive tokens of 4 rows.
+template <typename Tin, int D>
+__global__ void __launch_bounds__(256)
+probs_write_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K,
+                   const float *__restrict__ row_max, const float *__restrict__ row_sum,
+                   RowGeom geo, int h_kv, float *__restrict__ P) {
+  typedef typename FragOf<Tin>::type FQ;
+  constexpr int KS = D / 32;
+  constexpr int TN = 64;
+  constexpr int EPC = 16 / (int)sizeof(Tin);
+  constexpr int CPR = D / EPC;
+  constexpr int KROW = D + EPC;
+  constexpr int ITEMS = TN * CPR;
+  __shared__ __align__(16) Tin Ks[TN * KROW];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int t0 = blockIdx.x * TN, h = blockIdx.y, b = blockIdx.z;
+  const int n = geo.n, nq = geo.nq, G = geo.group;
+  const long head = (long)b * h_kv * G + h;  // b * h_q + h
+  const Tin *Kb = K + ((long)b * h_kv + h / G) * (long)n * D;
+  constexpr uint32_t RB = D * sizeof(Tin);
+  // rows past the end of the cache read as zeros (their tokens are not stored)
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (long)t0 * D, range_bytes(t0, min(n, t0 + TN), RB));
+#pragma unroll
+  for (int u = 0; u < (ITEMS + 255) / 256; ++u) {
+    const int idx = threadIdx.x + u * 256;
+    if (ITEMS % 256 == 0 || idx < ITEMS) {
+      const int row = idx / CPR, ch = idx % CPR;
+      *reinterpret_cast<U128 *>(&Ks[row * KROW + ch * EPC]) =
+          buf_load16(rk, (uint32_t)(row * D + ch * EPC) * sizeof(Tin));
+    }
+  }
+  // A fragment: query row 16 wv + col; results: rows 16 wv + 4 grp + j
+  const int rq = 16 * wv + col;
+  FQ qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qf[ks] = rq < nq ? load8<Tin>(Q + (head * nq + rq) * D + ks * 32 + 8 * grp) : zero8<Tin>();
+  float beta[4];
+  int last[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 16 * wv + 4 * grp + j;
+    beta[j] = r < nq ? row_max[head * nq + r] * kLog2e + log2f(row_sum[head * nq + r]) : 0.f;
+    last[j] = r < nq ? (r < geo.w ? n - geo.w + r : n - 1) : -1;
+  }
+  const float c = kLog2e * rsqrtf((float)D);
+  __syncthreads();
+#pragma unroll
+  for (int tb = 0; tb < TN / 16; ++tb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      acc = mma(qf[ks], load8<Tin>(&Ks[(tb * 16 + col) * KROW + ks * 32 + 8 * grp]), acc);
+    const int tok = t0 + tb * 16 + col;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * wv + 4 * grp + j;
+      if (r < nq && tok < n)
+        P[(head * nq + r) * (long)n + tok] =
+            tok <= last[j] ? hw_exp2(fmaf(acc[j], c, -beta[j])) : 0.f;
+    }
+  }
+}
+
+hipError_t launch_probs_write(int etype, int d, const void *Q, const void *K,
+                              const float *row_max, const float *row_sum, RowGeom geo, int batch,
+                              int h_kv, float *P, hipStream_t st) {
+  const dim3 grid((geo.n + 63) / 64, h_kv * geo.group, batch);
+  {
+    TimedLaunch tl_("probs_write", st);
+#define KVS_PW(T, DD) \
+  hipLaunchKernelGGL((probs_write_kernel<T, DD>), grid, dim3(256), 0, st, (const T *)Q, (const T *)K, \
+                     row_max, row_sum, geo, h_kv, P)
+    if (etype == E_F32) { if (d == 64) KVS_PW(float, 64); else KVS_PW(float, 128); }
+    else if (etype == E_BF16) { if (d == 64) KVS_PW(bf16, 64); else KVS_PW(bf16, 128); }
+    else { if (d == 64) KVS_PW(f16, 64); else KVS_PW(f16, 128); }
+#undef KVS_PW
+  }
+  return hipGetLastError();
+}
+
 SplitPlan attn_split_plan(int units, int n) {
   const int target = 256;  // about one workgroup per CU; fewer splits mean less partial-O traffic
   int splits = (target + units - 1) / units;

@@ -164,7 +164,7 @@ KVS_API size_t kvs_lore_workspace_bytes(const kvs_lore_desc *desc) {
 
 KVS_API kvs_status kvscore_probs(const kvs_lore_desc *desc, int32_t mask, const void *Q,
                                  const void *K, const void *V, float *row_max, float *row_sum,
-                                 float *O, void *ws, size_t ws_bytes, void *stream) {
+                                 float *O, float *P, void *ws, size_t ws_bytes, void *stream) {
   kvs_status st = check_lore(desc);
   if (st != KVS_OK) return st;
   if (mask == KVS_MASK_CAUSAL || mask == KVS_MASK_SLOTS)
@@ -188,7 +188,10 @@ KVS_API kvs_status kvscore_probs(const kvs_lore_desc *desc, int32_t mask, const 
   if (e != hipSuccess) return hip_status(e, "attention pass");
   e = kvs::launch_attn_combine_lore(desc->d, pm, pl, po, desc->batch * desc->h_q, p.split.splits,
                                     geo.nq, row_max, row_sum, O, s);
-  return hip_status(e, "attention combine");
+  if (e != hipSuccess || !P) return hip_status(e, "attention combine");
+  e = kvs::launch_probs_write(desc->dtype, desc->d, Q, K, row_max, row_sum, geo, desc->batch,
+                              desc->h_kv, P, s);
+  return hip_status(e, "probabilities");
 }
 
 KVS_API kvs_status kvscore_deletion(const kvs_lore_desc *desc, const void *Q, const void *K,

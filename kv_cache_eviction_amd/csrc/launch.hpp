@@ -46,6 +46,11 @@ hipError_t launch_attn_partial(int etype, int d, bool with_o, const void *Q, con
 hipError_t launch_attn_combine_lore(int d, const float *part_m, const float *part_l,
                                     const float *part_O, int heads, int splits, int nq,
                                     float *row_max, float *row_sum, float *O, hipStream_t st);
+// LORE: the dense probabilities P [batch][h_q][nq][n] from the combined
+// statistics (geo.w = 0: every row sees every token).
+hipError_t launch_probs_write(int etype, int d, const void *Q, const void *K,
+                              const float *row_max, const float *row_sum, RowGeom geo, int batch,
+                              int h_kv, float *P, hipStream_t st);
 // H2O: writes per-row constants {beta2, 0, 1, last-visible bits} [heads][64].
 hipError_t launch_attn_combine_rows(const float *part_m, const float *part_l, int heads,
                                     int splits, int group, int P, float4 *consts, hipStream_t st);

@@ -141,6 +141,31 @@ def lore_attention(Q, K, V, w, nthreads=0):
     return m, l, O
 
 
+def lore_probabilities(Q, K, w):
+    """The attention probabilities a_{q,i} of every scoring row over the cache.
+
+    LORE-KV page, Method (a_{q,i} of Eq. 5, softmax of q.k_i / sqrt(d)), with
+    the visibility of lore_attention: row r < w sees tokens 0..n-w+r, later
+    rows all n; invisible entries are exactly 0.  Written out directly
+    (logits, row maximum, exponentials, row sum), not through
+    lore_attention.  Returns P [b][h_q][n_q][n] fp64.
+    """
+    Q, K = _f64(Q), _f64(K)
+    b, h_q, n_q, d = Q.shape
+    _, h_kv, n, _ = K.shape
+    G = h_q // h_kv
+    P = np.zeros((b, h_q, n_q, n))
+    for bi in range(b):
+        for h in range(h_q):
+            s = Q[bi, h] @ K[bi, h // G].T / math.sqrt(d)          # [n_q][n]
+            for r in range(n_q):
+                last = n - w + r if r < w else n - 1
+                row = s[r, :last + 1]
+                e = np.exp(row - row.max())
+                P[bi, h, r, :last + 1] = e / e.sum()
+    return P
+
+
 def projection_factors(W_O, h_q, d):
     """R_h (upper triangular) with R_h^T R_h = W_h^T W_h for every query head.
 

@@ -62,7 +62,7 @@ def test_bad_descriptor_rejected_before_launch(kw, status):
     kv, lib = _lib()
     d = _desc(kv, **kw)
     assert lib.kvs_lore_workspace_bytes(ctypes.byref(d)) == 0
-    rc = lib.kvscore_probs(ctypes.byref(d), 1, None, None, None, None, None, None, None, 0, None)
+    rc = lib.kvscore_probs(ctypes.byref(d), 1, None, None, None, None, None, None, None, None, 0, None)
     assert rc == status, kv.last_error()
     assert kv.last_error()
 
@@ -72,10 +72,10 @@ def test_null_pointers_and_workspace():
     d = _desc(kv)
     need = lib.kvs_lore_workspace_bytes(ctypes.byref(d))
     assert need > 0
-    assert lib.kvscore_probs(ctypes.byref(d), 1, None, None, None, None, None, None, None, 0,
-                             None) == 1
+    assert lib.kvscore_probs(ctypes.byref(d), 1, None, None, None, None, None, None, None, None,
+                             0, None) == 1
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: a host check fails first
-    rc = lib.kvscore_probs(ctypes.byref(d), 1, fake, fake, fake, fake, fake, fake, fake, 16, None)
+    rc = lib.kvscore_probs(ctypes.byref(d), 1, fake, fake, fake, fake, fake, fake, fake, None, 16, None)
     assert rc == 3 and "workspace" in kv.last_error()
     rc = lib.kvscore_deletion(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake, fake,
                               fake, fake, 16, None)
@@ -109,7 +109,7 @@ def test_reliability_weights_host_checks():
     rc = lib.kvscore_reliability_weights(ctypes.byref(d), odd, fake, fake, f(1), f(1), f(0.3),
                                          fake, None, fake, big, None)
     assert rc == 1 and "aligned" in kv.last_error()
-    rc = lib.kvscore_probs(ctypes.byref(d), 1, fake, odd, fake, fake, fake, fake, fake, big, None)
+    rc = lib.kvscore_probs(ctypes.byref(d), 1, fake, odd, fake, fake, fake, fake, fake, None, big, None)
     assert rc == 1 and "aligned" in kv.last_error()
     assert lib.kv_compact(1, 1, 10, 5, 5, 128, 1, fake, fake, fake, odd, fake, None, None,
                           None, None) == 1
@@ -221,6 +221,6 @@ def test_probs_mask_checks():
     d = _desc(kv)
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: the mask check fails first
     for mask, status in ((kv.KVS_MASK_CAUSAL, 2), (kv.KVS_MASK_SLOTS, 2), (9, 1), (-1, 1)):
-        rc = lib.kvscore_probs(ctypes.byref(d), mask, fake, fake, fake, fake, fake, fake, fake, 0,
-                               None)
+        rc = lib.kvscore_probs(ctypes.byref(d), mask, fake, fake, fake, fake, fake, fake, fake, None,
+                               0, None)
         assert rc == status, (mask, kv.last_error())

@@ -142,6 +142,48 @@ def test_probs_without_mask(dev):
                            outs[kv.KVS_MASK_WINDOW_CAUSAL][1][..., :cfg.w])
 
 
+PROB_CASES = [
+    (TINY, 1),
+    (TINY.with_(name="bf16-d128-g4-n1000", dtype="bf16", d=128, h_q=8, h_kv=2, n=1000,
+                d_model=512, seed=19), 1),
+    (TINY.with_(name="f16-d64-mha-n777-nq11", dtype="f16", d=64, h_q=3, h_kv=3, n=777,
+                d_model=192, w=5, m=2, t=3, seed=20), 0),
+    (TINY.with_(name="bf16-d64-g2-b2-n300", dtype="bf16", d=64, h_q=4, h_kv=2, n=300, batch=2,
+                d_model=256, seed_per_seq=True, omega_per_seq=True, seed=21), 1),
+]
+
+
+@pytest.mark.parametrize("cfg,mask", PROB_CASES, ids=[c.name + "-mask%d" % m for c, m in PROB_CASES])
+def test_dense_probabilities(dev, cfg, mask):
+    """The optional dense probabilities P of kvscore_probs against the oracle's
+    softmax written out directly: hidden tokens exactly 0, visible ones within
+    5e-4 relative (the row statistics carry 1e-5 of the logit scale, and the
+    exponent amplifies an absolute logit error into a relative one) plus a
+    1e-9 floor for probabilities near fp32 underflow."""
+    inp = lore_inputs(cfg)
+    desc = kv.lore_desc(dtype=TORCH_DTYPES[cfg.dtype], **lore_desc_kwargs(cfg))
+    Q, K, V = (inp[k].to(dev).contiguous() for k in ("Q", "K", "V"))
+    b, hq, nq, d = Q.shape
+    m = torch.empty(b, hq, nq, device=dev)
+    l = torch.empty_like(m)
+    O = torch.empty(b, hq, nq, d, device=dev)
+    P = torch.full((b, hq, nq, cfg.n), 7.0, device=dev)
+    ws = torch.empty(kv.kvs_lore_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    kv.kvscore_probs(desc, Q, K, V, m, l, O, ws, mask=mask, P=P)
+    torch.cuda.synchronize()
+    w = cfg.w if mask == kv.KVS_MASK_WINDOW_CAUSAL else 0
+    ref = oracle.lore_probabilities(inp["Q"], inp["K"], w)
+    Pg = P.cpu().double().numpy()
+    hidden = np.zeros(ref.shape, dtype=bool)
+    for r in range(min(w, nq)):
+        hidden[:, :, r, cfg.n - w + r + 1:] = True
+    assert np.all(Pg[hidden] == 0)
+    err = np.abs(Pg - ref)[~hidden]
+    bound = 5e-4 * ref[~hidden] + 1e-9
+    assert np.all(err <= bound), "P err %g (rel)" % (err / np.maximum(ref[~hidden], 1e-30)).max()
+    assert np.allclose(Pg.sum(axis=-1), 1.0, atol=1e-4)
+
+
 def test_mistral_16k_full(dev):
     inp = lore_inputs(MISTRAL_16K)
     compare(MISTRAL_16K, run_gpu(MISTRAL_16K, inp, dev), run_oracle(MISTRAL_16K, inp))

@@ -207,3 +207,29 @@ def test_threads_do_not_change_results():
     a = oracle.lore_scores(Q, K, V, W_O, omega, nthreads=1, **args)["S"]
     b = oracle.lore_scores(Q, K, V, W_O, omega, nthreads=4, **args)["S"]
     np.testing.assert_array_equal(a, b)
+
+
+def test_probabilities_match_statistics_and_mask():
+    """lore_probabilities: rows sum to 1, entries past a window row's position
+    are exactly 0, and a = exp(s - row_max) / row_sum with lore_attention's
+    statistics (two independent computations of the same softmax); also
+    P @ V equals lore_attention's output."""
+    rng = np.random.default_rng(11)
+    b, hq, hk, n, d, w, nq = 2, 4, 2, 40, 16, 5, 9
+    Q = rng.standard_normal((b, hq, nq, d))
+    K = rng.standard_normal((b, hk, n, d))
+    V = rng.standard_normal((b, hk, n, d))
+    P = oracle.lore_probabilities(Q, K, w)
+    assert np.allclose(P.sum(axis=-1), 1.0, atol=1e-12)
+    for r in range(w):
+        assert np.all(P[:, :, r, n - w + r + 1:] == 0)
+    m, l, O = oracle.lore_attention(Q, K, V, w)
+    G = hq // hk
+    for bi in range(b):
+        for h in range(hq):
+            s = Q[bi, h] @ K[bi, h // G].T / np.sqrt(d)
+            for r in range(nq):
+                last = n - w + r if r < w else n - 1
+                ref = np.exp(s[r, :last + 1] - m[bi, h, r]) / l[bi, h, r]
+                assert np.allclose(P[bi, h, r, :last + 1], ref, rtol=1e-12, atol=0)
+            assert np.allclose(P[bi, h] @ V[bi, h // G], O[bi, h], rtol=1e-10, atol=1e-12)
