@@ -64,6 +64,17 @@ __device__ __forceinline__ long q_row(const RowGeom &g, int b, int h_kv, int kvh
   return ((long)b * h_kv + kvh) * g.n + (long)hv * 64 + r;
 }
 
+// LDS row of tile token t in the pass-1 K tile.  Block tb of the tile takes
+// token t = 32 (tb / 2) + 8 (col / 4) + 4 (tb % 2) + col % 4 into MFMA column
+// col (the order that makes each lane's logits the B-fragment k order of the
+// P.V product); storing that token in row 16 tb + col makes the fragment
+// reads walk 16 consecutive rows.
+__device__ __forceinline__ int kslot(int t) {
+  const int tb = ((t >> 5) << 1) | ((t >> 2) & 1);
+  const int cl = (((t >> 3) & 3) << 2) | (t & 3);
+  return tb * 16 + cl;
+}
+
 // QBW = 16-row query blocks per wave: a query head's 64 rows are spread over
 // 4/QBW waves.  Tiles of 64 tokens are double-buffered in LDS: the next tile's
 // global loads go to registers before the current tile is computed and into
@@ -96,9 +107,12 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
   constexpr int WPH = 4 / QBW;                // waves per query head
   constexpr int EPC = 16 / (int)sizeof(Tin);  // elements per 16-byte chunk
   constexpr int CPR = D / EPC;                // chunks per row
-  constexpr int KROW = D + EPC;               // padded LDS row (elements)
-  constexpr int VROW = TN + 16 / (int)sizeof(TV);
   constexpr bool V16 = sizeof(TV) == 2;
+  // padded LDS rows (elements).  16-bit rows carry 32 bytes of pad, which
+  // puts the 16-byte fragment reads of 16 consecutive rows (four k-slices
+  // per half-wave) in distinct banks; a 16-byte pad conflicted two ways
+  constexpr int KROW = D + (sizeof(Tin) == 2 ? 16 : EPC);
+  constexpr int VROW = TN + (V16 ? 16 : 4);
   constexpr float kSlack = 8.f;
   // K items: one 16-byte chunk; V items: a row pair (16-bit) or one row (fp32)
   constexpr int KITEMS = TN * CPR;
@@ -218,7 +232,7 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
       const int idx = threadIdx.x + u * NT;
       if (KITEMS % NT == 0 || idx < KITEMS) {
         const int row = idx / CPR, ch = idx % CPR;
-        *reinterpret_cast<U128 *>(&Ks[buf][row * KROW + ch * EPC]) = pk[u];
+        *reinterpret_cast<U128 *>(&Ks[buf][kslot(row) * KROW + ch * EPC]) = pk[u];
       }
     }
     if (WITH_O) {
@@ -282,10 +296,10 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
       constexpr bool MASKED = decltype(masked)::value;
       // S^T for the tile: block tb holds tokens (tb/2)*32 + 8*(row/4) + 4*(tb%2) + row%4.
       // LDS fragments are read one step ahead of the products that use them.
+      // (the stash put that token in LDS row 16 tb + col)
       auto load_k = [&](int tb, FQ (&kf)[KS]) {
-        const int trow = (tb >> 1) * 32 + 8 * (col >> 2) + 4 * (tb & 1) + (col & 3);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[ks] = load8<Tin>(&Ks[cur][trow * KROW + ks * 32 + 8 * grp]);
+        for (int ks = 0; ks < KS; ++ks) kf[ks] = load8<Tin>(&Ks[cur][(tb * 16 + col) * KROW + ks * 32 + 8 * grp]);
       };
       // P.V steps: (half h of the tile, 16-row block db of d), step = h * DB + db
       constexpr int PVS = WITH_O ? (TB / 2) * DB : 1;
@@ -547,7 +561,7 @@ probs_write_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K,
   constexpr int TN = 64;
   constexpr int EPC = 16 / (int)sizeof(Tin);
   constexpr int CPR = D / EPC;
-  constexpr int KROW = D + EPC;
+  constexpr int KROW = D + (sizeof(Tin) == 2 ? 16 : EPC);  // conflict-free fragment reads
   constexpr int ITEMS = TN * CPR;
   __shared__ __align__(16) Tin Ks[TN * KROW];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;

@@ -494,7 +494,8 @@ vnorm_kernel(const Tin *__restrict__ V, const typename ValueType<Tin>::type *__r
   constexpr int TN = 64;
   constexpr int EPC = 16 / (int)sizeof(Tin);
   constexpr int CPR = D / EPC;
-  constexpr int VROW = D + 16 / (int)sizeof(TV);
+  // 16-bit rows padded by 32 bytes: conflict-free fragment reads (as in the score pass)
+  constexpr int VROW = D + (sizeof(TV) == 2 ? 16 : 4);
   constexpr int PF = (TN * CPR + 255) / 256;
   __shared__ __align__(16) TV Vs[2][TN * VROW];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -664,12 +665,18 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
   constexpr int WPH = 4 / QBW;
   constexpr int EPC = 16 / (int)sizeof(Tin);
   constexpr int CPR = D / EPC;
-  constexpr int KROW = D + EPC;
-  constexpr int VROW = D + 16 / (int)sizeof(TV);
+  // 16-bit rows are padded by 32 bytes: the fragment reads (16 consecutive
+  // rows, four 16-byte k-slices per half-wave) then fall in distinct LDS
+  // banks, where a 16-byte pad left a two-way conflict on every read
+  constexpr int KROW = D + (sizeof(Tin) == 2 ? 16 : EPC);
+  constexpr int VROW = D + (sizeof(TV) == 2 ? 16 : 4);
   constexpr int ITEMS = TN * CPR;
   constexpr int PF = (ITEMS + NT - 1) / NT;
   constexpr float kTiny = 1.17549435e-38f;  // FLT_MIN
-  constexpr int V8ROW = 128 + 16;           // fp8 V row: 128 k-slots (zero past D), padded
+  // fp8 V row: 128 k-slots (zero past D) in 160 bytes; odd rows hold each
+  // pair of 16-byte chunks swapped, which makes the 32-byte fragment reads
+  // bank-conflict-free
+  constexpr int V8ROW = 128 + 32;
   __shared__ __align__(16) Tin Ks[2][TN * KROW];
   __shared__ __align__(16) TV Vs[MODE == 0 ? 2 : 1][MODE == 0 ? TN * VROW : 8];
   // V as fp8 e5m2 for the y_lo product (one block-scaled 16x16x128 MFMA)
@@ -802,7 +809,8 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
         const int row = idx / CPR, ch = idx % CPR;
         *reinterpret_cast<U128 *>(&Ks[buf][row * KROW + ch * EPC]) = pk[u];
         if (MODE == 0) store_converted16<Tin, TV>(pv[u], &Vs[buf][row * VROW + ch * EPC]);
-        if constexpr (SPLIT_Y) store_bf8x8<Tin>(pv[u], &V8s[buf][row * V8ROW + ch * EPC]);
+        if constexpr (SPLIT_Y)  // 8 fp8 bytes: half ch % 2 of 16-byte chunk ch / 2
+          store_bf8x8<Tin>(pv[u], &V8s[buf][row * V8ROW + ((((ch >> 1) ^ (row & 1)) << 4) | ((ch & 1) << 3))]);
       }
     }
     if (MODE == 0) Ns[buf][wv][lane] = pn;
@@ -822,8 +830,10 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
       // B fragment of the 16x16x128 product: token tb*16 + col, k = 32 grp .. +31
       // (with D = 64 the upper lanes hold zeros: their LDS slots are never written)
       if (32 * grp < D) {
-        const U128 *p8 = reinterpret_cast<const U128 *>(&V8s[cur][(tb * 16 + col) * V8ROW + 32 * grp]);
-        const U128 a = p8[0], b2 = p8[1];
+        const int r8 = tb * 16 + col;
+        const uint8_t *p8 = &V8s[cur][r8 * V8ROW];
+        const U128 a = *reinterpret_cast<const U128 *>(p8 + (((2 * grp) ^ (r8 & 1)) << 4));
+        const U128 b2 = *reinterpret_cast<const U128 *>(p8 + (((2 * grp + 1) ^ (r8 & 1)) << 4));
         v8 = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b2.x, (int)b2.y, (int)b2.z, (int)b2.w};
       } else {
         v8 = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
