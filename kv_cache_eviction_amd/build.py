@@ -28,7 +28,7 @@ LIB_SAN = os.path.join(BUILD_SAN, "libkvscore.so")
 # device code is compiled exactly as in the normal build
 SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
              "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
-SOURCES = ["attn.hip", "deletion.hip", "select.hip", "h2o.hip", "reliability.hip", "fidelity.hip", "peaks.hip",
+SOURCES = ["attn.hip", "deletion.hip", "select.hip", "h2o.hip", "reliability.hip", "fidelity.hip", "peaks.hip", "prefill.hip",
            "timing.cpp",
            "capi.cpp"]
 ARCH = "gfx950"

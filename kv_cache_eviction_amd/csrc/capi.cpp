@@ -550,8 +550,9 @@ KVS_API kvs_status kv_compact(int32_t batch, int32_t heads, int32_t n_src, int32
 
 namespace {
 
-// Longest prompt the prefill takes: its column-sum pass runs one launch per
-// eight 64-row blocks of the prompt (32 launches at 16384 tokens).
+// Longest prompt the prefill takes: an fp32 prompt's column-sum pass runs one
+// launch per eight 64-row blocks (32 launches at 16384 tokens); 16-bit
+// prompts run two launches at any length.
 constexpr int kMaxPrefill = 16384;
 
 kvs_status check_h2o(const kvs_h2o_desc *d, int mode) {
@@ -623,6 +624,10 @@ KVS_API kvs_status kvscore_h2o_accumulate(const kvs_h2o_desc *desc, int32_t mode
     const kvs::RowGeom geo{1, desc->cap, 64, 0, p.group};
     float *pm = at<float>(ws, p.off_pm), *pl = at<float>(ws, p.off_pl);
     float4 *consts = at<float4>(ws, p.off_consts);
+    if (desc->dtype != KVS_F32)  // 16-bit prompts: the balanced two-pass kernels
+      return hip_status(kvs::launch_prefill(desc->dtype, desc->d, q, K, desc->batch, desc->heads,
+                                            desc->cap, consts, acc, s),
+                        "prefill accumulate");
     hipError_t e = kvs::launch_attn_partial(desc->dtype, desc->d, false, q, K, nullptr, geo,
                                             desc->batch, desc->heads, p.split, pm, pl, nullptr, s);
     if (e != hipSuccess) return hip_status(e, "prefill row statistics");

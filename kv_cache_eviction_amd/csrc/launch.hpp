@@ -116,6 +116,12 @@ hipError_t measure_peaks(void *buf, size_t bytes, float *mfma_tflops, float *rea
 // H2O decode step.
 // write_slot (nullable): the slot each row's new token goes into (else the
 // lowest free one).
+// H2O prefill accumulate for bf16/fp16 prompts (prefill.hip): row constants
+// of the causal prompt rows into consts [batch*heads*ceil(P/64)][64], then
+// the column sums into acc [batch*heads][P].
+hipError_t launch_prefill(int etype, int d, const void *Q, const void *K, int batch, int heads,
+                          int P, float4 *consts, float *acc, hipStream_t st);
+
 hipError_t launch_h2o_decode(int etype, int d, int rows, int cap, int cur_len, int k_heavy,
                              int k_recent, const void *q, void *K, void *V, const void *k_new,
                              const void *v_new, const int32_t *write_slot, int32_t *slot_pos,
