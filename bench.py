@@ -51,7 +51,9 @@ def kernel_work(cfg):
                        "bound": "mfma"},
         "gram": {"flops": 2 * D * d * d * hq, "bytes": D * hq * d * s, "bound": "mfma"},
         "compact": {"flops": 0, "bytes": 2 * 2 * b * hk * n_keep * d * s, "bound": "hbm"},
-        "topb_select": {"flops": 0, "bytes": 4 * b * hk * n + 4 * b * hk * n_keep, "bound": "hbm"},
+        # the whole selection (topb_local + topb_select): S read, kept written
+        "topb": {"flops": 0, "bytes": 4 * b * hk * n + 4 * b * hk * n_keep, "bound": "hbm",
+                 "parts": ("topb_local", "topb_select")},
     }
 
 
@@ -81,10 +83,12 @@ def measured_traffic(kernel):
         rec = json.load(f)
     if rec.get("source_digest") != _csrc_digest():
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    if k is None:
+    parts = {"topb": ("topb_local", "topb_select")}.get(kernel, (kernel,))
+    ks = [rec.get("kernels", {}).get(p) for p in parts]
+    if any(k is None for k in ks):
         return None
-    return int(round((k["fetch_kib"] * rec["fetch_scale"] + k["write_kib"] * rec["write_scale"]) * 1024))
+    return int(round(sum((k["fetch_kib"] * rec["fetch_scale"] + k["write_kib"] * rec["write_scale"]) * 1024
+                         for k in ks)))
 
 
 # measured ceilings (kvs_measure_peaks), filled in by main(): reported beside
@@ -413,12 +417,32 @@ def bench_compact_qwen(kv, torch, dev, reps=20):
     ms = e0.elapsed_time(e1) / reps
     nbytes = 2 * 2 * rows * n_keep * d * 2  # read + write of the kept K and V rows
     gbs = nbytes / (ms * 1e-3) / 1e9
-    del K, V, sets, scrub
+    del K, V, sets
+    # The same bytes moved by a plain contiguous device copy, timed the same
+    # way (reps back-to-back launches, a different source slice each, after
+    # the scrub): what one launch of this size reaches on this machine without
+    # the kept-index indirection.
+    half = nbytes // 4  # bf16 elements read (= written) per rep
+    src = torch.empty(reps * half, dtype=torch.bfloat16, device=dev)
+    src.fill_(1.5)
+    dst = torch.empty_like(src)
+    scrub.fill_(2)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for i in range(reps):
+        dst[i * half:(i + 1) * half].copy_(src[i * half:(i + 1) * half])
+    e1.record(st)
+    torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1) / reps
+    copy_gbs = nbytes / (copy_ms * 1e-3) / 1e9
+    del src, dst, scrub
     torch.cuda.empty_cache()
     return {"workload": cfg.name + "-compact", "kernel_ms": round(ms, 4), "bytes": nbytes,
             "kept_sets": "sink + %d random whole chunks of %d + window, a different set per rep"
                          % (per, ch),
             "timing": "%d back-to-back launches, distinct kept sets and outputs" % reps,
+            "contiguous_copy_same_bytes": {"ms": round(copy_ms, 4), "achieved_gbs": round(copy_gbs, 1),
+                                           "compact_frac_of_copy": round(copy_ms / ms, 4)},
             "roofline": with_measured({"kernel": "compact", "bound": "hbm", "achieved": round(gbs, 1),
                                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None})}
@@ -625,6 +649,9 @@ def main():
     dominant = max(per, key=lambda k: per[k][1])
     roof = roofline_of(dominant, work, per[dominant][1] / per[dominant][0])
     others = {nm: roofline_of(nm, work, per[nm][1] / per[nm][0]) for nm in per if nm in work}
+    for nm, w in work.items():  # rooflines of steps that run as several kernels
+        if "parts" in w and all(p in per for p in w["parts"]):
+            others[nm] = roofline_of(nm, work, sum(per[p][1] / per[p][0] for p in w["parts"]))
     credited = sum(w["flops"] for w in work.values())
     layer_ms = ms_per_step / layers
 
