@@ -305,6 +305,8 @@ __device__ __forceinline__ float wave_max_dpp(float v) { return group4_max(row16
 
 // Fast hardware transcendentals (about 1 ulp).
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// max(a, b) for non-NaN inputs (written as the median of a, b and +inf)
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
 __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float hw_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
 __device__ __forceinline__ float hw_rsq(float x) { return __builtin_amdgcn_rsqf(x); }

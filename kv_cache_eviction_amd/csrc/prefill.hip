@@ -34,9 +34,6 @@ __device__ __forceinline__ int xcd_block(int nblk_pad) {
 
 constexpr float kNegBig = -1e30f;  // finite start of a running maximum
 
-// max(a, b) for non-NaN inputs as one v_med3 (the median of a, b and +inf):
-// fmaxf on matrix-core results costs two extra canonicalizing instructions
-__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
 
 template <bool B> using Bool = std::integral_constant<bool, B>;
 
