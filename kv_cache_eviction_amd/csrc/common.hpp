@@ -132,12 +132,12 @@ template <typename T> __device__ __forceinline__ uint32_t bits16(T x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x);
 }
 
-// 16 bytes of Tin converted to Tout and stored as one packed LDS write
-// (8 x bf16 -> 8 x f16, or a plain copy when the types match).
+// 16 bytes of Tin converted to Tout (8 x bf16 -> 8 x f16, or a plain copy
+// when the types match).
 template <typename Tin, typename Tout>
-__device__ __forceinline__ void store_converted16(const U128 &v, Tout *dst) {
+__device__ __forceinline__ U128 convert16(const U128 &v) {
   if constexpr (sizeof(Tin) == sizeof(Tout) && (sizeof(Tin) == 4 || __is_same(Tin, Tout))) {
-    *reinterpret_cast<U128 *>(dst) = v;
+    return v;
   } else if constexpr (__is_same(Tin, bf16) && __is_same(Tout, f16)) {
     // bf16 -> fp32 is a shift; fp32 -> fp16 of a bf16 value is exact in the
     // fp16 normal range, so the round-toward-zero pair conversion (one
@@ -149,7 +149,7 @@ __device__ __forceinline__ void store_converted16(const U128 &v, Tout *dst) {
     for (int e = 0; e < 4; ++e)
       ow[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[e] << 16),
                                                                       __uint_as_float(w[e] & 0xFFFF0000u)));
-    *reinterpret_cast<U128 *>(dst) = o;
+    return o;
   } else {
     const Elems16<Tin> ve = elems16<Tin>(v);
     U128 o;
@@ -158,26 +158,24 @@ __device__ __forceinline__ void store_converted16(const U128 &v, Tout *dst) {
     for (int e = 0; e < 4; ++e)
       ow[e] = bits16(from_f32<Tout>(to_f32(ve.e[2 * e]))) |
               (bits16(from_f32<Tout>(to_f32(ve.e[2 * e + 1]))) << 16);
-    *reinterpret_cast<U128 *>(dst) = o;
+    return o;
   }
 }
 
-// Eight 16-bit values (bf16 or fp16) as eight fp8 e5m2 bytes, clamped to the
-// format's largest finite magnitude, 57344; round to nearest even.
-template <typename Tin>
-__device__ __forceinline__ void store_bf8x8(const U128 &v, uint8_t *dst) {
-  const Elems16<Tin> ve = elems16<Tin>(v);
-  uint32_t w[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    float f[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f[e] = __builtin_amdgcn_fmed3f(to_f32(ve.e[4 * h + e]), -57344.f, 57344.f);
-    int p = __builtin_amdgcn_cvt_pk_bf8_f32(f[0], f[1], 0, false);
-    p = __builtin_amdgcn_cvt_pk_bf8_f32(f[2], f[3], p, true);
-    w[h] = (uint32_t)p;
-  }
-  *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+// ... and stored as one packed LDS write
+template <typename Tin, typename Tout>
+__device__ __forceinline__ void store_converted16(const U128 &v, Tout *dst) {
+  *reinterpret_cast<U128 *>(dst) = convert16<Tin, Tout>(v);
+}
+
+// Eight fp16 values (one 16-byte chunk) as eight fp8 e5m2 bytes: e5m2 has
+// fp16's sign and 5-bit exponent, so its byte is the fp16's upper byte (the
+// mantissa rounded toward zero, subnormals included, and fp16's largest
+// finite value maps to e5m2's, 57344).  v_perm_b32 picks bytes 1 and 3 of
+// each of two words: one instruction per four elements.
+__device__ __forceinline__ uint2 e5m2_of_f16x8(const U128 &h) {
+  return make_uint2(__builtin_amdgcn_perm(h.y, h.x, 0x07050301u),
+                    __builtin_amdgcn_perm(h.w, h.z, 0x07050301u));
 }
 
 // ---- raw buffer loads ----------------------------------------------------------

@@ -637,8 +637,9 @@ vnorm_kernel(const Tin *__restrict__ V, const typename ValueType<Tin>::type *__r
 //                  starts at -pi/2, so N - 2*acc = N - 2x + pi; for 16-bit
 //                  inputs y_hi . v runs on fp16 MFMA and y_lo . v as one
 //                  block-scaled fp8 MFMA (y_lo e4m3 with its row's power-of-
-//                  two scale, v e5m2): y_lo is about 2^-11 of y, so the fp8
-//                  roundings stay near 2^-15 of x;
+//                  two scale, v e5m2 taken as the upper byte of its fp16
+//                  value): y_lo is about 2^-11 of y, so the fp8 roundings
+//                  stay near 2^-14 of x;
 //                  sqrt(q2)/(1+eps-a) is formed as |q2| * rsqrt(|q2| (1+eps-a)^2
 //                  + FLT_MIN).  N - 2x + pi = (v-o)^T G~ (v-o) >= 0 in exact
 //                  arithmetic; it goes negative only by rounding when v ~ o,
@@ -808,9 +809,13 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
       if (ITEMS % NT == 0 || idx < ITEMS) {
         const int row = idx / CPR, ch = idx % CPR;
         *reinterpret_cast<U128 *>(&Ks[buf][row * KROW + ch * EPC]) = pk[u];
-        if (MODE == 0) store_converted16<Tin, TV>(pv[u], &Vs[buf][row * VROW + ch * EPC]);
-        if constexpr (SPLIT_Y)  // 8 fp8 bytes: half ch % 2 of 16-byte chunk ch / 2
-          store_bf8x8<Tin>(pv[u], &V8s[buf][row * V8ROW + ((((ch >> 1) ^ (row & 1)) << 4) | ((ch & 1) << 3))]);
+        if (MODE == 0) {
+          const U128 hv = convert16<Tin, TV>(pv[u]);
+          *reinterpret_cast<U128 *>(&Vs[buf][row * VROW + ch * EPC]) = hv;
+          if constexpr (SPLIT_Y)  // 8 fp8 bytes: half ch % 2 of 16-byte chunk ch / 2
+            *reinterpret_cast<uint2 *>(&V8s[buf][row * V8ROW + ((((ch >> 1) ^ (row & 1)) << 4) | ((ch & 1) << 3))]) =
+                e5m2_of_f16x8(hv);
+        }
       }
     }
     if (MODE == 0) Ns[buf][wv][lane] = pn;
@@ -940,6 +945,7 @@ score_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__
   prefetch(t_begin);
   stash(0);
   __syncthreads();
+#pragma clang loop unroll(disable)
   for (int it = 0; it < nt; ++it) {
     const int t0 = t_begin + it * TN;
     const int cur = it & 1;
