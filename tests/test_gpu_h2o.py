@@ -249,3 +249,32 @@ def test_decode_without_output_keeps_the_same_cache(dev, dtype, d):
             a, b = getattr(caches[0], name), getattr(caches[1], name)
             assert torch.equal(a, b), "step %d: %s differs without the output" % (s, name)
     assert bool((caches[1].O == 7).all())
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64), ("f16", 128)])
+@pytest.mark.parametrize("P", [1, 2, 63, 64, 65, 127, 129, 300, 1000])
+def test_prefill_accumulate_block_edges(dev, dtype, d, P):
+    """The causal prompt accumulate alone at prompt lengths around the 64-row
+    blocks, where the 16-bit kernels pair block p with block nb-1-p (nb = 1,
+    2, 3 and ragged last blocks, odd and even nb): acc against the oracle's
+    column sums, and two calls bit-identical (rows are added in a fixed
+    order)."""
+    b, h = 2, 3
+    g = torch.Generator().manual_seed(1000 + P)
+    Qp = torch.randn(b, h, P, d, generator=g)
+    Kp = torch.randn(b, h, P, d, generator=g)
+    Kp[:, :, ::7] *= 3.0  # a few heavy keys
+    dt = TORCH_DTYPES[dtype]
+    Qd, Kd = Qp.to(dt).to(dev), Kp.to(dt).to(dev)
+    desc = kv.h2o_desc(batch=b, heads=h, d=d, cap=P, dtype=dt)
+    ws = torch.empty(max(1, kv.kvs_h2o_workspace_bytes(desc, kv.KVS_H2O_PREFILL)), dtype=torch.uint8,
+                     device=dev)
+    accs = []
+    for _ in range(2):
+        acc = torch.full((b, h, P), float("nan"), dtype=torch.float32, device=dev)
+        kv.kvscore_h2o_accumulate(desc, kv.KVS_H2O_PREFILL, Qd, Kd, acc=acc, ws=ws)
+        torch.cuda.synchronize()
+        accs.append(acc.cpu())
+    ref = oracle.h2o_prefill_acc(Qd.cpu().double(), Kd.cpu().double())
+    np.testing.assert_allclose(accs[0].double().numpy(), ref, rtol=ACC_RTOL, atol=ACC_ATOL)
+    assert torch.equal(accs[0], accs[1])
