@@ -133,8 +133,9 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
   const U128 vq = *reinterpret_cast<const U128 *>(v_new + row * D + sub * EPC);
 
   // slot map and accumulators into LDS, eight 64-slot blocks per lane loaded
-  // together; lowest free slot, and how many slots hold a token
-  int ws = -1, nvalid = 0;
+  // together; lowest free slot, how many slots hold a token, and the highest
+  // that does
+  int ws = -1, nvalid = 0, top = -1;
   for (int base = 0; base < cap; base += 64 * 8) {
     int pv[8];
     float av[8];
@@ -156,6 +157,7 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
       const unsigned long long vb = __ballot(s < cap && pv[u] >= 0);
       nvalid += __popcll(vb);
       if (ws < 0 && fb) ws = base + 64 * u + __ffsll((long long)fb) - 1;
+      if (vb) top = base + 64 * u + 63 - __clzll((long long)vb);
     }
   }
   wave_lds_sync();
@@ -168,6 +170,15 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
     if (lane == 0 && evict_slot) evict_slot[row] = -2;
     return;
   }
+
+  // Slots at or above `hi` hold nothing and are not the new token's, so the
+  // passes over the slots stop at the batch that covers hi - 1: with the
+  // lowest free slot taking each new token and at most one eviction a step,
+  // the occupied slots stay a prefix with at most one hole, and a cache that
+  // is still filling skips its free tail.  prob[] is written for every slot
+  // below hiS and read only there.
+  const int hi = max(top, ws) + 1;
+  const int hiS = min(cap, (hi + STEP - 1) / STEP * STEP);
 
   // the query unpacked (unused for fp16, whose FMAs read the packed chunk)
   float qv[EPC];
@@ -191,7 +202,7 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
   // logits of every valid slot; the new token's slot, whose load is skipped,
   // takes its key from registers
   U128 cur[U];
-  for (int base = 0; base < cap; base += STEP) {
+  for (int base = 0; base < hiS; base += STEP) {
     load_batch(cur, rk, base, true);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -210,13 +221,13 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
   load_batch(cur, rv, 0, O != nullptr);
 
   float mx = -INFINITY;
-  for (int s = lane; s < cap; s += 64) mx = fmaxf(mx, prob[s]);
+  for (int s = lane; s < hiS; s += 64) mx = fmaxf(mx, prob[s]);
   mx = wave_max_dpp(mx);
   float l = 0.f;
-  for (int s = lane; s < cap; s += 64) l += hw_exp2(prob[s] - mx);
+  for (int s = lane; s < hiS; s += 64) l += hw_exp2(prob[s] - mx);
   l = wave_sum_dpp(l);
   const float inv = 1.f / l;
-  for (int s = lane; s < cap; s += 64) {
+  for (int s = lane; s < hiS; s += 64) {
     const bool valid = (s == ws) || pos_s[s] >= 0;
     float a = 0.f;
     if (valid) {
@@ -233,12 +244,12 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
     float ov[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) ov[e] = 0.f;
-    for (int base = 0; base < cap; base += STEP) {
+    for (int base = 0; base < hiS; base += STEP) {
       if (base > 0) load_batch(cur, rv, base, true);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int s = base + u * RPI + rr;
-        const float a = s < cap ? prob[s] : 0.f;
+        const float a = s < hiS ? prob[s] : 0.f;
         axpy16<T>(a, s == ws ? vq : cur[u], ov);
       }
     }
