@@ -29,15 +29,29 @@
 
 namespace kvs {
 
-// Last key row r of virtual head hv sees (-1: none).  Mode 2 (counter-causal):
-// virtual head hv = (query head in the group) * nq + block, row position
-// R = block * 64 + r sees keys R+1 .. n-1, so the last position sees none.
-// The counter-causal forms (REV) are compiled only into the kernels launched
-// with mode 2.
+// Mode 2 (counter-causal): virtual head hv = (query head in the group) * nq
+// + j, and j names 64-row block rev_block(j): row position R = block * 64 + r
+// sees keys R+1 .. n-1, so early blocks see most of the cache and late ones
+// little.  A workgroup takes four consecutive virtual heads, the 2 x 4 waves
+// two per head, and wave w runs on SIMD w % 4.  The blocks are laid out so
+// that each group of four j holds two early and two late blocks, in the
+// order (a, a+1, n_b-1-a, n_b-2-a): every workgroup then carries about the
+// same work, and every SIMD pairs a wave of an early block with one of a
+// late block, so a SIMD whose short wave has finished still has a long one.
+// (The zigzag 0, n_b-1, 1, n_b-2, ... with the middle two of each full group
+// of four swapped; a bijection on the n_b blocks.)
+__device__ __forceinline__ int rev_block(const RowGeom &g, int hv) {
+  const int nb = g.nq, j = hv % nb;
+  const int q = (j < nb - nb % 4 && (j & 3) == 1) ? j + 1 : (j < nb - nb % 4 && (j & 3) == 2) ? j - 1 : j;
+  return (q & 1) ? nb - 1 - (q >> 1) : (q >> 1);
+}
+
+// Last key row r of virtual head hv sees (-1: none).  The counter-causal
+// forms (REV) are compiled only into the kernels launched with mode 2.
 template <bool REV>
 __device__ __forceinline__ int row_last(const RowGeom &g, int hv, int r) {
   if constexpr (REV) {
-    const int R = (hv % g.nq) * 64 + r;
+    const int R = rev_block(g, hv) * 64 + r;
     return R < g.n - 1 ? g.n - 1 : -1;
   }
   if (g.mode == 0) {
@@ -51,7 +65,7 @@ __device__ __forceinline__ int row_last(const RowGeom &g, int hv, int r) {
 // First key row r of virtual head hv sees (mode 2 only; 0 otherwise).
 template <bool REV>
 __device__ __forceinline__ int row_first(const RowGeom &g, int hv, int r) {
-  if constexpr (REV) return (hv % g.nq) * 64 + r + 1;
+  if constexpr (REV) return rev_block(g, hv) * 64 + r + 1;
   return 0;
 }
 
@@ -59,7 +73,7 @@ __device__ __forceinline__ int row_first(const RowGeom &g, int hv, int r) {
 template <bool REV>
 __device__ __forceinline__ long q_row(const RowGeom &g, int b, int h_kv, int kvh, int hv, int r) {
   if constexpr (REV)  // Q [b][h_q][n][d], query head kvh * G + hv / nq
-    return (((long)b * h_kv + kvh) * (g.group / g.nq) + hv / g.nq) * g.n + (long)(hv % g.nq) * 64 + r;
+    return (((long)b * h_kv + kvh) * (g.group / g.nq) + hv / g.nq) * g.n + (long)rev_block(g, hv) * 64 + r;
   if (g.mode == 0) return (((long)b * h_kv + kvh) * g.group + hv) * g.nq + r;
   return ((long)b * h_kv + kvh) * g.n + (long)hv * 64 + r;
 }
@@ -271,7 +285,7 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
     int wg_lo = 0x7FFFFFFF;
     for (int h2 = 0; h2 < hpw; ++h2) {
       const int v = hs * hpw + h2;
-      if (v < geo.group) wg_lo = min(wg_lo, (v % geo.nq) * 64 + 1);
+      if (v < geo.group) wg_lo = min(wg_lo, rev_block(geo, v) * 64 + 1);
     }
     if (wg_lo > t_begin) it0 = min(nt, (wg_lo - t_begin) / TN);
   }
@@ -414,7 +428,7 @@ attn_partial_kernel(const Tin *__restrict__ Q, const Tin *__restrict__ K, const 
       for (int qb = 0; qb < QBW; ++qb) {
         const float fix = (mtop[qb] == -INFINITY) ? 1.f : hw_exp2(mref[qb] - mtop[qb]);
         const float l = group4_sum(lsum[qb] * fix);
-        const int pos = (hv % geo.nq) * 64 + (qb0 + qb) * 16 + col;
+        const int pos = rev_block(geo, hv) * 64 + (qb0 + qb) * 16 + col;
         if (pos < n) {
           const long orow = ohead * n + pos;
           if (grp == 0) {
