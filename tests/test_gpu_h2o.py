@@ -296,3 +296,13 @@ def test_prefill_accumulate_longest_prompt(dev):
     torch.cuda.synchronize()
     ref = oracle.h2o_prefill_acc(Qd.cpu().double(), Kd.cpu().double())
     np.testing.assert_allclose(acc.cpu().double().numpy(), ref, rtol=ACC_RTOL, atol=ACC_ATOL)
+
+
+def test_widest_cache_lockstep(dev):
+    """The widest slot cache the decode takes (2048 slots: two rows per
+    workgroup, each row's arrays 24 KB of LDS), prompt 2054 tokens, budget
+    95% of the length, 100 steps in lockstep."""
+    cfg = OPT30B_H2O.with_(name="widest", batch=1, heads=2, d=128, prompt=2054, steps=100,
+                           heavy_frac=0.50, recent_frac=0.45, seed=35)
+    assert cfg.cap == 2048
+    run_lockstep(cfg, dev, list(range(2)), cfg.steps)
