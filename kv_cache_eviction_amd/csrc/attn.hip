@@ -491,7 +491,10 @@ attn_combine_lore_kernel(const float *__restrict__ pm, const float *__restrict__
   const float *hm = pm + head * splits * 64;
   const float *hl = pl + head * splits * 64;
   const float *ho = pO + (head * splits * (long)D + d) * 64 + q;  // split stride D * 64
-  constexpr int SPT = 32;          // splits per thread in the weight phase (splits <= 128)
+  // splits per thread held in registers in the weight phase (every fourth
+  // split: up to 32 splits); further splits are read again in a loop.  Few
+  // registers keep four waves per SIMD, so the grid runs in one round.
+  constexpr int SPT = 8;
   float ov[CH], mv[SPT], lv[SPT];
 #pragma unroll
   for (int u = 0; u < CH; ++u) ov[u] = u < splits ? ho[(long)u * D * 64] : 0.f;
@@ -504,6 +507,7 @@ attn_combine_lore_kernel(const float *__restrict__ pm, const float *__restrict__
   float mloc = -INFINITY;
 #pragma unroll
   for (int u = 0; u < SPT; ++u) mloc = fmaxf(mloc, mv[u]);
+  for (int s = part + 4 * SPT; s < splits; s += 4) mloc = fmaxf(mloc, hm[s * 64 + q]);
   pmax[part * 64 + q] = mloc;
   __syncthreads();
   const float M = fmaxf(fmaxf(pmax[q], pmax[64 + q]), fmaxf(pmax[128 + q], pmax[192 + q]));
@@ -517,6 +521,11 @@ attn_combine_lore_kernel(const float *__restrict__ pm, const float *__restrict__
       wsh[s * 64 + q] = wgt;
       lloc += lv[u] * wgt;
     }
+  }
+  for (int s = part + 4 * SPT; s < splits; s += 4) {
+    const float wgt = exp2f(hm[s * 64 + q] - muse);
+    wsh[s * 64 + q] = wgt;
+    lloc += hl[s * 64 + q] * wgt;
   }
   psum[part * 64 + q] = lloc;
   __syncthreads();
