@@ -362,6 +362,15 @@ prep_mfma_kernel(const f16 *__restrict__ Gv, const float *__restrict__ O,
   const f16 *G = Gv + (long)h * D * D;
   // A operand: lane (col, grp) holds o[16w + col][32 ks + 8 grp + e]
   const int ra = wv * 16 + col;
+  // the row constants' inputs are requested first, so their loads are not a
+  // round trip of their own after the products
+  const int rc = wv * 16 + 4 * grp + (col & 3);
+  float rmax = 0.f, rsum = 1.f, om = 0.f;
+  if (col < 4 && rc < nq) {
+    rmax = row_max[hb * nq + rc];
+    rsum = row_sum[hb * nq + rc];
+    if (rc >= w) om = omega[(long)b * m + (rc - w) / t];
+  }
   float oa[KS][8];
   float amax = 0.f;
 #pragma unroll
@@ -455,12 +464,12 @@ prep_mfma_kernel(const f16 *__restrict__ Gv, const float *__restrict__ O,
     float beta2 = 0.f, wr = 0.f;
     int last = -1;
     if (r < nq) {
-      beta2 = row_max[hb * nq + r] * kLog2e + log2f(row_sum[hb * nq + r]);
+      beta2 = rmax * kLog2e + log2f(rsum);
       if (r < w) {
         wr = 1.f / (float)w;
         last = n - w + r;
       } else {
-        wr = lambda_l * omega[(long)b * m + (r - w) / t] / (float)t;
+        wr = lambda_l * om / (float)t;
         last = n - 1;
       }
     }

@@ -150,8 +150,33 @@ topb_local_kernel(const float *__restrict__ S, int n, int n_sink, int w, int chu
   // pooling: chunk c holds tokens [c*chunk, c*chunk + chunk); its key is the
   // order key of the mean over its candidates (0 when it has none)
   int toks = 0;
+  // Chunks of 4 tokens wholly inside the candidate range (all but the ones
+  // at the sink and the window) are read as one 16-byte load each, the
+  // thread's four loads issued together; the sum keeps the token order, so
+  // the pooled value is the same as the general loop's.
+  const int tt0 = (c0 + 4 * (int)threadIdx.x) * chunk;
+  const bool whole4 = chunk == 4 && 4 * (int)threadIdx.x + 3 < items && tt0 >= lo &&
+                      tt0 + 16 <= hi && ((reinterpret_cast<uintptr_t>(Sr + tt0) & 15) == 0) &&
+                      (!pooled || (reinterpret_cast<uintptr_t>(pooled + row * n + tt0) & 15) == 0);
+  if (whole4) {
+    float4 sv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sv[k] = reinterpret_cast<const float4 *>(Sr + tt0)[k];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = 4 * threadIdx.x + k;
+      const float P = (((sv[k].x + sv[k].y) + sv[k].z) + sv[k].w) / 4.f;
+      const uint32_t key = order_key(P);
+      keys_ws[row * nchunks + c0 + i] = key;
+      if (pooled)
+        reinterpret_cast<float4 *>(pooled + row * n + tt0)[k] = make_float4(P, P, P, P);
+      seg_keys[i] = key;
+    }
+    toks = 16;
+  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
+    if (whole4) break;
     const int i = 4 * threadIdx.x + k;
     uint32_t key = 0;
     if (i < items) {
