@@ -126,3 +126,36 @@ def test_retention_shift_matches_oracle(dev, budget):
         assert np.all(ref == 0)
     else:
         assert np.all(ref > 0)
+
+
+@pytest.mark.parametrize("s_off,p_off", [(0, 0), (1, 0), (0, 3), (2, 1)])
+def test_pooled_output_and_misaligned_buffers(dev, s_off, p_off):
+    """Scores and pooled output as views that start s_off / p_off floats into
+    a larger buffer (4-byte but not 16-byte aligned when nonzero): the pooling
+    reads whole 4-token chunks with 16-byte loads only where both buffers
+    allow it, so every alignment must give the oracle's kept set and its
+    pooled scores (chunk means of the same fp32 scores, summed in token
+    order, hence equal to fp32 rounding of the fp64 mean)."""
+    g = torch.Generator().manual_seed(76 + 4 * s_off + p_off)
+    b, hk, n, n_sink, w, chunk, budget = 1, 3, 9001, 1, 32, 4, 300
+    S = torch.rand(b, hk, n, generator=g) ** 3
+    desc = kv.lore_desc(batch=b, n=n, h_q=hk, h_kv=hk, d=128, d_model=1, w=w, m=0, t=0,
+                        n_sink=n_sink, chunk=chunk, budget=budget)
+    ws = torch.empty(kv.kvs_topb_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    kept = torch.empty(b, hk, desc.n_keep, dtype=torch.int32, device=dev)
+    sbuf = torch.empty(b * hk * n + 8, device=dev)
+    pbuf = torch.full((b * hk * n + 8,), 7.0, device=dev)
+    Sd = sbuf[s_off:s_off + b * hk * n].view(b, hk, n)
+    Pd = pbuf[p_off:p_off + b * hk * n].view(b, hk, n)
+    Sd.copy_(S.to(dev))
+    kv.kvscore_topb_select(desc, Sd, kept, Pd, ws)
+    torch.cuda.synchronize()
+    ko, po = oracle.topb_select(S.double().numpy(), n_sink=n_sink, w=w, chunk=chunk, budget=budget)
+    check_kept(kept.cpu().numpy(), ko, po, n_sink, w, budget)
+    pg = Pd.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isnan(pg), np.isnan(po)), "pooled NaNs differ from the protected set"
+    fin = ~np.isnan(po)
+    assert np.all(np.abs(pg[fin] - po[fin]) <= 1e-6 * np.abs(po[fin]) + 1e-37)
+    # nothing outside the view was written
+    rest = torch.cat([pbuf[:p_off], pbuf[p_off + b * hk * n:]]).cpu()
+    assert torch.all(rest == 7.0)
