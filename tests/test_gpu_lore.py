@@ -90,6 +90,13 @@ SMALL = [
                d_model=512, seed=15),
     TINY.with_(name="bf16-d128-g16-n600", dtype="bf16", d=128, h_q=16, h_kv=1, n=600,
                d_model=2048, budget=30, seed=16, window_from_facts=False),
+    # one KV head over a long cache: pass 1 runs 79 (and 40) token splits, so
+    # the merge holds 8 split weights per thread in registers and reads the
+    # rest again, and takes the partial O in several rounds of 32
+    TINY.with_(name="bf16-d128-g4-n40000-79splits", dtype="bf16", d=128, h_q=4, h_kv=1,
+               n=40000, d_model=512, budget=200, seed=19),
+    TINY.with_(name="f16-d64-g2-n20000-40splits", dtype="f16", d=64, h_q=2, h_kv=1, n=20000,
+               d_model=128, budget=100, seed=20),
 ]
 
 
