@@ -89,6 +89,13 @@ __device__ __forceinline__ void axpy16(float a, const U128 &b, float (&o)[16 / s
   }
 }
 
+// x * y rounded to fp32 and never fused into a following add, so a product
+// used by two code paths gives both the same sums.
+__device__ __forceinline__ float mul_rounded(float x, float y) {
+#pragma clang fp contract(off)
+  return x * y;
+}
+
 __device__ __forceinline__ uint32_t order_key_pos(float x) {
   const uint32_t u = __float_as_uint(x + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -200,8 +207,10 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
   };
 
   // logits of every valid slot; the new token's slot, whose load is skipped,
-  // takes its key from registers
+  // takes its key from registers.  The row maximum is kept in registers on
+  // the way, so the softmax needs no pass of its own for it.
   U128 cur[U];
+  float mx = -INFINITY;
   for (int base = 0; base < hiS; base += STEP) {
     load_batch(cur, rk, base, true);
 #pragma unroll
@@ -211,33 +220,31 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
       const bool valid = inb && (s == ws || pos_s[s] >= 0);
       float part = dot16<T>(qq, qv, s == ws ? kq : cur[u], 0.f);
       part = lane_group_sum<LPR>(part);
-      if (sub == 0 && inb) prob[s] = valid ? part * c : -INFINITY;
+      const float lg = valid ? part * c : -INFINITY;
+      mx = fmaxf(mx, lg);
+      if (sub == 0 && inb) prob[s] = lg;
     }
   }
+  mx = wave_max_dpp(mx);
   wave_lds_sync();
   // the first batch of value rows is in flight during the softmax: issued
   // after the LDS fence, and without a branch on O (no output: nothing is
   // read), so no wait for it is placed before the softmax
   load_batch(cur, rv, 0, O != nullptr);
 
-  float mx = -INFINITY;
-  for (int s = lane; s < hiS; s += 64) mx = fmaxf(mx, prob[s]);
-  mx = wave_max_dpp(mx);
+  // one pass forms the exponentials (kept in prob[]) and their sum; the
+  // probabilities a = e / l are formed where they are used, in the pass over
+  // the value rows and in the accumulator pass.  a is a rounded product
+  // (never contracted into the accumulator's add), so a step with and one
+  // without the output leave the same accumulators.
   float l = 0.f;
-  for (int s = lane; s < hiS; s += 64) l += hw_exp2(prob[s] - mx);
+  for (int s = lane; s < hiS; s += 64) {
+    const float e = hw_exp2(prob[s] - mx);
+    prob[s] = e;
+    l += e;
+  }
   l = wave_sum_dpp(l);
   const float inv = 1.f / l;
-  for (int s = lane; s < hiS; s += 64) {
-    const bool valid = (s == ws) || pos_s[s] >= 0;
-    float a = 0.f;
-    if (valid) {
-      a = hw_exp2(prob[s] - mx) * inv;
-      const float na = ((s == ws) ? 0.f : acc_s[s]) + a;
-      acc_s[s] = na;
-      ac[s] = na;
-    }
-    prob[s] = a;
-  }
   wave_lds_sync();
 
   if (O) {
@@ -249,7 +256,7 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int s = base + u * RPI + rr;
-        const float a = s < hiS ? prob[s] : 0.f;
+        const float a = s < hiS ? mul_rounded(prob[s], inv) : 0.f;
         axpy16<T>(a, s == ws ? vq : cur[u], ov);
       }
     }
@@ -270,18 +277,26 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
   }
   if (lane == 0) pos[ws] = newpos;
 
-  int ev = -1;
-  if (nvalid + 1 > k_heavy + k_recent) {
-    const int recent_from = cur_len - k_recent;
-    unsigned long long best = ~0ull;
-    for (int s = lane; s < cap; s += 64) {
-      const int p = (s == ws) ? newpos : pos_s[s];
-      if (p >= 0 && p < recent_from) {
-        const unsigned long long key =
-            ((unsigned long long)order_key_pos(acc_s[s]) << 32) | (uint32_t)(0x7FFFFFFF - p);
-        best = key < best ? key : best;
-      }
+  // One pass adds each retained token's probability to its accumulator and,
+  // when the cache is over budget, finds the eviction candidate: the lowest
+  // accumulator outside the recent window, the later position on ties.
+  // Every occupied slot and the new token's lie below hiS.
+  const bool over = nvalid + 1 > k_heavy + k_recent;
+  const int recent_from = cur_len - k_recent;
+  unsigned long long best = ~0ull;
+  for (int s = lane; s < hiS; s += 64) {
+    const int p = (s == ws) ? newpos : pos_s[s];
+    if (p < 0) continue;
+    const float na = ((s == ws) ? 0.f : acc_s[s]) + mul_rounded(prob[s], inv);
+    ac[s] = na;
+    if (over && p < recent_from) {
+      const unsigned long long key =
+          ((unsigned long long)order_key_pos(na) << 32) | (uint32_t)(0x7FFFFFFF - p);
+      best = key < best ? key : best;
     }
+  }
+  int ev = -1;
+  if (over) {
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const unsigned long long other = __shfl_xor(best, o, 64);
@@ -290,7 +305,7 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
     if (best != ~0ull) {
       const int pev = 0x7FFFFFFF - (int)(uint32_t)(best & 0xFFFFFFFFull);
       int cand = -1;
-      for (int s = lane; s < cap; s += 64) {
+      for (int s = lane; s < hiS; s += 64) {
         const int p = (s == ws) ? newpos : pos_s[s];
         if (p == pev) cand = s;
       }
