@@ -234,9 +234,10 @@ h2o_decode_kernel(const T *__restrict__ q, T *__restrict__ K, T *__restrict__ V,
 
   // one pass forms the exponentials (kept in prob[]) and their sum; the
   // probabilities a = e / l are formed where they are used, in the pass over
-  // the value rows and in the accumulator pass.  a is a rounded product
-  // (never contracted into the accumulator's add), so a step with and one
-  // without the output leave the same accumulators.
+  // the value rows and in the accumulator pass (the same code with and
+  // without the output, so both leave the same accumulators).  a is a
+  // rounded product, never contracted into the accumulator's add, so the
+  // value pass and the accumulators use the same a.
   float l = 0.f;
   for (int s = lane; s < hiS; s += 64) {
     const float e = hw_exp2(prob[s] - mx);
