@@ -34,6 +34,9 @@
  *    is available from kvs_last_error() (thread-local).  Nothing aborts or
  *    prints.
  *  - Outputs must not alias inputs unless an argument says it is in/out.
+ *  - Sequences x heads (batch * h_kv, batch * heads) and the query heads h_q
+ *    of one call are at most 65535: each indexes one grid dimension of a
+ *    launch.  More returns KVS_ERR_UNSUPPORTED.
  *  - Calls on one stream run in order; calls on different streams that share
  *    a workspace race.
  */

@@ -45,6 +45,15 @@ kvs_status hip_status(hipError_t e, const char *what) {
 
 size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
+// Sequences x heads (and the query heads of a layer) index one grid
+// dimension of the scoring, selection and compaction launches, which holds
+// at most 65535 workgroups.
+constexpr long kMaxRows = 65535;
+kvs_status check_rows(long rows, const char *what) {
+  if (rows > kMaxRows) return fail(KVS_ERR_UNSUPPORTED, std::string(what) + " above 65535");
+  return KVS_OK;
+}
+
 int n_pad_of(int n) { return (n + 63) / 64 * 64; }
 
 // Plans of the LORE workspace; every entry point lays out its scratch from
@@ -63,6 +72,8 @@ kvs_status check_lore(const kvs_lore_desc *d) {
   if (!d) return fail(KVS_ERR_INVALID, "descriptor is NULL");
   if (d->batch < 1 || d->n < 1 || d->h_q < 1 || d->h_kv < 1 || d->d_model < 1)
     return fail(KVS_ERR_INVALID, "batch, n, h_q, h_kv and d_model must be >= 1");
+  if (check_rows((long)d->batch * d->h_kv, "batch * h_kv") != KVS_OK) return KVS_ERR_UNSUPPORTED;
+  if (check_rows(d->h_q, "h_q") != KVS_OK) return KVS_ERR_UNSUPPORTED;
   if (d->h_q % d->h_kv != 0) return fail(KVS_ERR_INVALID, "h_q must be a multiple of h_kv");
   if (d->h_q / d->h_kv > 16) return fail(KVS_ERR_UNSUPPORTED, "query-head group larger than 16");
   if (d->d != 64 && d->d != 128) return fail(KVS_ERR_UNSUPPORTED, "head dim must be 64 or 128");
@@ -117,6 +128,7 @@ kvs_status check_select(const kvs_lore_desc *d) {
   if (!d) return fail(KVS_ERR_INVALID, "descriptor is NULL");
   if (d->batch < 1 || d->h_kv < 1 || d->n < 1)
     return fail(KVS_ERR_INVALID, "batch, h_kv and n must be >= 1");
+  if (check_rows((long)d->batch * d->h_kv, "batch * h_kv") != KVS_OK) return KVS_ERR_UNSUPPORTED;
   if (d->n_sink < 0 || d->w < 0 || d->budget < 0)
     return fail(KVS_ERR_INVALID, "n_sink, w and budget must be >= 0");
   if ((long)d->n_sink + d->w > d->n) return fail(KVS_ERR_INVALID, "n must be >= n_sink + w");
@@ -296,6 +308,8 @@ kvs_status check_fidelity(const kvs_lore_desc *d, int n_f, int n_keep) {
   if (!d) return fail(KVS_ERR_INVALID, "descriptor is NULL");
   if (d->batch < 1 || d->n < 1 || d->h_q < 1 || d->h_kv < 1)
     return fail(KVS_ERR_INVALID, "batch, n, h_q and h_kv must be >= 1");
+  if (check_rows((long)d->batch * d->h_kv, "batch * h_kv") != KVS_OK) return KVS_ERR_UNSUPPORTED;
+  if (check_rows(d->h_q, "h_q") != KVS_OK) return KVS_ERR_UNSUPPORTED;
   if (d->h_q % d->h_kv != 0) return fail(KVS_ERR_INVALID, "h_q must be a multiple of h_kv");
   if (d->h_q / d->h_kv > 16) return fail(KVS_ERR_UNSUPPORTED, "query-head group larger than 16");
   if (d->d != 64 && d->d != 128) return fail(KVS_ERR_UNSUPPORTED, "head dim must be 64 or 128");
@@ -380,6 +394,8 @@ kvs_status check_counter_causal(const kvs_lore_desc *d) {
   if (!d) return fail(KVS_ERR_INVALID, "descriptor is NULL");
   if (d->batch < 1 || d->n < 1 || d->h_q < 1 || d->h_kv < 1)
     return fail(KVS_ERR_INVALID, "batch, n, h_q and h_kv must be >= 1");
+  if (check_rows((long)d->batch * d->h_kv, "batch * h_kv") != KVS_OK) return KVS_ERR_UNSUPPORTED;
+  if (check_rows(d->h_q, "h_q") != KVS_OK) return KVS_ERR_UNSUPPORTED;
   if (d->h_q % d->h_kv != 0) return fail(KVS_ERR_INVALID, "h_q must be a multiple of h_kv");
   if (d->d != 64 && d->d != 128) return fail(KVS_ERR_UNSUPPORTED, "head dim must be 64 or 128");
   if (d->n > (1 << 22)) return fail(KVS_ERR_UNSUPPORTED, "n above 2^22 tokens");
@@ -432,6 +448,8 @@ KVS_API kvs_status kvscore_refresh(int32_t batch, int32_t heads, int32_t n, int3
                                    int32_t *ids_out, void *ws, size_t ws_bytes, void *stream) {
   if (batch < 1 || heads < 1 || n < 1)
     return fail(KVS_ERR_INVALID, "kvscore_refresh: batch, heads and n must be >= 1");
+  if (check_rows((long)batch * heads, "kvscore_refresh: batch * heads") != KVS_OK)
+    return KVS_ERR_UNSUPPORTED;
   if (n > (1 << 28)) return fail(KVS_ERR_UNSUPPORTED, "kvscore_refresh: n above 2^28 tokens");
   if (d != 64 && d != 128) return fail(KVS_ERR_UNSUPPORTED, "kvscore_refresh: head dim must be 64 or 128");
   if (dtype != KVS_F32 && dtype != KVS_BF16 && dtype != KVS_F16)
@@ -533,6 +551,8 @@ KVS_API kvs_status kv_compact(int32_t batch, int32_t heads, int32_t n_src, int32
     return fail(KVS_ERR_INVALID, "kv_compact: batch, heads, n_src, cap_dst must be >= 1, n_keep >= 0");
   if (n_keep > n_src || n_keep > cap_dst)
     return fail(KVS_ERR_INVALID, "kv_compact: n_keep exceeds n_src or cap_dst");
+  if (check_rows((long)batch * heads, "kv_compact: batch * heads") != KVS_OK)
+    return KVS_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return fail(KVS_ERR_UNSUPPORTED, "kv_compact: head dim must be 64 or 128");
   if (dtype != KVS_F32 && dtype != KVS_BF16 && dtype != KVS_F16)
     return fail(KVS_ERR_INVALID, "kv_compact: unknown dtype");
@@ -559,6 +579,7 @@ kvs_status check_h2o(const kvs_h2o_desc *d, int mode) {
   if (!d) return fail(KVS_ERR_INVALID, "descriptor is NULL");
   if (d->batch < 1 || d->heads < 1 || d->cap < 1)
     return fail(KVS_ERR_INVALID, "batch, heads and cap must be >= 1");
+  if (check_rows((long)d->batch * d->heads, "batch * heads") != KVS_OK) return KVS_ERR_UNSUPPORTED;
   if (d->d != 64 && d->d != 128) return fail(KVS_ERR_UNSUPPORTED, "head dim must be 64 or 128");
   if (d->dtype != KVS_F32 && d->dtype != KVS_BF16 && d->dtype != KVS_F16)
     return fail(KVS_ERR_INVALID, "unknown dtype");

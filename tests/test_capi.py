@@ -57,6 +57,8 @@ def _desc(kv, **kw):
     (dict(eps=float("nan")), 1),
     (dict(lambda_l=-0.5), 1),         # the lookahead weight is nonnegative
     (dict(budget=-1), 1),
+    (dict(batch=32768, h_q=8, h_kv=2), 2),   # 65536 (sequence, KV head) rows
+    (dict(batch=1, h_q=65536, h_kv=4096), 2),  # 65536 query heads
 ])
 def test_bad_descriptor_rejected_before_launch(kw, status):
     kv, lib = _lib()
@@ -224,3 +226,28 @@ def test_probs_mask_checks():
         rc = lib.kvscore_probs(ctypes.byref(d), mask, fake, fake, fake, fake, fake, fake, fake, None,
                                0, None)
         assert rc == status, (mask, kv.last_error())
+
+
+def test_row_limits_of_one_launch():
+    """Sequences x heads index one grid dimension (at most 65535 workgroups):
+    every entry point refuses more before enqueueing anything, and accepts
+    the largest count."""
+    kv, lib = _lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: a host check fails first
+    over = kv.lore_desc(batch=16384, n=1024, h_q=4, h_kv=4, d=128, d_model=1)   # 65536 rows
+    edge = kv.lore_desc(batch=16383, n=1024, h_q=4, h_kv=4, d=128, d_model=1)   # 65532 rows
+    assert lib.kvs_topb_workspace_bytes(ctypes.byref(over)) == 0
+    assert "65535" in kv.last_error()
+    assert lib.kvs_topb_workspace_bytes(ctypes.byref(edge)) > 0
+    assert lib.kvscore_topb_select(ctypes.byref(over), fake, fake, None, fake, 1 << 40, None) == 2
+    assert lib.kvs_fidelity_workspace_bytes(ctypes.byref(over), 8, 100) == 0
+    assert lib.kvscore_counter_causal(ctypes.byref(over), *([fake] * 6), None) == 2
+    assert lib.kv_compact(256, 256, 10, 5, 5, 128, 1, fake, fake, fake, fake, fake, None, None,
+                          None, None) == 2
+    assert lib.kvscore_refresh(256, 256, 640, 128, 1, 16, 64, fake, fake, fake, None, fake, fake,
+                               fake, None, fake, 1 << 40, None) == 2
+    h = kv.h2o_desc(batch=256, heads=256, d=128, cap=300, cur_len=10)
+    assert lib.kvs_h2o_workspace_bytes(ctypes.byref(h), kv.KVS_H2O_PREFILL) == 0
+    rc = lib.kvscore_h2o_accumulate(ctypes.byref(h), kv.KVS_H2O_DECODE, *([fake] * 10), None, 0,
+                                    None)
+    assert rc == 2 and "65535" in kv.last_error()
