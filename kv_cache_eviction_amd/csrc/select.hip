@@ -129,13 +129,15 @@ __device__ __forceinline__ int chunk_tokens(int cj, int chunk, int lo, int hi) {
 // chunks from S (keys for the final pass, pooled scores when asked for), then
 // keeps, in index order, the chunks whose key reaches the 16-bit bin of the
 // segment's own top-B threshold (all of them when the segment holds at most
-// B tokens).
+// B tokens).  A row of one segment (kept != nullptr) is selected here in
+// full: the 4-digit threshold, then the kept list, as the final level would.
 constexpr int kSeg = 1024;
 
 __global__ void __launch_bounds__(256)
 topb_local_kernel(const float *__restrict__ S, int n, int n_sink, int w, int chunk, int nchunks,
                   int B, int nseg, uint32_t *__restrict__ keys_ws, float *__restrict__ pooled,
-                  int32_t *__restrict__ cand, int32_t *__restrict__ cand_n) {
+                  int32_t *__restrict__ cand, int32_t *__restrict__ cand_n,
+                  int32_t *__restrict__ kept, int n_keep) {
   __shared__ int hist[4 * 256];
   __shared__ int scan_sh[5];
   __shared__ uint32_t s_prefix;
@@ -198,6 +200,57 @@ topb_local_kernel(const float *__restrict__ S, int n, int n_sink, int w, int chu
       }
     }
     seg_keys[i] = key;
+  }
+  if (kept) {
+    // one segment holds the whole row: the protected entries, then the top B
+    int32_t *kr = kept + row * n_keep;
+    for (int i = threadIdx.x; i < n_sink; i += blockDim.x) kr[i] = i;
+    for (int i = threadIdx.x; i < w; i += blockDim.x) kr[n_sink + max(B, 0) + i] = n - w + i;
+    if (B <= 0) return;
+    int total;
+    block_exclusive_scan(toks, scan_sh, &total);  // (also orders the seg_keys writes)
+    uint32_t tau = 0;
+    int rem = 0;
+    if (total > B)
+      tau = radix_threshold(
+          items, [&](int i) { return seg_keys[i]; },
+          [&](int i) { return chunk_tokens(c0 + i, chunk, lo, hi); }, B, hist, &s_prefix, &s_rem,
+          &rem);
+    // in index order: chunks above tau whole, tau chunks until rem tokens
+    // (ties to the lower index), as the final level emits them
+    int cnt[4], tcnt = 0;
+    uint32_t key[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = 4 * threadIdx.x + k;
+      cnt[k] = i < items ? max(chunk_tokens(c0 + i, chunk, lo, hi), 0) : 0;
+      key[k] = i < items ? seg_keys[i] : 0u;
+      if (cnt[k] > 0 && key[k] == tau) tcnt += cnt[k];
+    }
+    int dummy;
+    int tb = block_exclusive_scan(tcnt, scan_sh, &dummy);  // tau tokens before this thread
+    int take[4], ntake = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      take[k] = 0;
+      if (cnt[k] > 0) {
+        if (key[k] > tau) {
+          take[k] = cnt[k];
+        } else if (key[k] == tau) {
+          take[k] = min(max(rem - tb, 0), cnt[k]);
+          tb += cnt[k];
+        }
+      }
+      ntake += take[k];
+    }
+    int out = n_sink + block_exclusive_scan(ntake, scan_sh, &dummy);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int a = max((c0 + 4 * (int)threadIdx.x + k) * chunk, lo);
+      for (int t = 0; t < take[k]; ++t, ++out)
+        if (out < n_sink + B) kr[out] = a + t;
+    }
+    return;
   }
   if (B <= 0) return;  // nothing to select: the pooled output was the only work
   int total;
@@ -382,13 +435,16 @@ hipError_t launch_topb(const float *S, int rows, int n, int n_sink, int w, int c
   int32_t *cand_n = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + 2 * al((size_t)rows * nchunks * 4));
   const int n_cand = n - n_sink - w;
   const int B = budget < n_cand ? budget : n_cand;
+  // a row of one segment is selected in full by the first level
+  const bool one = nseg == 1;
   {
     TimedLaunch tl_("topb_local", st);
     hipLaunchKernelGGL(topb_local_kernel, dim3(nseg, rows), dim3(256), 0, st, S, n, n_sink, w,
-                       chunk, nchunks, B, nseg, keys_ws, pooled, cand, cand_n);
+                       chunk, nchunks, B, nseg, keys_ws, pooled, cand, cand_n,
+                       one ? kept : nullptr, n_keep);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || one) return e;
   {
     TimedLaunch tl_("topb_select", st);
     hipLaunchKernelGGL(topb_final_kernel, dim3(rows), dim3(1024), 0, st, n, n_sink, w, chunk,

@@ -83,6 +83,9 @@ def test_budget_covers_all_candidates(dev):
     (70000, 2, 31, 4, 9000),    # large budget: survivors of many segments
     (9000, 0, 1, 1, 777),       # chunk 1 (token-level ranking)
     (20000, 1, 32, 8, 257),     # chunk 8
+    (4096, 1, 32, 4, 300),      # exactly one segment (1024 chunks): selected in the first level
+    (1024, 0, 205, 1, 204),     # the H2O prompt reduction's shape, one segment
+    (1030, 3, 7, 5, 1),         # one segment, one candidate kept from a cut chunk
 ])
 def test_edges(dev, n, n_sink, w, chunk, budget):
     g = torch.Generator().manual_seed(n + budget)
@@ -159,3 +162,18 @@ def test_pooled_output_and_misaligned_buffers(dev, s_off, p_off):
     # nothing outside the view was written
     rest = torch.cat([pbuf[:p_off], pbuf[p_off + b * hk * n:]]).cpu()
     assert torch.all(rest == 7.0)
+
+
+@pytest.mark.parametrize("n,chunk,budget", [(4000, 4, 999), (1024, 1, 205), (600, 3, 100)])
+def test_one_segment_ties_exact(dev, n, chunk, budget):
+    """Rows of one segment are selected in full by the first level.  Scores on
+    a coarse grid with whole chunks (exact chunk means): the kept sets must
+    equal the oracle's exactly, ties at the threshold going to the lower
+    index, including a threshold chunk that is only partly kept."""
+    g = torch.Generator().manual_seed(77 + n)
+    n_sink = chunk  # whole chunks only
+    w = (n - n_sink) % chunk + chunk  # the window ends the candidates on a chunk edge
+    S = torch.randint(0, 6, (2, 3, n), generator=g).float() / 8
+    kept = run_select(dev, S, n_sink, w, chunk, budget)
+    o, _ = oracle.topb_select(S.double().numpy(), n_sink=n_sink, w=w, chunk=chunk, budget=budget)
+    assert np.array_equal(kept, o)
