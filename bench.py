@@ -516,9 +516,8 @@ def main():
                          "known-size kernel that scales HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the scoring path needs no collectives, and this "
-              "build runs on a single MI355X (see the sharding notes). Use --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the scoring path runs on a single MI355X and "
+              "needs no collectives. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
