@@ -28,8 +28,11 @@ hipEvent_t take_event() {
     g_pool.pop_back();
     return e;
   }
+  // timing-only events: without the system-scope fence a default event
+  // performs when it is recorded (an L2 write-back and invalidation), so the
+  // bracket measures the kernel and does not slow the work that follows it
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
