@@ -191,15 +191,18 @@ def test_ragged_prompt_lockstep(dev):
     run_lockstep(cfg, dev, list(range(4)), cfg.steps)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
 @pytest.mark.parametrize("prompt,heavy,recent", [(2048, 0.1, 0.1), (3000, 0.2, 0.1)],
                          ids=["p2048", "p3000-ragged"])
-def test_long_prompt_lockstep(dev, prompt, heavy, recent):
+def test_long_prompt_lockstep(dev, prompt, heavy, recent, dtype):
     """Prompts beyond 1024 tokens (the H2O page's long-sequence runs use 2048
-    and more): the column-sum pass then runs several head-subset launches
-    from the last rows to the first, and the attention pass's workgroups stop
-    at their rows' last key.  P = 3000 is not a multiple of 64."""
+    and more).  16-bit prompts run the paired-block rows and column-sum
+    passes; fp32 prompts the general attention pass, whose column-sum pass
+    then runs several head-subset launches from the last rows to the first
+    while the attention pass's workgroups stop at their rows' last key.
+    P = 3000 is not a multiple of 64."""
     cfg = OPT30B_H2O.with_(name="long", batch=2, heads=3, prompt=prompt, steps=48,
-                           heavy_frac=heavy, recent_frac=recent, seed=35)
+                           heavy_frac=heavy, recent_frac=recent, seed=35, dtype=dtype)
     run_lockstep(cfg, dev, list(range(cfg.batch * cfg.heads)), cfg.steps)
 
 
