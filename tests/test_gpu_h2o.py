@@ -283,16 +283,19 @@ def test_prefill_accumulate_block_edges(dev, dtype, d, P):
     assert torch.equal(accs[0], accs[1])
 
 
-def test_prefill_accumulate_longest_prompt(dev):
-    """The longest prompt the prefill takes (16384 tokens, 128 row-block
-    pairs): acc of one (sequence, head) row against the oracle."""
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_prefill_accumulate_longest_prompt(dev, dt):
+    """The longest prompt the prefill takes (16384 tokens): acc of one
+    (sequence, head) row against the oracle.  16-bit prompts run 128
+    row-block pairs; fp32 prompts the general attention pass and 32
+    column-sum launches."""
     P, d = 16384, 128
     g = torch.Generator().manual_seed(16384)
     Qp = torch.randn(1, 1, P, d, generator=g)
     Kp = torch.randn(1, 1, P, d, generator=g)
     Kp[:, :, ::11] *= 3.0
-    Qd, Kd = Qp.to(torch.bfloat16).to(dev), Kp.to(torch.bfloat16).to(dev)
-    desc = kv.h2o_desc(batch=1, heads=1, d=d, cap=P, dtype=torch.bfloat16)
+    Qd, Kd = Qp.to(dt).to(dev), Kp.to(dt).to(dev)
+    desc = kv.h2o_desc(batch=1, heads=1, d=d, cap=P, dtype=dt)
     ws = torch.empty(kv.kvs_h2o_workspace_bytes(desc, kv.KVS_H2O_PREFILL), dtype=torch.uint8, device=dev)
     acc = torch.full((1, 1, P), float("nan"), dtype=torch.float32, device=dev)
     kv.kvscore_h2o_accumulate(desc, kv.KVS_H2O_PREFILL, Qd, Kd, acc=acc, ws=ws)
