@@ -32,6 +32,32 @@ def test_golden_uniform_keys():
             assert got[p] == pytest.approx(exp[p], rel=1e-13)
 
 
+def test_golden_log_keys():
+    """Non-uniform weights: keys ln(p + 1) under unit queries weigh each token
+    in proportion to p + 1 (hand-derived fractions in the fixture)."""
+    g = golden("h2o_log_keys.json")
+    P, T = g["prompt"], g["steps"]
+    L = P + T
+    Q = np.ones((1, L, 1))
+    K = np.log(np.arange(L, dtype=np.float64) + 1.0).reshape(1, L, 1)
+    V = (np.arange(L, dtype=np.float64) + 1.0).reshape(1, L, 1)
+    ora = oracle.H2OOracle(Q[:, :P], K[:, :P], V[:, :P], g["heavy_frac"], g["recent_frac"], cap=8)
+    np.testing.assert_allclose(ora.prefill_acc[0], g["expected_prefill_acc"], rtol=1e-13)
+    assert sorted(ora.retained(0)) == g["expected_kept_prompt"]
+    for s in range(T):
+        o, _ = ora.attend(Q[:, P + s], K[:, P + s], V[:, P + s])
+        assert o[0, 0] == pytest.approx(g["expected_o"][s], rel=1e-13)
+        slot = ora.choose()
+        pos = int(ora.pos[0, slot[0]]) if slot[0] >= 0 else -1
+        assert pos == g["expected_evicted_pos"][s]
+        ora.evict(slot)
+        exp = {int(k): v for k, v in g["expected_retained_after"][s].items()}
+        got = ora.retained(0)
+        assert sorted(got) == sorted(exp)
+        for p in exp:
+            assert got[p] == pytest.approx(exp[p], rel=1e-13)
+
+
 def test_def22_zero_keys_identity():
     """H2O page, Def. 2.2: zeroing evicted keys and subtracting the spurious
     exp(0) = 1 terms gives the softmax over the retained set."""
