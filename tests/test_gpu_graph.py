@@ -63,3 +63,45 @@ def test_layer_graph_replays_match_eager(dev):
         for a, b in zip((ev.S, ev.kept, Ko, Vo), ref):
             assert torch.equal(a, b), "replay %d differs from the eager run" % rep
     assert not torch.equal(other.S, ev.S)
+
+
+def test_layers_on_concurrent_streams_match_sequential(dev):
+    """Two layers enqueued on two streams at once, each with its own buffers
+    and workspace, give bit-for-bit the results of running them one after the
+    other: the library keeps no state between calls that concurrent streams
+    could share (the stream argument is passed through the binding)."""
+    cfg = TINY.with_(name="streams-bf16", dtype="bf16", d=128, h_q=8, h_kv=2, n=5000,
+                     d_model=512, budget=120, seed=72)
+    desc = kv.lore_desc(dtype=TORCH_DTYPES[cfg.dtype], **lore_desc_kwargs(cfg))
+    xs = [{k: v.to(dev).contiguous() for k, v in lore_inputs(cfg, l, device=dev).items()}
+          for l in range(2)]
+    evs = [kv.LoreEviction(desc, dev) for _ in range(2)]
+    outs = [(torch.empty(cfg.batch, cfg.h_kv, desc.n_keep, cfg.d, dtype=xs[0]["K"].dtype, device=dev),
+             torch.empty(cfg.batch, cfg.h_kv, desc.n_keep, cfg.d, dtype=xs[0]["K"].dtype, device=dev))
+            for _ in range(2)]
+
+    def run(i, stream=None):
+        x, (Ko, Vo) = xs[i], outs[i]
+        evs[i].run(x["Q"], x["K"], x["V"], x["W_O"], x["omega"], Ko, Vo, stream=stream)
+
+    for i in range(2):
+        run(i)
+    torch.cuda.synchronize()
+    ref = [[t.clone() for t in (evs[i].S, evs[i].kept, *outs[i])] for i in range(2)]
+    for rep in range(3):
+        for i in range(2):
+            for t in (evs[i].S, *outs[i]):
+                t.zero_()
+            evs[i].kept.fill_(-1)
+        torch.cuda.synchronize()
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        for s in streams:
+            s.wait_stream(torch.cuda.current_stream())
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                run(i, stream=streams[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            got = (evs[i].S, evs[i].kept, *outs[i])
+            for a, b in zip(got, ref[i]):
+                assert torch.equal(a, b), "rep %d: layer %d differs on concurrent streams" % (rep, i)
