@@ -312,3 +312,40 @@ def test_widest_cache_lockstep(dev):
                            heavy_frac=0.50, recent_frac=0.45, seed=35)
     assert cfg.cap == 2048
     run_lockstep(cfg, dev, list(range(2)), cfg.steps)
+
+
+def test_decode_on_concurrent_streams_matches_sequential(dev):
+    """Two slot caches stepped on two streams at once give bit for bit what
+    stepping them one after the other gives: the decode keeps no state
+    outside the caller's buffers."""
+    cfg = OPT30B_H2O.with_(name="streams", batch=2, heads=3, prompt=300, steps=40, seed=37)
+    dt = TORCH_DTYPES[cfg.dtype]
+    inps = [h2o_inputs(cfg.with_(seed=37 + i), device="cpu") for i in range(2)]
+
+    def fresh():
+        cs = [kv.H2OCache(cfg.batch, cfg.heads, cfg.d, cfg.cap, dt, cfg.heavy_frac,
+                          cfg.recent_frac, dev) for _ in range(2)]
+        for c, inp in zip(cs, inps):
+            c.prefill(*(inp[k].to(dev) for k in ("Qp", "Kp", "Vp")))
+        torch.cuda.synchronize()
+        return cs
+
+    seq, con = fresh(), fresh()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in range(cfg.steps):
+        step_in = [tuple(inp[x][s].to(dev) for x in ("q", "k", "v")) for inp in inps]
+        for c, (q, k, v) in zip(seq, step_in):
+            c.step(q, k, v)
+        outs_seq = [c.O.clone() for c in seq]
+        torch.cuda.synchronize()
+        for st in streams:
+            st.wait_stream(torch.cuda.current_stream())
+        for c, (q, k, v), st in zip(con, step_in, streams):
+            with torch.cuda.stream(st):
+                c.step(q, k, v, stream=st)
+        torch.cuda.synchronize()
+        for i in range(2):
+            for name in ("K", "V", "slot_pos", "acc", "evict_slot"):
+                assert torch.equal(getattr(seq[i], name), getattr(con[i], name)), \
+                    "step %d cache %d: %s differs on concurrent streams" % (s, i, name)
+            assert torch.equal(outs_seq[i], con[i].O), "step %d cache %d: O differs" % (s, i)
