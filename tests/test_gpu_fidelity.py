@@ -98,16 +98,13 @@ def test_keeping_everything_and_one_token(dev):
 
 
 @pytest.mark.parametrize("cfg", [LLAMA_128K, QWEN_14B_BATCH], ids=["llama128k", "qwen14b"])
-def test_full_size_sampled_kv_head(dev, cfg):
+def test_full_size_every_head(dev, cfg):
+    """The full-size launches; the oracle checks the cosine of every held-out
+    query of every query head and sequence, and the per-sequence means."""
     inp = lore_inputs(cfg, 0, device=dev)
     desc, ev, K, V, Ko, Vo = retained(cfg, dev, inp)
     Qf = future_queries(cfg, inp, 64, device=dev)
     cos, fid = ev.fidelity(Qf, K, V, Ko, Vo)
     torch.cuda.synchronize()
-    g = 3 % cfg.h_kv
-    bb = cfg.batch - 1
-    heads = list(range(g * cfg.group, (g + 1) * cfg.group))
-    # the oracle on one KV head of one sequence: its query heads against it
-    ref = oracle.output_fidelity(Qf[bb:bb + 1, heads].cpu(), K[bb:bb + 1, g:g + 1].cpu(),
-                                 V[bb:bb + 1, g:g + 1].cpu(), ev.kept[bb:bb + 1, g:g + 1].cpu())
-    compare(cos[bb:bb + 1], fid, ref, "%s seq %d kv head %d" % (cfg.name, bb, g), heads=heads)
+    ref = oracle.output_fidelity(Qf.cpu(), K.cpu(), V.cpu(), ev.kept.cpu())
+    compare(cos, fid, ref, cfg.name)
