@@ -99,13 +99,16 @@ def test_refresh_tiny(dev, n, J, n_sys):
     check_refresh(inp, run_refresh(inp, 2, J, n_sys, dev), J, n_sys)
 
 
-def test_attention_full_size_sampled_kv_head(dev):
-    cfg = QWEN7B_REFRESH  # n = 5120 cached tokens, 28 query heads
+def test_attention_full_size_every_head(dev):
+    """The full-size launch (n = 5120 cached tokens, 28 query heads over 4 KV
+    heads); the oracle checks every query head of every KV head."""
+    cfg = QWEN7B_REFRESH
     inp = refresh_inputs(cfg, device=dev)
     got = run_attention(cfg, inp, dev)
     G = cfg.h_q // cfg.h_kv
-    compare_attention(cfg, {k: v.cpu() for k, v in inp.items()}, got,
-                      list(range(2 * G, 3 * G)), cfg.name)
+    host = {k: v.cpu() for k, v in inp.items()}
+    for g in range(cfg.h_kv):
+        compare_attention(cfg, host, got, list(range(g * G, (g + 1) * G)), cfg.name)
 
 
 def run_refresh(inp, heads_K, J, n_sys, dev, with_ids=True):
