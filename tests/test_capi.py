@@ -251,3 +251,21 @@ def test_row_limits_of_one_launch():
     rc = lib.kvscore_h2o_accumulate(ctypes.byref(h), kv.KVS_H2O_DECODE, *([fake] * 10), None, 0,
                                     None)
     assert rc == 2 and "65535" in kv.last_error()
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/kvscore.h is a C header: it compiles as C11 and as C++17 with
+    every warning an error, and each declared entry point can be named from
+    C (compile only; nothing is linked)."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    inc = os.path.join(root, "include")
+    hdr = open(os.path.join(inc, "kvscore.h")).read()
+    names = sorted(set(re.findall(r"\b(kvs_\w+|kvscore_\w+|kv_compact)\(", hdr)))
+    assert "kvscore_deletion" in names and "kv_compact" in names
+    body = "\n".join("  (void)&%s;" % n for n in names)
+    src = tmp_path / "use.c"
+    src.write_text('#include "kvscore.h"\nint main(void) {\n%s\n  return 0;\n}\n' % body)
+    for cmd in (["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only"],
+                ["g++", "-x", "c++", "-std=c++17", "-Wall", "-Wextra", "-Werror", "-fsyntax-only"]):
+        r = subprocess.run(cmd + ["-I", inc, str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
