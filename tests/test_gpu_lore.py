@@ -97,6 +97,9 @@ SMALL = [
                n=40000, d_model=512, budget=200, seed=19),
     TINY.with_(name="f16-d64-g2-n20000-40splits", dtype="f16", d=64, h_q=2, h_kv=1, n=20000,
                d_model=128, budget=100, seed=20),
+    # fp16 inputs through the 16-bit MFMA paths over many tiles and splits
+    TINY.with_(name="f16-d128-g4-n16384", dtype="f16", d=128, h_q=8, h_kv=2, n=16384,
+               d_model=1024, budget=256, seed=21),
 ]
 
 
