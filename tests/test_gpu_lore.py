@@ -100,6 +100,9 @@ SMALL = [
     # fp16 inputs through the 16-bit MFMA paths over many tiles and splits
     TINY.with_(name="f16-d128-g4-n16384", dtype="f16", d=128, h_q=8, h_kv=2, n=16384,
                d_model=1024, budget=256, seed=21),
+    # fp32 inputs over many tiles and splits (d 64, GQA 2, a ragged tail)
+    TINY.with_(name="f32-d64-g2-n9001", dtype="f32", d=64, h_q=4, h_kv=2, n=9001,
+               d_model=256, budget=200, seed=22),
 ]
 
 
