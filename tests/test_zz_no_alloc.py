@@ -63,9 +63,14 @@ def test_noalloc_matches_workspace_entry_two_calls(dev):
     k1 = _both(dev, big, n_sink=1, w=32, chunk=4, budget=128)
     small = _scores((2, 3, 5003), 502, dev)
     k2 = _both(dev, small, n_sink=3, w=17, chunk=4, budget=300)
-    # and both match the oracle's selection (up to the tie band)
-    for S, k, (n_sink, w, budget) in ((big, k1, (1, 32, 128)), (small, k2, (3, 17, 300))):
-        o, pooled = oracle.topb_select(S.double().cpu().numpy(), n_sink=n_sink, w=w, chunk=4,
+    # third: rows of one segment (the H2O prompt reduction's shape), which the
+    # first kernel selects in full
+    tiny = _scores((3, 4, 1024), 503, dev)
+    k3 = _both(dev, tiny, n_sink=0, w=205, chunk=1, budget=204)
+    # and all match the oracle's selection (up to the tie band)
+    for S, k, (n_sink, w, chunk, budget) in ((big, k1, (1, 32, 4, 128)), (small, k2, (3, 17, 4, 300)),
+                                             (tiny, k3, (0, 205, 1, 204))):
+        o, pooled = oracle.topb_select(S.double().cpu().numpy(), n_sink=n_sink, w=w, chunk=chunk,
                                        budget=budget)
         check_kept(k, o, pooled, n_sink, w, budget)
 
